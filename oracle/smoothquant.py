@@ -1,0 +1,255 @@
+"""CPU oracle of the SmoothQuant W8A8 linear-layer path.
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's CPU
+baseline leg may import this module.  It shares no code with the HIP library
+and is never on the product path.
+
+It is the plain, slow, step-by-step definition of what the path computes,
+written from the jisaku.com glossary page "SmoothQuant" (cited below by section
+name) and, where that page is silent, from the readings listed in the design
+notes (R-numbers).  Every floating-point step that decides an INT8 code is done
+in IEEE fp32 (numpy float32 ufuncs: one correctly rounded operation each, no
+fused multiply-add); the smoothing factors are formed in fp64 and rounded once
+to fp32.  Integer results (codes, accumulators) are exact.
+
+Layouts: activations X are M x K (token major), weights W are N x K (output
+channel major, the page's W_j is column j of this array, i.e. input channel j).
+bf16 data is carried as uint16 bit patterns.
+
+Parity status of each function is stated in its docstring ("pinned by" names
+the test that ties it to something other than itself).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+QMAX = 127  # symmetric INT8 grid [-127, 127] (R2)
+
+
+# ---------------------------------------------------------------- dtypes
+
+
+def widen(x, dtype: str) -> np.ndarray:
+    """fp16 / bf16 storage -> float32 values (exact widening).
+
+    ``dtype`` "f16": ``x`` is a float16 array.  "bf16": ``x`` holds uint16 bit
+    patterns; the fp32 value has the same sign, exponent and the 7 stored
+    mantissa bits followed by 16 zero bits.
+    Pinned by tests/test_oracle_pins.py::test_widen_bf16_bits.
+    """
+    if dtype == "f16":
+        assert x.dtype == np.float16
+        return x.astype(np.float32)
+    if dtype == "bf16":
+        assert x.dtype == np.uint16
+        return (x.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    raise ValueError(dtype)
+
+
+def round_to_bf16(v: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), round to nearest, ties to even.
+
+    Written from the IEEE definition: keep the upper 16 bits of the fp32
+    pattern, rounding by the discarded lower 16 bits (above half: up; exactly
+    half: up only if the kept last bit is 1).  Inputs are finite (R18).
+    Pinned by tests/test_oracle_pins.py::test_round_to_bf16_*.
+    """
+    bits = np.ascontiguousarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    hi = bits >> np.uint64(16)
+    lo = bits & np.uint64(0xFFFF)
+    up = (lo > 0x8000) | ((lo == 0x8000) & ((hi & np.uint64(1)) == 1))
+    return (hi + up.astype(np.uint64)).astype(np.uint16)
+
+
+def narrow(v: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 -> output storage dtype with round to nearest even (R11, R12)."""
+    if dtype == "f16":
+        return v.astype(np.float16)  # numpy's conversion is correctly rounded
+    if dtype == "bf16":
+        return round_to_bf16(v)
+    raise ValueError(dtype)
+
+
+# ---------------------------------------------------------------- step (1)
+
+
+def channel_amax(x, dtype: str, amax=None) -> np.ndarray:
+    """Per-input-channel max |x| over all rows (running max over batches).
+
+    Section "ハイパーパラメータ α" uses max(|X_j|) (over calibration tokens,
+    channel j) and max(|W_j|) (over output channels, input channel j); the
+    usage example's ``get_act_scales`` collects the activation statistic.  For
+    X (T x K) and for W (N x K) this is the max over axis 0 (R4).  ``amax``
+    (float32[K]) is the running value from earlier batches; the max is exact
+    and order free, so batches may be folded in any order.
+    Pinned by test_channel_amax_* (brute force, resumability, membership).
+    """
+    a = np.abs(widen(x, dtype)).max(axis=0).astype(np.float32)
+    if amax is not None:
+        a = np.maximum(a, np.asarray(amax, dtype=np.float32))
+    return a
+
+
+# ---------------------------------------------------------------- step (2)
+
+
+def smooth_factor(a: float, b: float, alpha: float) -> float:
+    """s_j = max|X_j|**alpha / max|W_j|**(1 - alpha) (section "ハイパーパラメータ α").
+
+    Formed in fp64 with the C library's pow and one division, then rounded
+    once to fp32 (R5).  A channel whose activation or weight maximum is zero
+    gets s = 1 (R6).
+    Pinned by test_smooth_factor_alpha_limits / _alpha_half / _balance / _dead.
+    """
+    if a == 0.0 or b == 0.0:
+        return 1.0
+    return float(np.float32(math.pow(a, alpha) / math.pow(b, 1.0 - alpha)))
+
+
+def smooth_factors(amax_x, amax_w, alpha: float):
+    """Vector form of :func:`smooth_factor` plus inv_s = RN32(1 / s) (R7).
+
+    Returns (s, inv_s), both float32[K].
+    """
+    amax_x = np.asarray(amax_x, dtype=np.float32)
+    amax_w = np.asarray(amax_w, dtype=np.float32)
+    assert amax_x.shape == amax_w.shape
+    s = np.empty(amax_x.shape, dtype=np.float32)
+    for j in range(amax_x.shape[0]):
+        s[j] = smooth_factor(float(amax_x[j]), float(amax_w[j]), float(alpha))
+    inv_s = np.float32(1.0) / s  # one fp32 division per channel
+    return s, inv_s.astype(np.float32)
+
+
+# ------------------------------------------------------ smoothing itself
+
+
+def smooth_fp64(x64: np.ndarray, w64: np.ndarray, s: np.ndarray):
+    """The smoothing identity in fp64 (section "平滑化変換の数学").
+
+    X~ = X diag(s)^-1 divides input channel j of X by s_j; W~ = diag(s) W
+    multiplies input channel j of W by s_j (W is N x K here, so that is column
+    j).  Returns (X~, W~) in fp64.
+    Pinned by test_smoothing_identity_fp64.
+    """
+    s64 = np.asarray(s, dtype=np.float64)
+    return x64 / s64[None, :], w64 * s64[None, :]
+
+
+def apply_col_scale(v32: np.ndarray, c) -> np.ndarray:
+    """v[t, j] * c[j] in fp32, one rounding per element.
+
+    With c = inv_s on activations this is X diag(s)^-1 (R7: multiply by the
+    stored reciprocal); with c = s on weights it is the fold diag(s) W, kept in
+    fp32 and not rounded to the model dtype (R8).
+    """
+    return (np.asarray(v32, dtype=np.float32) * np.asarray(c, dtype=np.float32)[None, :]).astype(np.float32)
+
+
+# ------------------------------------------------------------ quantizer
+
+
+def quantize_rows(v32: np.ndarray):
+    """Symmetric per-row INT8 quantization (R2, R3, R9, R10).
+
+    For each row: amax = max |v|; delta = RN32(amax / 127) is the stored
+    dequant scale; r = RN32(127 / amax); code = clamp(RNE(RN32(v * r)),
+    -127, 127).  A zero row gives all-zero codes and delta = 0.  Section
+    "Activation外れ値問題" gives the INT8 range; the symmetric grid, the
+    per-row granularity and round-half-even are readings R2, R3, R9.
+    Returns (q int8[rows, cols], delta float32[rows]).
+    Pinned by test_quantize_* (exhaustive nearest code, ties, range, bound).
+    """
+    v32 = np.asarray(v32, dtype=np.float32)
+    rows = v32.shape[0]
+    q = np.zeros(v32.shape, dtype=np.int8)
+    delta = np.zeros(rows, dtype=np.float32)
+    for t in range(rows):
+        m = np.float32(np.abs(v32[t]).max()) if v32.shape[1] else np.float32(0)
+        if m == 0:
+            continue
+        delta[t] = m / np.float32(QMAX)
+        r = np.float32(QMAX) / m
+        y = (v32[t] * r).astype(np.float32)
+        q[t] = np.clip(np.rint(y), -QMAX, QMAX).astype(np.int8)
+    return q, delta
+
+
+def scale_quant_rows(x, dtype: str, col_scale):
+    """Per-column scale then per-row quantization: steps (2b) and (3).
+
+    (W, s) gives the folded per-output-channel INT8 weight; (X, inv_s) gives
+    the smoothed per-token INT8 activation with its dynamic scale.
+    """
+    return quantize_rows(apply_col_scale(widen(x, dtype), col_scale))
+
+
+# ---------------------------------------------------------------- step (4)
+
+
+def gemm_i32(qa: np.ndarray, qb: np.ndarray) -> np.ndarray:
+    """C[t, k] = sum_j qa[t, j] * qb[k, j], exact (section comparing GPTQ/AWQ:
+    SmoothQuant multiplies the INT8 operands directly, with no dequantization
+    before the product).
+
+    Computed as an fp64 matrix product of the int8 values: every product and
+    every partial sum is an integer of magnitude <= 127*127*K < 2**53, so each
+    is exactly representable and any summation order gives the exact sum.  The
+    result is checked to fit int32.
+    Pinned by test_gemm_* (Python-integer triple loop, closed forms).
+    """
+    qa = np.asarray(qa, dtype=np.int8)
+    qb = np.asarray(qb, dtype=np.int8)
+    K = qa.shape[1]
+    assert qb.shape[1] == K
+    assert QMAX * QMAX * max(K, 1) < 2 ** 53
+    c = qa.astype(np.float64) @ qb.astype(np.float64).T
+    c = c.astype(np.int64)
+    assert np.abs(c).max(initial=0) < 2 ** 31
+    return c.astype(np.int32)
+
+
+# ---------------------------------------------------------------- step (5)
+
+
+def dequant(c: np.ndarray, sa, sb, out_dtype: str) -> np.ndarray:
+    """Y[t, k] = out(RN32(RN32(f32(C[t, k]) * sa[t]) * sb[k])) (R11).
+
+    f32(C) rounds the int32 accumulator to nearest even; each product is one
+    fp32 rounding, applied left to right; the final conversion to fp16 / bf16
+    rounds to nearest even.  Per-token x per-output-channel scales factor out
+    of the K sum, which is what lets the product run in INT8.
+    Pinned by test_dequant_* (closed form, end-to-end error bound).
+    """
+    cf = np.asarray(c, dtype=np.int32).astype(np.float32)
+    y = (cf * np.asarray(sa, dtype=np.float32)[:, None]).astype(np.float32)
+    y = (y * np.asarray(sb, dtype=np.float32)[None, :]).astype(np.float32)
+    return narrow(y, out_dtype)
+
+
+# ------------------------------------------------------ composed flows
+
+
+def prepare_weight(w, dtype: str, amax_x, alpha: float):
+    """Offline weight path: amax_w, (s, inv_s), folded INT8 weight and scales.
+
+    Mirrors the usage example's ``smooth_lm`` then ``quantize_model``.
+    Returns dict(amax_w, s, inv_s, qw, sw).
+    """
+    amax_w = channel_amax(w, dtype)
+    s, inv_s = smooth_factors(amax_x, amax_w, alpha)
+    qw, sw = scale_quant_rows(w, dtype, s)
+    return dict(amax_w=amax_w, s=s, inv_s=inv_s, qw=qw, sw=sw)
+
+
+def linear(x, dtype: str, inv_s, qw, sw):
+    """Runtime forward: smooth + per-token quant, INT8 GEMM, dequant.
+
+    Returns dict(qx, sx, c, y).
+    """
+    qx, sx = scale_quant_rows(x, dtype, inv_s)
+    c = gemm_i32(qx, qw)
+    y = dequant(c, sx, sw, dtype)
+    return dict(qx=qx, sx=sx, c=c, y=y)

@@ -1,0 +1,351 @@
+"""Pins of the CPU oracle against facts fixed outside it (CPU only).
+
+Each test ties one oracle function to something other than its own formula:
+exact rational arithmetic, brute force over all candidates, closed forms,
+invariants, library routines, or values printed on the jisaku.com glossary
+page "SmoothQuant" (cited by section).
+"""
+from __future__ import annotations
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.exact import (F, decimal_pow_ratio, rn16, rn32, rn32_decimal, rnbf16,
+                         ulp32)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+rng = np.random.default_rng(12345)
+
+
+def _bf16_bits(x32: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns via torch's own conversion (an independent routine)."""
+    t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+# ------------------------------------------------------------------ dtypes
+
+
+def test_widen_bf16_bits():
+    bits = np.array([0x3F80, 0xC000, 0x3F00, 0x4049, 0x7F7F, 0x0001, 0x8000], dtype=np.uint16)
+    want = [1.0, -2.0, 0.5, 3.140625, (2 - 2 ** -7) * 2.0 ** 127, 2.0 ** -133, -0.0]
+    got = oracle.widen(bits, "bf16")
+    assert got.dtype == np.float32
+    for g, w in zip(got.tolist(), want):
+        assert g == w and math.copysign(1, g) == math.copysign(1, w)
+
+
+def test_widen_f16_exact():
+    h = np.array([0.1, -65504, 6e-8, 1.5], dtype=np.float16)
+    assert [F(v) for v in oracle.widen(h, "f16")] == [F(v) for v in h]
+
+
+def test_round_to_bf16_ties_and_exact():
+    one = 1.0
+    cases = {
+        one + 2 ** -8: 0x3F80,        # halfway, kept bit even -> down
+        one + 3 * 2 ** -8: 0x3F82,    # halfway, kept bit odd -> up
+        one + 2 ** -8 + 2 ** -20: 0x3F81,  # just above halfway -> up
+        -(one + 2 ** -8): 0xBF80,
+        0.0: 0x0000,
+    }
+    for v, bits in cases.items():
+        assert int(oracle.round_to_bf16(np.array([v], np.float32))[0]) == bits
+
+
+def test_round_to_bf16_vs_exact_and_torch():
+    x = (rng.standard_normal(4000) * np.exp(rng.uniform(-30, 30, 4000))).astype(np.float32)
+    got = oracle.round_to_bf16(x)
+    assert np.array_equal(got, _bf16_bits(x))
+    for v, g in zip(x[:300], got[:300]):
+        want = rnbf16(F(v))
+        assert oracle.widen(np.array([g], np.uint16), "bf16")[0] == np.float32(want)
+
+
+# ------------------------------------------------------------ channel amax
+
+
+def test_channel_amax_brute_force():
+    x = (rng.standard_normal((37, 24)) * 10).astype(np.float16)
+    x[3, 5] = -0.0
+    got = oracle.channel_amax(x, "f16")
+    for j in range(24):
+        best = Fraction(0)
+        for t in range(37):
+            best = max(best, abs(F(x[t, j])))
+        assert F(got[j]) == best
+        # the maximum is one of the inputs of column j
+        assert any(abs(F(x[t, j])) == best for t in range(37))
+
+
+def test_channel_amax_resumable_bf16():
+    x32 = (rng.standard_normal((64, 40)) * 3).astype(np.float32)
+    xb = _bf16_bits(x32)
+    whole = oracle.channel_amax(xb, "bf16")
+    a = oracle.channel_amax(xb[:17], "bf16")
+    b = oracle.channel_amax(xb[17:], "bf16", amax=a)
+    c = oracle.channel_amax(xb[40:], "bf16")
+    d = oracle.channel_amax(xb[:40], "bf16", amax=c)
+    assert np.array_equal(whole, b) and np.array_equal(whole, d)
+
+
+def test_channel_amax_on_weights_is_over_output_channels():
+    # W is N x K; max|W_j| runs over the N output channels of input channel j.
+    w = np.zeros((5, 3), np.float16)
+    w[4, 0] = -7
+    w[0, 2] = 2
+    assert oracle.channel_amax(w, "f16").tolist() == [7.0, 0.0, 2.0]
+
+
+# ------------------------------------------------------- smoothing factors
+
+
+def _rand_amax(n):
+    return np.exp(rng.uniform(-6, 6, n)).astype(np.float32)
+
+
+def test_smooth_factor_alpha_limits():
+    a, b = _rand_amax(500), _rand_amax(500)
+    s1, inv1 = oracle.smooth_factors(a, b, 1.0)
+    assert np.array_equal(s1, a)  # alpha = 1: s_j = max|X_j|
+    s0, inv0 = oracle.smooth_factors(a, b, 0.0)
+    for j in range(500):
+        assert s0[j] == rn32(1 / F(b[j]))  # alpha = 0: s_j = 1 / max|W_j|
+        assert inv1[j] == rn32(1 / F(s1[j])) and inv0[j] == rn32(1 / F(s0[j]))
+
+
+@pytest.mark.parametrize("alpha", [0.5, 0.8, 0.3])
+def test_smooth_factor_general_alpha_correctly_rounded(alpha):
+    a, b = _rand_amax(300), _rand_amax(300)
+    s, inv = oracle.smooth_factors(a, b, alpha)
+    near = 0
+    for j in range(300):
+        want, dist = rn32_decimal(decimal_pow_ratio(float(a[j]), float(b[j]), alpha))
+        if dist < 2.0 ** -45:
+            near += 1  # fp64 evaluation may round either way this close to a midpoint
+            assert abs(float(s[j]) - float(want)) <= ulp32(want)
+        else:
+            assert s[j] == want, (j, a[j], b[j])
+        assert inv[j] == rn32(1 / F(s[j]))
+    assert near == 0
+
+
+def test_smooth_factor_balance():
+    """max|X~_j| = a/s = (ab)**(1-alpha) and max|W~_j| = b*s = (ab)**alpha."""
+    a, b = _rand_amax(200), _rand_amax(200)
+    for alpha in (0.5, 0.8):
+        s, _ = oracle.smooth_factors(a, b, alpha)
+        a64, b64, s64 = a.astype(float), b.astype(float), s.astype(float)
+        np.testing.assert_allclose(a64 / s64, (a64 * b64) ** (1 - alpha), rtol=2e-7)
+        np.testing.assert_allclose(b64 * s64, (a64 * b64) ** alpha, rtol=2e-7)
+        if alpha == 0.5:  # equal split of the difficulty
+            np.testing.assert_allclose(a64 / s64, b64 * s64, rtol=3e-7)
+
+
+def test_smooth_factor_alpha_semantics():
+    """alpha = 1 normalises the activation channels (all difficulty goes to W);
+    alpha = 0 normalises the weight channels (reading R1 of the page's labels)."""
+    a, b = _rand_amax(50), _rand_amax(50)
+    s1, _ = oracle.smooth_factors(a, b, 1.0)
+    assert np.allclose(a.astype(float) / s1, 1.0)
+    s0, _ = oracle.smooth_factors(a, b, 0.0)
+    assert np.allclose(b.astype(float) * s0, 1.0, rtol=1e-7)
+
+
+def test_smooth_factor_dead_channel():
+    s, inv = oracle.smooth_factors(np.array([0, 3, 0], np.float32),
+                                   np.array([2, 0, 0], np.float32), 0.5)
+    assert s.tolist() == [1, 1, 1] and inv.tolist() == [1, 1, 1]
+
+
+def test_smoothing_identity_fp64():
+    """Y = X W = (X diag(s)^-1)(diag(s) W), section on the smoothing math."""
+    x = rng.standard_normal((33, 48))
+    x[:, 7] *= 90
+    w = rng.standard_normal((20, 48)) * 0.02  # N x K
+    s = np.exp(rng.uniform(-4, 4, 48)).astype(np.float32)
+    xt, wt = oracle.smooth_fp64(x, w, s)
+    y = x @ w.T
+    yt = xt @ wt.T
+    scale = np.abs(x) @ np.abs(w).T
+    assert np.max(np.abs(yt - y) / scale) <= 1e-12
+    # smoothing really moved the outlier: channel 7 of X~ is X's channel 7 / s_7
+    assert np.allclose(xt[:, 7] * s[7], x[:, 7])
+
+
+# ----------------------------------------------------------------- quantizer
+
+
+def _nearest_code(y: Fraction) -> int:
+    """Brute force over all 255 symmetric codes; ties go to the even code."""
+    best = None
+    for c in range(-127, 128):
+        d = abs(y - c)
+        if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+            best = (d, c)
+    return best[1]
+
+
+def test_quantize_exhaustive_nearest_code():
+    v = (rng.standard_normal((12, 40)) * np.exp(rng.uniform(-8, 8, (12, 1)))).astype(np.float32)
+    v[3, 11] *= 300  # an outlier element
+    q, d = oracle.quantize_rows(v)
+    for t in range(12):
+        m = max(abs(F(e)) for e in v[t])
+        assert F(d[t]) == F(rn32(m / 127))
+        r = rn32(Fraction(127) / m)
+        for j in range(40):
+            y = rn32(F(v[t, j]) * F(r))
+            assert int(q[t, j]) == _nearest_code(F(y))
+
+
+def test_quantize_crafted_ties():
+    # amax = 127 gives r = 1 exactly and delta = 1: codes are RNE of the values.
+    v = np.array([[127, 2.5, -2.5, 3.5, 0.5, -0.5, 1.5, -126.5]], np.float32)
+    q, d = oracle.quantize_rows(v)
+    assert q.tolist() == [[127, 2, -2, 4, 0, 0, 2, -126]] and d.tolist() == [1.0]
+
+
+def test_quantize_range_and_extremes():
+    v = (rng.standard_normal((200, 64)) * np.exp(rng.uniform(-10, 10, (200, 1)))).astype(np.float32)
+    v[5] = 0
+    q, d = oracle.quantize_rows(v)
+    assert q.min() >= -127 and q.max() <= 127
+    assert not (q == -128).any()
+    assert d[5] == 0 and not q[5].any()
+    for t in range(200):
+        if t != 5:
+            assert np.abs(q[t].astype(int)).max() == 127  # the amax element maps to +-127
+
+
+def test_quantize_error_bound():
+    v = (rng.standard_normal((50, 128)) * 4).astype(np.float32)
+    q, d = oracle.quantize_rows(v)
+    err = np.abs(v.astype(float) - q.astype(float) * d[:, None].astype(float))
+    assert (err <= d[:, None] / 2 * (1 + 2 ** -13)).all()
+
+
+def test_golden_page_outlier_example():
+    """The page's ordinary / outlier channel values (tests/golden, cited there).
+
+    Per-token quantization without smoothing lets the outlier set the scale:
+    the ordinary channel keeps at most a couple of levels.  After smoothing the
+    outlier channel (alpha = 0.5 with unit weight maxima) the ordinary channel
+    gets a much finer grid, the page's reason for moving difficulty into W.
+    """
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "page_outlier_example.txt"))
+            if l.strip() and not l.startswith("#")]
+    x = np.array([[float(r[1]), float(r[2])] for r in rows], np.float16)
+    x32 = oracle.widen(x, "f16")
+    amax = oracle.channel_amax(x, "f16")
+    assert amax.tolist() == [float(np.float16(1.2)), float(np.float16(127.4))]
+    q, d = oracle.quantize_rows(x32)
+    for t in range(5):
+        m = max(abs(F(e)) for e in x32[t])
+        r = rn32(Fraction(127) / m)
+        for j in range(2):
+            assert int(q[t, j]) == _nearest_code(F(rn32(F(x32[t, j]) * F(r))))
+    # closed-form values for this example: the ordinary channel of token 0 is -1
+    assert q[0].tolist() == [-1, 127] and q[3].tolist() == [2, 127]
+    # smoothing with alpha = 0.5 and unit weight maxima: s = sqrt(amax_x)
+    s, inv = oracle.smooth_factors(amax, np.ones(2, np.float32), 0.5)
+    qs, ds = oracle.scale_quant_rows(x, "f16", inv)
+    err_plain = np.abs(q[:, 0] * d - x32[:, 0])
+    err_smooth = np.abs(qs[:, 0] * ds / inv[0] - x32[:, 0])
+    assert err_smooth.max() < err_plain.max() / 4
+
+
+# ---------------------------------------------------------------------- GEMM
+
+
+def test_gemm_brute_force_python_ints():
+    for (m, n, k) in [(1, 1, 1), (3, 5, 7), (9, 4, 64), (2, 3, 130)]:
+        qa = rng.integers(-127, 128, (m, k), dtype=np.int8)
+        qb = rng.integers(-127, 128, (n, k), dtype=np.int8)
+        c = oracle.gemm_i32(qa, qb)
+        assert c.dtype == np.int32 and c.shape == (m, n)
+        for i in range(m):
+            for j in range(n):
+                assert int(c[i, j]) == sum(int(qa[i, t]) * int(qb[j, t]) for t in range(k))
+
+
+def test_gemm_closed_forms():
+    K = 28672
+    ones = np.full((1, K), 127, np.int8)
+    assert int(oracle.gemm_i32(ones, -ones)[0, 0]) == -16129 * K == -462450688
+    qa = rng.integers(-127, 128, (6, 48), dtype=np.int8)
+    ident = (np.eye(48, dtype=np.int16) * 127).astype(np.int8)
+    assert np.array_equal(oracle.gemm_i32(qa, ident), qa.astype(np.int32) * 127)
+
+
+def test_gemm_large_k_vs_integer_matmul():
+    qa = rng.choice(np.array([-127, 127, -126, 125], np.int8), (4, 28672))
+    qb = rng.integers(-127, 128, (5, 28672), dtype=np.int8)
+    want = qa.astype(np.int64) @ qb.astype(np.int64).T  # numpy integer loop, no BLAS
+    assert np.array_equal(oracle.gemm_i32(qa, qb), want)
+
+
+# ------------------------------------------------------------------- dequant
+
+
+def test_dequant_exact_rounding():
+    c = rng.integers(-(2 ** 28), 2 ** 28, (8, 9)).astype(np.int32)
+    c[0, 0] = 2 ** 24 + 1  # int -> fp32 tie: rounds to even (2**24)
+    c[0, 1] = 2 ** 24 + 3  # -> 2**24 + 4
+    sa = np.exp(rng.uniform(-12, -4, 8)).astype(np.float32)
+    sb = np.exp(rng.uniform(-12, -4, 9)).astype(np.float32)
+    y16 = oracle.dequant(c, sa, sb, "f16")
+    ybf = oracle.dequant(c, sa, sb, "bf16")
+    for i in range(8):
+        for j in range(9):
+            cf = rn32(Fraction(int(c[i, j])))
+            if (i, j) == (0, 0):
+                assert F(cf) == 2 ** 24
+            if (i, j) == (0, 1):
+                assert F(cf) == 2 ** 24 + 4
+            t = rn32(F(cf) * F(sa[i]))
+            y = rn32(F(t) * F(sb[j]))
+            assert F(y16[i, j]) == F(rn16(F(y)))
+            assert F(oracle.widen(ybf[i:i + 1, j], "bf16")[0]) == F(rnbf16(F(y)))
+
+
+def test_linear_end_to_end_error_bound_and_method_sanity():
+    """Oracle linear vs fp64 X W^T: within the quantization error bound, and
+    smoothing (alpha = 0.5) beats no smoothing on outlier data (the page's
+    claim that X~ is easier to quantize)."""
+    M, K, N = 48, 256, 40
+    x32 = rng.standard_normal((M, K)).astype(np.float32)
+    out = rng.choice(K, 3, replace=False)
+    x32[:, out] *= np.array([60, -90, 110], np.float32)
+    x = x32.astype(np.float16)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    xf, wf = x.astype(float), w.astype(float)
+    y64 = xf @ wf.T
+    amax_x = oracle.channel_amax(x, "f16")
+    errs = {}
+    for alpha in (None, 0.5):
+        if alpha is None:
+            qw, sw = oracle.scale_quant_rows(w, "f16", np.ones(K, np.float32))
+            inv = np.ones(K, np.float32)
+            s = inv
+        else:
+            p = oracle.prepare_weight(w, "f16", amax_x, alpha)
+            qw, sw, inv, s = p["qw"], p["sw"], p["inv_s"], p["s"]
+        r = oracle.linear(x, "f16", inv, qw, sw)
+        y = r["y"].astype(float)
+        # per-element bound: sum_j (|x~| dw/2 + |w~| dx/2 + dx dw/4) + rounding
+        xt = np.abs(xf * inv.astype(float)[None, :])
+        wt = np.abs(wf * s.astype(float)[None, :])
+        dx, dw = r["sx"].astype(float), sw.astype(float)
+        bound = (xt.sum(1)[:, None] * dw[None, :] / 2 + dx[:, None] * wt.sum(1)[None, :] / 2
+                 + K * dx[:, None] * dw[None, :] / 4)
+        bound = bound * (1 + 1e-3) + np.abs(y64) * 2e-3 + 1e-3
+        assert (np.abs(y - y64) <= bound).all()
+        errs[alpha] = np.abs(y - y64).mean()
+    assert errs[0.5] < errs[None] / 2
