@@ -1,0 +1,291 @@
+"""Benchmark of the SmoothQuant W8A8 linear-layer path on one MI355X.
+
+One step = one pass of the whole path over one batch, for every linear layer
+of the Llama-2-7B-shaped decoder block (prefill, M = 2048 tokens):
+  1. channel amax: fold one fresh 2048-token calibration batch into the
+     layer's running max|X_j| (streaming calibration; step i uses batch i)
+  2. max|W_j| over the weight, smoothing factors s and 1/s, fold s into W and
+     quantize it per output channel
+  3. smooth X (X / s) and quantize it per token
+  4.+5. INT8 GEMM with the fused dequant epilogue -> fp16 Y
+All inputs are resident in HBM before the timed region.
+
+value = the step's INT8 GEMM work (2 M N K summed over the layers) divided by
+the whole step's wall time, in TOPS.  The roofline object reports the GEMM
+kernel (the dominant kernel) against the dense INT8 MFMA peak, with its
+average launch duration taken from HIP events recorded around every GEMM
+launch inside the timed region.  cpu_baseline times the CPU oracle on the
+host cores over one step of the same workload.
+
+python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0  # MI355X dense INT8 MFMA, 10^12 int ops / s
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+METRIC = "W8A8 GEMM TOPS + smooth/quant GB/s (% of MI355X peak), Llama-2-7B shapes"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama2_7b_prefill")
+    ap.add_argument("--alpha", type=float, default=0.5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=20,
+                    help="repetitions per kernel in the per-kernel breakdown pass")
+    return ap.parse_args()
+
+
+def gemm_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.h"):
+        with open(os.path.join(ROOT, "w8a8_int8_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_traffic(workload: str):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
+    or None when there is none or the GEMM source changed since it was taken."""
+    path = os.path.join(PROFILES, f"gemm_i8_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("gemm_source_hash") != gemm_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Layer:
+    """Device buffers of one linear layer; all inputs generated up front."""
+
+    def __init__(self, wl, li, n_batches, alpha, dev):
+        import torch
+
+        import w8a8_int8_amd as w8
+        from w8a8_int8_amd import synth
+
+        L = wl.layers[li]
+        self.name, self.K, self.N, self.M = L.name, L.K, L.N, wl.M[0]
+        self.alpha = alpha
+        self.cal = [synth.calibration(wl, li, wl.cal_batch, chunk=i, device=dev)
+                    for i in range(n_batches)]
+        self.w = synth.weights(wl, li, device=dev)
+        self.x = synth.activations(wl, li, self.M, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.amax_x = torch.zeros(self.K, **f32)
+        self.amax_w = torch.zeros(self.K, **f32)
+        self.s = torch.empty(self.K, **f32)
+        self.inv_s = torch.empty(self.K, **f32)
+        self.qw = torch.empty((self.N, self.K), dtype=torch.int8, device=dev)
+        self.sw = torch.empty(self.N, **f32)
+        self.qx = torch.empty((self.M, self.K), dtype=torch.int8, device=dev)
+        self.sx = torch.empty(self.M, **f32)
+        self.y = torch.empty((self.M, self.N), dtype=self.x.dtype, device=dev)
+        self.w8 = w8
+
+    def gemm_ops(self):
+        return 2.0 * self.M * self.N * self.K
+
+    def step(self, i, ev=None):
+        w8 = self.w8
+        w8.channel_amax(self.cal[i % len(self.cal)], self.amax_x)
+        self.amax_w.zero_()
+        w8.channel_amax(self.w, self.amax_w)
+        w8.smooth_factors(self.amax_x, self.amax_w, self.alpha, self.s, self.inv_s)
+        w8.scale_quant_rows(self.w, self.s, self.qw, self.sw)
+        w8.scale_quant_rows(self.x, self.inv_s, self.qx, self.sx)
+        if ev is not None:
+            ev[0].record()
+        w8.gemm_dequant(self.qx, self.sx, self.qw, self.sw, self.x.dtype, self.y)
+        if ev is not None:
+            ev[1].record()
+
+
+def kernel_breakdown(layers, reps):
+    """Per-kernel mean durations (HIP events), each kernel type timed alone."""
+    import torch
+
+    def timed(fn, n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn(0)
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(n):
+            fn(i)
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b) / n * 1e-3  # seconds
+
+    w8 = layers[0].w8
+    out = {}
+    for L in layers:
+        d = {}
+        nb = len(L.cal)
+        t = timed(lambda i: w8.channel_amax(L.cal[i % nb], L.amax_x), reps)
+        by = L.cal[0].numel() * 2
+        d["channel_amax_calib"] = dict(us=t * 1e6, GBs=by / t / 1e9, frac_hbm=by / t / 1e9 / PEAK_HBM_GBS)
+        t = timed(lambda i: w8.channel_amax(L.w, L.amax_w), reps)
+        by = L.w.numel() * 2
+        d["channel_amax_weight"] = dict(us=t * 1e6, GBs=by / t / 1e9, frac_hbm=by / t / 1e9 / PEAK_HBM_GBS)
+        t = timed(lambda i: w8.scale_quant_rows(L.w, L.s, L.qw, L.sw), reps)
+        by = L.w.numel() * 3 + 4 * (L.N + L.K)
+        d["fold_quant_weight"] = dict(us=t * 1e6, GBs=by / t / 1e9, frac_hbm=by / t / 1e9 / PEAK_HBM_GBS)
+        t = timed(lambda i: w8.scale_quant_rows(L.x, L.inv_s, L.qx, L.sx), reps)
+        by = L.x.numel() * 3 + 4 * (L.M + L.K)
+        d["smooth_quant_act"] = dict(us=t * 1e6, GBs=by / t / 1e9, frac_hbm=by / t / 1e9 / PEAK_HBM_GBS)
+        t = timed(lambda i: w8.gemm_dequant(L.qx, L.sx, L.qw, L.sw, L.x.dtype, L.y), reps)
+        ops = L.gemm_ops()
+        d["gemm_dequant"] = dict(us=t * 1e6, TOPS=ops / t / 1e12, frac_mfma=ops / t / 1e12 / PEAK_INT8_TOPS)
+        out[f"{L.name}_{L.K}x{L.N}"] = {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in d.items()}
+    return out
+
+
+def cpu_baseline(wl, layers, alpha):
+    """The CPU oracle, as it stands, over one step of the same workload."""
+    import oracle
+    from w8a8_int8_amd import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    dname = wl.dtype
+    host = [(synth.to_numpy_bits(L.cal[0]), synth.to_numpy_bits(L.w), synth.to_numpy_bits(L.x))
+            for L in layers]
+    ops = 0.0
+    t0 = time.perf_counter()
+    for (xc, w, x), L in zip(host, layers):
+        ax = oracle.channel_amax(xc, dname)
+        p = oracle.prepare_weight(w, dname, ax, alpha)
+        oracle.linear(x, dname, p["inv_s"], p["qw"], p["sw"])
+        ops += L.gemm_ops()
+    dt = time.perf_counter() - t0
+    return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": (f"one full step of {wl.name} on the host: for each of the "
+                       f"{len(layers)} layers, amax over one {wl.cal_batch}-token calibration "
+                       f"batch, weight amax + smoothing factors + fold/quant, and the forward "
+                       f"(smooth+quant, exact INT8 GEMM, dequant) at M={wl.M[0]}")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by rows/columns without collectives on the hot path; "
+              "see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from w8a8_int8_amd import _lib, synth
+
+    _lib.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda:0"
+    wl = synth.WORKLOADS[args.workload]
+    n_batches = max(1, min(args.steps + args.warmup, wl.cal_tokens // wl.cal_batch))
+    layers = [Layer(wl, li, n_batches, args.alpha, dev) for li in range(len(wl.layers))]
+    torch.cuda.synchronize()
+    print(f"[bench] {wl.name}: {len(layers)} layers, M={wl.M[0]}, buffers ready", file=sys.stderr,
+          flush=True)
+
+    step_i = 0
+    for _ in range(args.warmup):
+        for L in layers:
+            L.step(step_i)
+        step_i += 1
+    torch.cuda.synchronize()
+
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in layers] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        for L, ev in zip(layers, evs[k]):
+            L.step(step_i, ev)
+        step_i += 1
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    ms_per_step = elapsed / args.steps * 1e3
+    ops_per_step = sum(L.gemm_ops() for L in layers)
+    value = ops_per_step / (elapsed / args.steps) / 1e12
+
+    gemm_s = [sum(a.elapsed_time(b) for a, b in row) * 1e-3 for row in evs]
+    gemm_launch_avg = sum(gemm_s) / (len(gemm_s) * len(layers))
+    ops_per_launch = ops_per_step / len(layers)
+    achieved = ops_per_launch / gemm_launch_avg / 1e12
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    kernels = kernel_breakdown(layers, args.kernel_reps)
+    print("[bench] per-kernel pass done", file=sys.stderr, flush=True)
+
+    traffic = pmc_traffic(wl.name)
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic (seeded outlier-bearing activations, N(0, sigma) weights)",
+        "config": {
+            "workload": wl.name,
+            "M": wl.M[0],
+            "layers": [f"{L.name}:{L.K}->{L.N}" for L in layers],
+            "calibration_tokens_per_step": wl.cal_batch,
+            "alpha": args.alpha,
+            "act_dtype": wl.dtype,
+        },
+        "roofline": {
+            "kernel": "gemm_dequant (k_gemm_i8)",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_INT8_TOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_INT8_TOPS, 4),
+            "traffic": traffic,
+            "ops_per_launch": ops_per_launch,
+            "avg_launch_us": round(gemm_launch_avg * 1e6, 3),
+        },
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(wl, layers, args.alpha)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

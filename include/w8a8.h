@@ -1,0 +1,194 @@
+/*
+ * w8a8.h -- C ABI of the SmoothQuant W8A8 linear-layer path on MI355X (gfx950).
+ *
+ * Source of the method: the jisaku.com glossary page "SmoothQuant"
+ * (アクティベーション平滑化量子化).  Each entry point names the section of that
+ * page that defines its operation.
+ *
+ * The path, for one linear layer Y = X W (X: M x K activations, W: the
+ * layer's weight with K input and N output channels):
+ *   1. channel amax over calibration activations      w8a8_channel_amax
+ *   2. smoothing factors s, their reciprocals          w8a8_smooth_factors
+ *      fold s into W and quantize W per output channel w8a8_channel_amax (on W)
+ *                                                       + w8a8_scale_quant_rows
+ *   3. X diag(s)^-1 and per-token INT8 quantization    w8a8_scale_quant_rows
+ *   4. INT8 x INT8 -> INT32 product                    w8a8_gemm_i32 (diagnostic)
+ *   5. dequantize with per-token x per-channel scales  w8a8_gemm_dequant (fuses 4+5)
+ *   runtime forward = 3 + 4 + 5                         w8a8_linear
+ *
+ * Conventions shared by every entry point
+ *   - Layout: all matrices are row-major and contiguous.  Activations are
+ *     M x K (token major).  Weights are stored N x K (output channel major),
+ *     so the page's "W_j" (input channel j) is column j of that array.
+ *   - Memory: pointers are DEVICE pointers on the current HIP device unless a
+ *     comment says otherwise.  The caller allocates and owns every buffer; the
+ *     library allocates nothing and keeps no mutable state, so concurrent calls
+ *     on different streams are safe when their buffers do not overlap.
+ *   - Asynchrony: device work is enqueued on `stream` (0 = the null stream)
+ *     and the call returns without synchronizing.
+ *   - Errors: every check below runs on the host before any HIP call; a failed
+ *     check returns its status and enqueues nothing.  W8A8_ERR_HIP means the
+ *     launch itself failed (hipGetLastError).  No entry point aborts.
+ *   - NULL: a pointer may be NULL only when the array it points to is empty
+ *     (zero elements); otherwise NULL is W8A8_ERR_NULL.
+ *   - Alignment: matrix base pointers must be 16-byte aligned and row lengths
+ *     multiples of 16 bytes, so that every row starts on a 16-byte boundary.
+ *   - Arithmetic: fp32 steps are single IEEE operations with round to nearest
+ *     even (no fused multiply-add); integer results are exact.  Inputs must be
+ *     finite; outputs for non-finite inputs are unspecified.
+ */
+#ifndef W8A8_H
+#define W8A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W8A8_ABI_VERSION 1
+
+/* Largest K for which 127 * 127 * K fits int32, so that every accumulator
+ * (and every partial sum) of the INT8 product is exact in int32. */
+#define W8A8_MAX_K 131072
+
+typedef enum {
+  W8A8_OK = 0,
+  W8A8_ERR_NULL = 1,      /* a required pointer is NULL */
+  W8A8_ERR_SHAPE = 2,     /* a size is negative, too large, or breaks a multiple-of rule */
+  W8A8_ERR_ALIGN = 3,     /* a pointer is not aligned as required */
+  W8A8_ERR_DTYPE = 4,     /* unknown dtype code */
+  W8A8_ERR_ARG = 5,       /* another argument is out of range (alpha, workspace size) */
+  W8A8_ERR_HIP = 6,       /* the HIP launch failed */
+} w8a8_status_t;
+
+/* Storage type of activations, weights and outputs. */
+typedef enum {
+  W8A8_F16 = 0, /* IEEE binary16 */
+  W8A8_BF16 = 1 /* bfloat16 */
+} w8a8_dtype_t;
+
+/* ABI version of the loaded library (W8A8_ABI_VERSION it was built with). */
+int w8a8_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* w8a8_status_str(int status);
+
+/*
+ * Step 1 (and the weight half of step 2): per-column running maximum of |x|.
+ * Page section "ハイパーパラメータ α": the smoothing factor uses max(|X_j|)
+ * over the calibration tokens and max(|W_j|) over the output channels; the
+ * usage example collects the former with `get_act_scales`.
+ *
+ *   x     [rows x cols] fp16/bf16 (dtype), row-major, 16-byte aligned.
+ *   amax  [cols] fp32, in/out: amax[j] = max(amax[j], max_t |x[t, j]|).
+ *         Before the first call the caller fills it with +0.0f; later calls
+ *         (further calibration batches, in any order) keep folding into it.
+ *         Every value in it must be a non-negative finite float.
+ *   rows >= 0 (0 leaves amax unchanged), 1 <= cols, cols % 8 == 0.
+ * For a weight stored N x K, rows = N and cols = K give max|W_j|.
+ * Errors: NULL, SHAPE, ALIGN (x not 16-byte, amax not 4-byte aligned), DTYPE, HIP.
+ */
+w8a8_status_t w8a8_channel_amax(const void* x, int dtype, int64_t rows, int64_t cols,
+                                float* amax, hipStream_t stream);
+
+/*
+ * Step 2: smoothing factors.  Page section "ハイパーパラメータ α":
+ * s_j = max(|X_j|)^alpha / max(|W_j|)^(1 - alpha).
+ *
+ *   amax_x, amax_w  [K] fp32 channel maxima of the activations and weights.
+ *   alpha           migration strength, 0 <= alpha <= 1 (the page's default is 0.5).
+ *   s, inv_s        [K] fp32 outputs: s_j evaluated in fp64 and rounded once to
+ *                   fp32; inv_s_j = 1 / s_j as one fp32 division.  A channel whose
+ *                   amax_x or amax_w is zero gets s_j = inv_s_j = 1.
+ *   K >= 0.
+ * Errors: NULL, SHAPE, ARG (alpha outside [0, 1] or NaN), HIP.
+ */
+w8a8_status_t w8a8_smooth_factors(const float* amax_x, const float* amax_w, int64_t K,
+                                  double alpha, float* s, float* inv_s, hipStream_t stream);
+
+/*
+ * Steps 2 (weights) and 3 (activations): scale every column, then quantize
+ * every row to symmetric INT8.  Page section "平滑化変換の数学": X~ = X s^-1
+ * and W~ = s W; with (x = W, col_scale = s) this folds s into the weight and
+ * quantizes it per output channel, with (x = X, col_scale = inv_s) it smooths
+ * the activations and quantizes them per token.  For each row t:
+ *   v_j = fp32(x[t, j]) * col_scale[j]
+ *   m   = max_j |v_j|;  row_scale[t] = m / 127;  r = 127 / m
+ *   q[t, j] = clamp(round_half_even(v_j * r), -127, 127)
+ * A row with m == 0 gets row_scale 0 and all-zero codes.
+ *
+ *   x          [rows x cols] fp16/bf16, 16-byte aligned.
+ *   col_scale  [cols] fp32, 16-byte aligned.
+ *   q          [rows x cols] int8 output, 16-byte aligned.
+ *   row_scale  [rows] fp32 output (the dequantization scale of each row).
+ *   rows >= 0, cols >= 0, cols % 16 == 0, cols <= 65536.
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, HIP.
+ */
+w8a8_status_t w8a8_scale_quant_rows(const void* x, int dtype, int64_t rows, int64_t cols,
+                                    const float* col_scale, int8_t* q, float* row_scale,
+                                    hipStream_t stream);
+
+/*
+ * Step 4 alone (a diagnostic / test entry point): C = qa qb^T in exact int32.
+ * Page section comparing GPTQ / AWQ / SmoothQuant: the INT8 operands are
+ * multiplied directly, without dequantizing first.
+ *
+ *   qa  [M x K] int8 (per-token codes), 16-byte aligned.
+ *   qb  [N x K] int8 (per-output-channel weight codes), 16-byte aligned.
+ *   c   [M x N] int32 output, c[t, k] = sum_j qa[t, j] * qb[k, j], 16-byte aligned.
+ *   M >= 0, N >= 0, 0 <= K <= W8A8_MAX_K, K % 16 == 0, N % 8 == 0.
+ *   K == 0 writes zeros.  Codes must lie in [-127, 127] (as produced by
+ *   w8a8_scale_quant_rows); a -128 code could overflow int32 at the largest K.
+ * Errors: NULL, SHAPE, ALIGN, HIP.
+ */
+w8a8_status_t w8a8_gemm_i32(const int8_t* qa, const int8_t* qb, int32_t* c, int64_t M,
+                            int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * Steps 4 + 5 fused: y[t, k] = out(fp32(fp32(C[t, k]) * sa[t]) * sb[k]) with C
+ * as in w8a8_gemm_i32, each product one fp32 rounding, out() the round to
+ * nearest even conversion to fp16 / bf16 (out_dtype).  The per-token and
+ * per-channel scales factor out of the K sum, so the product stays in INT8.
+ *
+ *   sa  [M] fp32 per-token scales; sb [N] fp32 per-output-channel scales,
+ *       16-byte aligned.
+ *   y   [M x N] fp16/bf16 output, 16-byte aligned.
+ *   Shape rules as w8a8_gemm_i32.
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, HIP.
+ */
+w8a8_status_t w8a8_gemm_dequant(const int8_t* qa, const float* sa, const int8_t* qb,
+                                const float* sb, void* y, int out_dtype, int64_t M, int64_t N,
+                                int64_t K, hipStream_t stream);
+
+/* Bytes of workspace w8a8_linear needs for M tokens of K channels
+ * (the INT8 activations and their per-token scales, each 256-byte aligned). */
+size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K);
+
+/*
+ * Runtime forward of one smoothed W8A8 linear layer (steps 3 + 4 + 5):
+ * (qX, sx) = scale_quant_rows(x, inv_s) into the workspace, then
+ * y = gemm_dequant(qX, sx, qw, sw).  Two launches on `stream`, no host sync.
+ *
+ *   x          [M x K] fp16/bf16 activations (dtype; y has the same dtype).
+ *   inv_s      [K] fp32 reciprocal smoothing factors, 16-byte aligned.
+ *   qw, sw     [N x K] int8 folded weight codes and [N] fp32 scales (16-byte aligned).
+ *   y          [M x N] output.
+ *   workspace  device buffer of ws_bytes >= w8a8_linear_workspace_bytes(M, K),
+ *              256-byte aligned; its contents on return are the INT8
+ *              activations (M x K) followed by their scales.
+ *   Shape rules: those of both steps (K % 16 == 0, K <= 65536, N % 8 == 0).
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, ARG (workspace too small), HIP.
+ */
+w8a8_status_t w8a8_linear(const void* x, int dtype, const float* inv_s, const int8_t* qw,
+                          const float* sw, void* y, int64_t M, int64_t N, int64_t K,
+                          void* workspace, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W8A8_H */

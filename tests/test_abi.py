@@ -1,0 +1,141 @@
+"""C ABI of libw8a8 without a GPU: it loads, exports every symbol the header
+declares, and rejects bad arguments on the host before any HIP call."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from w8a8_int8_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w8a8.h")
+
+OK, ENULL, ESHAPE, EALIGN, EDTYPE, EARG = 0, 1, 2, 3, 4, 5
+
+# Fake, never dereferenced device addresses: every call below must fail its
+# host-side checks.  With a GPU present these tests are skipped (a validation
+# bug would then launch a kernel on them); the GPU suite covers error paths
+# with real buffers.
+P = 1 << 20  # 16-byte aligned, non-null
+PODD = P + 4  # 4-byte aligned only
+
+cpu_only = pytest.mark.skipif(torch.cuda.is_available(),
+                              reason="fake pointers are only safe without a GPU")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w8a8_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_header_symbols():
+    lib = _lib.load()
+    syms = declared_symbols()
+    assert len(syms) == 9
+    for s in syms:
+        assert hasattr(lib, s), s
+        assert s in _lib.PROTOTYPES, s
+    assert lib.w8a8_abi_version() == 1
+
+
+def test_status_strings():
+    lib = _lib.load()
+    for code in range(0, 7):
+        s = lib.w8a8_status_str(code)
+        assert s and s.decode()
+    assert lib.w8a8_status_str(99).decode() == "unknown status"
+
+
+def test_workspace_bytes():
+    lib = _lib.load()
+    assert lib.w8a8_linear_workspace_bytes(0, 0) == 0
+    assert lib.w8a8_linear_workspace_bytes(1, 16) == 256 + 256
+    assert lib.w8a8_linear_workspace_bytes(2048, 4096) == 2048 * 4096 + 2048 * 4
+    assert lib.w8a8_linear_workspace_bytes(-1, 16) == 0
+
+
+@cpu_only
+def test_channel_amax_rejects():
+    f = _lib.load().w8a8_channel_amax
+    assert f(0, 0, 4, 8, P, 0) == ENULL
+    assert f(0, 0, 0, 8, 0, 0) == ENULL  # amax is always required
+    assert f(P, 0, 4, 8, 0, 0) == ENULL
+    assert f(P, 7, 4, 8, P, 0) == EDTYPE
+    assert f(P, 0, -1, 8, P, 0) == ESHAPE
+    assert f(P, 0, 4, 0, P, 0) == ESHAPE
+    assert f(P, 0, 4, 12, P, 0) == ESHAPE
+    assert f(PODD, 0, 4, 8, P, 0) == EALIGN
+    assert f(P, 1, 4, 8, P + 2, 0) == EALIGN
+
+
+@cpu_only
+def test_smooth_factors_rejects():
+    f = _lib.load().w8a8_smooth_factors
+    assert f(0, P, 8, 0.5, P, P, 0) == ENULL
+    assert f(P, P, 8, 0.5, P, 0, 0) == ENULL
+    assert f(0, 0, 0, 0.5, 0, 0, 0) == OK  # K == 0: nothing to do, no launch
+    assert f(P, P, -1, 0.5, P, P, 0) == ESHAPE
+    assert f(P, P, 8, -0.01, P, P, 0) == EARG
+    assert f(P, P, 8, 1.5, P, P, 0) == EARG
+    assert f(P, P, 8, float("nan"), P, P, 0) == EARG
+    assert f(P + 2, P, 8, 0.5, P, P, 0) == EALIGN
+
+
+@cpu_only
+def test_scale_quant_rows_rejects():
+    f = _lib.load().w8a8_scale_quant_rows
+    assert f(0, 0, 4, 16, P, P, P, 0) == ENULL
+    assert f(P, 0, 4, 16, P, P, 0, 0) == ENULL
+    assert f(0, 0, 0, 16, P, 0, 0, 0) == OK  # no rows: nothing to do, no launch
+    assert f(P, 2, 4, 16, P, P, P, 0) == EDTYPE
+    assert f(P, 0, -4, 16, P, P, P, 0) == ESHAPE
+    assert f(P, 0, 4, 24, P, P, P, 0) == ESHAPE  # cols % 16
+    assert f(P, 0, 4, 65536 + 16, P, P, P, 0) == ESHAPE
+    assert f(PODD, 0, 4, 16, P, P, P, 0) == EALIGN
+    assert f(P, 0, 4, 16, PODD, P, P, 0) == EALIGN
+    assert f(P, 0, 4, 16, P, PODD, P, 0) == EALIGN
+    assert f(P, 0, 4, 16, P, P, P + 2, 0) == EALIGN
+
+
+@cpu_only
+def test_gemm_rejects():
+    lib = _lib.load()
+    g = lib.w8a8_gemm_i32
+    assert g(0, P, P, 4, 8, 16, 0) == ENULL
+    assert g(P, P, 0, 4, 8, 16, 0) == ENULL
+    assert g(0, P, 0, 0, 8, 16, 0) == OK  # empty output: no launch
+    assert g(P, P, P, -1, 8, 16, 0) == ESHAPE
+    assert g(P, P, P, 4, 12, 16, 0) == ESHAPE  # N % 8
+    assert g(P, P, P, 4, 8, 24, 0) == ESHAPE  # K % 16
+    assert g(P, P, P, 4, 8, 131072 + 16, 0) == ESHAPE  # int32 exactness bound
+    assert g(PODD, P, P, 4, 8, 16, 0) == EALIGN
+    assert g(P, P, PODD, 4, 8, 16, 0) == EALIGN
+    d = lib.w8a8_gemm_dequant
+    assert d(P, 0, P, P, P, 0, 4, 8, 16, 0) == ENULL
+    assert d(P, P, P, P, P, 3, 4, 8, 16, 0) == EDTYPE
+    assert d(P, P, P, PODD, P, 0, 4, 8, 16, 0) == EALIGN
+    assert d(P, P, P, P, P, 0, 4, 9, 16, 0) == ESHAPE
+
+
+@cpu_only
+def test_linear_rejects():
+    lin = _lib.load().w8a8_linear
+    need = _lib.load().w8a8_linear_workspace_bytes(4, 16)
+    assert lin(P, 0, P, P, P, P, 4, 8, 16, 0, need, 0) == ENULL
+    assert lin(P, 5, P, P, P, P, 4, 8, 16, P, need, 0) == EDTYPE
+    assert lin(P, 0, P, P, P, P, 4, 8, 16, P, need - 1, 0) == EARG
+    assert lin(P, 0, P, P, P, P, 4, 8, 16, P + 16, need, 0) == EALIGN  # workspace 256 B
+    assert lin(P, 0, P, P, P, P, 4, 8, 24, P, 1 << 20, 0) == ESHAPE
+    assert lin(P, 0, P, P, P, P, 4, 12, 16, P, need, 0) == ESHAPE
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError, match="no fallback"):
+        _lib.load()

@@ -1,0 +1,323 @@
+"""GPU parity: the HIP path against the CPU oracle, element by element.
+
+Every input comes from the seeded generator in w8a8_int8_amd.synth; the
+oracle gets the same bits on the host.  Integer results (codes, accumulators)
+and the fp32 scales must be bit-identical; fp16/bf16 outputs must be
+bit-identical too (both sides follow the same fp32 operation order) and are
+additionally checked against the bar max|dY| <= 1e-3 max|Y| + 1 ulp.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import w8a8_int8_amd as w8
+from tests.exact import rn32_decimal, decimal_pow_ratio, ulp32
+from w8a8_int8_amd import _lib, synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TINY = synth.WORKLOADS["tiny_512"]
+
+
+def np_bits(t: torch.Tensor):
+    return synth.to_numpy_bits(t)
+
+
+def dt_name(t: torch.Tensor) -> str:
+    return {torch.float16: "f16", torch.bfloat16: "bf16"}[t.dtype]
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+def rand_act(rows, cols, dtype, seed, outliers=3):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    x = torch.randn((rows, cols), generator=g)
+    if cols and outliers:
+        idx = torch.randperm(cols, generator=g)[:outliers]
+        x[:, idx] *= 80.0
+    return x.to(dtype).to(DEV)
+
+
+def y_values(y_np: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f16":
+        return y_np.astype(np.float64)
+    return oracle.widen(y_np, "bf16").astype(np.float64)
+
+
+def assert_y_close(y_gpu: np.ndarray, y_or: np.ndarray, dtype: str):
+    a, b = y_values(y_gpu, dtype), y_values(y_or, dtype)
+    if dtype == "f16":
+        ulp = np.spacing(np.abs(b).astype(np.float16)).astype(np.float64)
+    else:
+        e = np.floor(np.log2(np.maximum(np.abs(b), 2.0 ** -126)))
+        ulp = 2.0 ** (e - 7)
+    tol = 1e-3 * np.abs(b).max(initial=0.0) + ulp
+    assert (np.abs(a - b) <= tol).all()
+    # both sides take the same fp32 steps: expect identical bits
+    assert np.array_equal(y_gpu.view(np.uint16), y_or.view(np.uint16))
+
+
+def assert_s_parity(s_gpu, inv_gpu, amax_x, amax_w, alpha):
+    s_or, inv_or = oracle.smooth_factors(amax_x, amax_w, alpha)
+    diff = np.nonzero(s_gpu.view(np.uint32) != s_or.view(np.uint32))[0]
+    for j in diff:
+        # only acceptable where the fp64 value sits on an fp32 rounding midpoint
+        # to within the fp64 evaluation error of pow (device vs host libm)
+        _, dist = rn32_decimal(decimal_pow_ratio(float(amax_x[j]), float(amax_w[j]), alpha))
+        assert dist < 2.0 ** -45, (j, s_gpu[j], s_or[j])
+        assert abs(float(s_gpu[j]) - float(s_or[j])) <= ulp32(s_or[j])
+    ok = np.setdiff1d(np.arange(len(s_or)), diff)
+    assert np.array_equal(inv_gpu[ok].view(np.uint32), inv_or[ok].view(np.uint32))
+    return len(diff)
+
+
+# ------------------------------------------------------------ step 1: amax
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("rows,cols", [(1, 8), (37, 136), (300, 1032), (2048, 4096),
+                                       (1000, 11008), (129, 28672)])
+def test_channel_amax(dtype, rows, cols):
+    x = rand_act(rows, cols, dtype, seed=rows * 7 + cols)
+    got = host(w8.channel_amax(x))
+    want = oracle.channel_amax(np_bits(x), dt_name(x))
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_channel_amax_running_batches():
+    xs = [rand_act(r, 520 * 8, torch.float16, seed=r) for r in (2048, 5, 777)]
+    amax = None
+    want = None
+    for x in xs:
+        amax = w8.channel_amax(x, amax)
+        want = oracle.channel_amax(np_bits(x), "f16", amax=want)
+    assert np.array_equal(host(amax).view(np.uint32), want.view(np.uint32))
+
+
+def test_channel_amax_large_calibration_slice():
+    """One call over 131072 calibration tokens of a 4096-channel layer (1 GiB)."""
+    wl = synth.WORKLOADS["llama2_7b_prefill"]
+    x = synth.calibration(wl, 0, 131072, chunk=99, device=DEV)
+    got = host(w8.channel_amax(x))
+    want = oracle.channel_amax(np_bits(x), "f16")
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_channel_amax_zero_rows_keeps_running_value():
+    amax = torch.full((64,), 3.0, device=DEV)
+    x = torch.empty((0, 64), dtype=torch.float16, device=DEV)
+    w8.channel_amax(x, amax)
+    assert (amax == 3.0).all()
+
+
+# -------------------------------------------------------- step 2: factors
+
+
+@pytest.mark.parametrize("alpha", [0.0, 0.3, 0.5, 0.8, 1.0])
+def test_smooth_factors(alpha):
+    rng = np.random.default_rng(int(alpha * 10))
+    K = 28672
+    ax = np.exp(rng.uniform(-8, 8, K)).astype(np.float32)
+    aw = np.exp(rng.uniform(-8, 3, K)).astype(np.float32)
+    ax[:5] = 0
+    aw[3:9] = 0
+    s, inv = w8.smooth_factors(torch.from_numpy(ax).to(DEV), torch.from_numpy(aw).to(DEV), alpha)
+    n = assert_s_parity(host(s), host(inv), ax, aw, alpha)
+    assert n == 0
+
+
+# ------------------------------------------------- steps 2b/3: scale + quant
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("rows,cols", [(1, 16), (3, 48), (64, 512), (1025, 4096),
+                                       (2050, 7168), (4100, 11008), (33, 28672),
+                                       (5, 65536), (7, 0)])
+def test_scale_quant_rows(dtype, rows, cols):
+    x = rand_act(rows, cols, dtype, seed=rows + 3 * cols)
+    if rows > 2:
+        x[1] = 0  # a zero row: codes 0, scale 0
+    g = torch.Generator(device="cpu").manual_seed(cols)
+    c = torch.exp(torch.rand(cols, generator=g) * 8 - 4).to(DEV)
+    q, d = w8.scale_quant_rows(x, c)
+    q_or, d_or = oracle.scale_quant_rows(np_bits(x), dt_name(x), host(c))
+    assert np.array_equal(host(q), q_or)
+    assert np.array_equal(host(d).view(np.uint32), d_or.view(np.uint32))
+    assert not (host(q) == -128).any()
+
+
+# ---------------------------------------------------------------- step 4
+
+
+def rand_codes(rows, cols, seed):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    return torch.randint(-127, 128, (rows, cols), generator=g, dtype=torch.int8).to(DEV)
+
+
+# shapes cover the three tile configurations (128x128, 256x128, 256x256),
+# ragged M, N and K tails, K = 0 and empty outputs
+GEMM_SHAPES = [(1, 8, 16), (37, 136, 80), (300, 520, 1040), (64, 512, 512),
+               (2048, 4096, 256), (4000, 8184, 272), (4096, 8192, 144), (513, 264, 4112),
+               (5, 16, 0), (0, 8, 32), (8, 0, 32)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_gemm_i32(M, N, K):
+    qa, qb = rand_codes(M, K, M + K), rand_codes(N, K, N + 2 * K + 1)
+    c = host(w8.gemm_i32(qa, qb))
+    assert np.array_equal(c, oracle.gemm_i32(host(qa), host(qb)))
+
+
+def test_gemm_i32_extremes():
+    K = 28672
+    qa = torch.full((33, K), 127, dtype=torch.int8, device=DEV)
+    qb = torch.full((16, K), -127, dtype=torch.int8, device=DEV)
+    c = host(w8.gemm_i32(qa, qb))
+    assert (c == -16129 * K).all()
+
+
+@pytest.mark.parametrize("out", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("M,N,K", [(37, 136, 80), (300, 520, 1040), (2048, 4096, 256),
+                                   (4000, 8184, 272), (5, 16, 0)])
+def test_gemm_dequant(out, M, N, K):
+    qa, qb = rand_codes(M, K, M + K), rand_codes(N, K, N + 2 * K + 1)
+    g = torch.Generator(device="cpu").manual_seed(M * N)
+    sa = (torch.rand(M, generator=g) * 0.05 + 1e-3).to(DEV)
+    sb = (torch.rand(N, generator=g) * 2e-4 + 1e-5).to(DEV)
+    y = w8.gemm_dequant(qa, sa, qb, sb, out)
+    name = "f16" if out == torch.float16 else "bf16"
+    y_or = oracle.dequant(oracle.gemm_i32(host(qa), host(qb)), host(sa), host(sb), name)
+    assert_y_close(np_bits(y), y_or, name)
+
+
+# ------------------------------------------------------ end to end, tiny
+
+
+def test_tiny_linear_end_to_end():
+    wl = TINY
+    xc = synth.calibration(wl, 0, wl.cal_tokens, device=DEV)
+    w = synth.weights(wl, 0, device=DEV)
+    x = synth.activations(wl, 0, wl.M[0], device=DEV)
+    amax_x = w8.channel_amax(xc)
+    p = w8.prepare_weight(w, amax_x, 0.5)
+    y = w8.linear(x, p["inv_s"], p["qw"], p["sw"])
+    # separate entry points give the same result as the fused linear call
+    qx, sx = w8.scale_quant_rows(x, p["inv_s"])
+    y2 = w8.gemm_dequant(qx, sx, p["qw"], p["sw"], torch.float16)
+    assert torch.equal(y, y2)
+
+    ax_or = oracle.channel_amax(np_bits(xc), "f16")
+    assert np.array_equal(host(amax_x), ax_or)
+    po = oracle.prepare_weight(np_bits(w), "f16", ax_or, 0.5)
+    assert np.array_equal(host(p["amax_w"]), po["amax_w"])
+    assert assert_s_parity(host(p["s"]), host(p["inv_s"]), ax_or, po["amax_w"], 0.5) == 0
+    assert np.array_equal(host(p["qw"]), po["qw"])
+    assert np.array_equal(host(p["sw"]).view(np.uint32), po["sw"].view(np.uint32))
+    lo = oracle.linear(np_bits(x), "f16", po["inv_s"], po["qw"], po["sw"])
+    assert np.array_equal(host(qx), lo["qx"])
+    assert np.array_equal(host(sx).view(np.uint32), lo["sx"].view(np.uint32))
+    assert np.array_equal(host(w8.gemm_i32(qx, p["qw"])), lo["c"])
+    assert_y_close(np_bits(y), lo["y"], "f16")
+
+
+def test_zero_activation_rows_give_zero_outputs():
+    wl = TINY
+    w = synth.weights(wl, 0, device=DEV)
+    x = synth.activations(wl, 0, 40, device=DEV)
+    x[7] = 0
+    p = w8.prepare_weight(w, torch.ones(512, device=DEV), 0.5)
+    y = w8.linear(x, p["inv_s"], p["qw"], p["sw"])
+    assert (y[7] == 0).all() and (y[6] != 0).any()
+
+
+def test_gpu_alignment_errors_with_real_buffers():
+    x = torch.zeros((4, 40), dtype=torch.float16, device=DEV)
+    amax = torch.zeros(32, device=DEV)
+    lib = _lib.load()
+    st = torch.cuda.current_stream().cuda_stream
+    # a view that starts 2 bytes into the buffer is rejected before any launch
+    assert lib.w8a8_channel_amax(x.data_ptr() + 2, 0, 4, 32, amax.data_ptr(), st) == 3
+    buf = torch.zeros(4 * 32 + 8, dtype=torch.float16, device=DEV)
+    xm = buf[1:1 + 4 * 32].view(4, 32)  # contiguous, 2 bytes past a 16-byte boundary
+    with pytest.raises(_lib.W8A8Error):
+        w8.scale_quant_rows(xm, torch.ones(32, device=DEV))
+
+
+# ---------------------------------------- the five workloads at full size
+
+
+def _sample_rows(M, n=48, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set([0, M - 1]) | set(rng.integers(0, M, n).tolist())
+    return np.array(sorted(rows))
+
+
+def _workload_cases():
+    cases = []
+    for name, wl in synth.WORKLOADS.items():
+        for li in range(len(wl.layers)):
+            for alpha in wl.alphas:
+                cases.append(pytest.param(name, li, alpha, id=f"{name}-{wl.layers[li].name}-a{alpha}"))
+    return cases
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,li,alpha", _workload_cases())
+def test_workload_layer(name, li, alpha):
+    """Full-size layer through the calls the benchmark times, against the oracle:
+    amax, s, inv_s, qW, sw, qX and sx in full; Y and C on sampled token rows."""
+    wl = synth.WORKLOADS[name]
+    L = wl.layers[li]
+    dname = wl.dtype
+    cal_rows = min(wl.cal_batch, wl.cal_tokens)
+    xc = synth.calibration(wl, li, cal_rows, device=DEV)
+    w = synth.weights(wl, li, device=DEV)
+    Mmax = max(wl.M)
+    x_all = synth.activations(wl, li, Mmax, device=DEV)
+
+    amax_x = w8.channel_amax(xc)
+    p = w8.prepare_weight(w, amax_x, alpha)
+    torch.cuda.synchronize()
+
+    ax_or = oracle.channel_amax(np_bits(xc), dname)
+    assert np.array_equal(host(amax_x).view(np.uint32), ax_or.view(np.uint32))
+    w_np = np_bits(w)
+    del w
+    aw_or = oracle.channel_amax(w_np, dname)
+    assert np.array_equal(host(p["amax_w"]).view(np.uint32), aw_or.view(np.uint32))
+    s_or, inv_or = oracle.smooth_factors(ax_or, aw_or, alpha)
+    assert assert_s_parity(host(p["s"]), host(p["inv_s"]), ax_or, aw_or, alpha) == 0
+    qw_or, sw_or = oracle.scale_quant_rows(w_np, dname, s_or)
+    del w_np
+    assert np.array_equal(host(p["qw"]), qw_or)
+    assert np.array_equal(host(p["sw"]).view(np.uint32), sw_or.view(np.uint32))
+
+    ys = {}
+    for M in wl.M:
+        x = x_all[:M].contiguous()
+        ws = torch.empty(w8.linear_workspace_bytes(M, L.K), dtype=torch.uint8, device=DEV)
+        y = w8.linear(x, p["inv_s"], p["qw"], p["sw"], workspace=ws)
+        qx = ws[:M * L.K].view(torch.int8).view(M, L.K)
+        off = (M * L.K + 255) // 256 * 256
+        sx = ws[off:off + 4 * M].view(torch.float32)
+        qx_or, sx_or = oracle.scale_quant_rows(np_bits(x), dname, inv_or)
+        assert np.array_equal(host(qx), qx_or)
+        assert np.array_equal(host(sx).view(np.uint32), sx_or.view(np.uint32))
+        rows = _sample_rows(M, seed=M + li)
+        c_or = oracle.gemm_i32(qx_or[rows], qw_or)
+        y_or = oracle.dequant(c_or, sx_or[rows], sw_or, dname)
+        y_np = np_bits(y)
+        assert_y_close(y_np[rows], y_or, dname)
+        c = host(w8.gemm_i32(qx, p["qw"]))
+        assert np.array_equal(c[rows], c_or)
+        ys[M] = y_np
+    # decode shapes: the first rows do not depend on how many rows follow
+    ms = sorted(wl.M)
+    for a, b in zip(ms, ms[1:]):
+        assert np.array_equal(ys[a].view(np.uint16), ys[b][:a].view(np.uint16))

@@ -1,0 +1,177 @@
+"""Python binding of libw8a8 over torch tensors.
+
+Argument marshalling only: each function checks devices, dtypes and
+contiguity, allocates missing outputs with torch (device memory plumbing) and
+calls the C entry point of the same name on the current HIP stream.  Every
+step of the computation runs in the library's HIP kernels; there is no
+fallback path.
+
+Names follow the usage example on the jisaku.com glossary page "SmoothQuant"
+(section "インストール・使用例"): ``channel_amax`` collects the activation
+statistics (``get_act_scales``), ``smooth_factors`` + ``prepare_weight``
+smooth and quantize a layer (``smooth_lm``, ``quantize_model``), and
+``linear`` runs the W8A8 forward.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float16: _lib.W8A8_F16, torch.bfloat16: _lib.W8A8_BF16}
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _dev(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if t.device.type != "cuda":
+            raise ValueError(f"expected a GPU tensor, got one on {t.device}")
+        if not t.is_contiguous():
+            raise ValueError("expected a contiguous tensor")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"expected float16 or bfloat16, got {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _need(t: torch.Tensor, dtype: torch.dtype, shape) -> None:
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"expected {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+
+
+def channel_amax(x: torch.Tensor, amax: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Fold max|x| over the rows of ``x`` (rows x cols) into ``amax`` (fp32[cols]).
+
+    A new ``amax`` starts at zero; passing the previous result continues a
+    running maximum over calibration batches.
+    """
+    _dev(x)
+    rows, cols = x.shape
+    if amax is None:
+        amax = torch.zeros(cols, dtype=torch.float32, device=x.device)
+    _dev(amax)
+    _need(amax, torch.float32, (cols,))
+    lib = _lib.load()
+    _lib.check("w8a8_channel_amax", lib.w8a8_channel_amax(
+        _ptr(x), _dtype_code(x), rows, cols, _ptr(amax), _stream()))
+    return amax
+
+
+def smooth_factors(amax_x: torch.Tensor, amax_w: torch.Tensor, alpha: float,
+                   s: Optional[torch.Tensor] = None, inv_s: Optional[torch.Tensor] = None):
+    """(s, inv_s): s_j = amax_x[j]**alpha / amax_w[j]**(1 - alpha), inv_s = 1 / s."""
+    _dev(amax_x, amax_w)
+    K = amax_x.shape[0]
+    _need(amax_x, torch.float32, (K,))
+    _need(amax_w, torch.float32, (K,))
+    s = torch.empty(K, dtype=torch.float32, device=amax_x.device) if s is None else s
+    inv_s = torch.empty(K, dtype=torch.float32, device=amax_x.device) if inv_s is None else inv_s
+    _dev(s, inv_s)
+    lib = _lib.load()
+    _lib.check("w8a8_smooth_factors", lib.w8a8_smooth_factors(
+        _ptr(amax_x), _ptr(amax_w), K, float(alpha), _ptr(s), _ptr(inv_s), _stream()))
+    return s, inv_s
+
+
+def scale_quant_rows(x: torch.Tensor, col_scale: torch.Tensor,
+                     q: Optional[torch.Tensor] = None, row_scale: Optional[torch.Tensor] = None):
+    """(q int8 rows x cols, row_scale fp32[rows]) of x * col_scale per row."""
+    _dev(x, col_scale)
+    rows, cols = x.shape
+    _need(col_scale, torch.float32, (cols,))
+    q = torch.empty((rows, cols), dtype=torch.int8, device=x.device) if q is None else q
+    row_scale = (torch.empty(rows, dtype=torch.float32, device=x.device)
+                 if row_scale is None else row_scale)
+    _dev(q, row_scale)
+    _need(q, torch.int8, (rows, cols))
+    _need(row_scale, torch.float32, (rows,))
+    lib = _lib.load()
+    _lib.check("w8a8_scale_quant_rows", lib.w8a8_scale_quant_rows(
+        _ptr(x), _dtype_code(x), rows, cols, _ptr(col_scale), _ptr(q), _ptr(row_scale),
+        _stream()))
+    return q, row_scale
+
+
+def gemm_i32(qa: torch.Tensor, qb: torch.Tensor, c: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Exact int32 C = qa @ qb.T for qa (M x K) and qb (N x K) int8."""
+    _dev(qa, qb)
+    M, K = qa.shape
+    N = qb.shape[0]
+    _need(qb, torch.int8, (N, K))
+    _need(qa, torch.int8, (M, K))
+    c = torch.empty((M, N), dtype=torch.int32, device=qa.device) if c is None else c
+    _dev(c)
+    _need(c, torch.int32, (M, N))
+    lib = _lib.load()
+    _lib.check("w8a8_gemm_i32", lib.w8a8_gemm_i32(_ptr(qa), _ptr(qb), _ptr(c), M, N, K, _stream()))
+    return c
+
+
+def gemm_dequant(qa: torch.Tensor, sa: torch.Tensor, qb: torch.Tensor, sb: torch.Tensor,
+                 out_dtype: torch.dtype = torch.float16,
+                 y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = (C * sa[:, None]) * sb[None, :] rounded to ``out_dtype``, C = qa @ qb.T."""
+    _dev(qa, sa, qb, sb)
+    M, K = qa.shape
+    N = qb.shape[0]
+    _need(qa, torch.int8, (M, K))
+    _need(qb, torch.int8, (N, K))
+    _need(sa, torch.float32, (M,))
+    _need(sb, torch.float32, (N,))
+    y = torch.empty((M, N), dtype=out_dtype, device=qa.device) if y is None else y
+    _dev(y)
+    _need(y, out_dtype, (M, N))
+    lib = _lib.load()
+    _lib.check("w8a8_gemm_dequant", lib.w8a8_gemm_dequant(
+        _ptr(qa), _ptr(sa), _ptr(qb), _ptr(sb), _ptr(y), _DT[out_dtype], M, N, K, _stream()))
+    return y
+
+
+def linear_workspace_bytes(M: int, K: int) -> int:
+    return int(_lib.load().w8a8_linear_workspace_bytes(M, K))
+
+
+def linear(x: torch.Tensor, inv_s: torch.Tensor, qw: torch.Tensor, sw: torch.Tensor,
+           y: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """W8A8 forward of one smoothed linear layer: y = dequant(quant(x * inv_s) @ qw.T)."""
+    _dev(x, inv_s, qw, sw)
+    M, K = x.shape
+    N = qw.shape[0]
+    _need(inv_s, torch.float32, (K,))
+    _need(qw, torch.int8, (N, K))
+    _need(sw, torch.float32, (N,))
+    y = torch.empty((M, N), dtype=x.dtype, device=x.device) if y is None else y
+    _dev(y)
+    _need(y, x.dtype, (M, N))
+    need = linear_workspace_bytes(M, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _dev(workspace)
+    lib = _lib.load()
+    _lib.check("w8a8_linear", lib.w8a8_linear(
+        _ptr(x), _dtype_code(x), _ptr(inv_s), _ptr(qw), _ptr(sw), _ptr(y), M, N, K,
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
+    return y
+
+
+def prepare_weight(w: torch.Tensor, amax_x: torch.Tensor, alpha: float) -> dict:
+    """Offline weight path of one layer: max|W_j|, (s, inv_s), folded INT8 weight.
+
+    ``w`` is N x K (output channel major).  Returns dict(amax_w, s, inv_s, qw, sw).
+    """
+    amax_w = channel_amax(w)
+    s, inv_s = smooth_factors(amax_x, amax_w, alpha)
+    qw, sw = scale_quant_rows(w, s)
+    return dict(amax_w=amax_w, s=s, inv_s=inv_s, qw=qw, sw=sw)

@@ -1,0 +1,143 @@
+// C ABI of libw8a8: argument validation and dispatch to the kernels.
+//
+// Every check runs on the host before any HIP call, so a rejected call
+// enqueues nothing and touches no device state.  The entry points, their
+// arguments and their error codes are documented in include/w8a8.h.
+#include "../../include/w8a8.h"
+
+#include <math.h>
+
+#include "common.h"
+
+namespace {
+
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+inline w8a8_status_t hip_status(hipError_t e) { return e == hipSuccess ? W8A8_OK : W8A8_ERR_HIP; }
+
+inline bool valid_dtype(int dt) { return dt == W8A8_F16 || dt == W8A8_BF16; }
+
+constexpr int64_t kMaxRows = (int64_t)1 << 31;  // 32-bit row indices in the kernels
+constexpr int64_t kMaxQuantCols = 65536;         // 1024 threads x 8 chunks x 8 values
+constexpr size_t kWsAlign = 256;
+
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+w8a8_status_t check_gemm(const void* qa, const void* qb, const void* out, int64_t M, int64_t N,
+                         int64_t K) {
+  if (M < 0 || N < 0 || K < 0 || M >= kMaxRows || N >= kMaxRows || K > W8A8_MAX_K ||
+      K % 16 != 0 || N % 8 != 0)
+    return W8A8_ERR_SHAPE;
+  // a pointer may be NULL only when its array is empty
+  if ((!qa && M * K) || (!qb && N * K) || (!out && M * N)) return W8A8_ERR_NULL;
+  // the kernels address each operand tile with 32-bit offsets: BM x K bytes
+  if (!aligned(qa, 16) || !aligned(qb, 16) || !aligned(out, 16)) return W8A8_ERR_ALIGN;
+  return W8A8_OK;
+}
+
+w8a8_status_t check_quant(const void* x, int dtype, int64_t rows, int64_t cols,
+                          const float* col_scale, const int8_t* q, const float* row_scale) {
+  if (!valid_dtype(dtype)) return W8A8_ERR_DTYPE;
+  if (rows < 0 || cols < 0 || rows >= kMaxRows || cols > kMaxQuantCols || cols % 16 != 0)
+    return W8A8_ERR_SHAPE;
+  // a pointer may be NULL only when its array is empty
+  if ((!x && rows * cols) || (!q && rows * cols) || (!col_scale && cols) || (!row_scale && rows))
+    return W8A8_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(col_scale, 16) || !aligned(row_scale, 4))
+    return W8A8_ERR_ALIGN;
+  return W8A8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w8a8_abi_version(void) { return W8A8_ABI_VERSION; }
+
+const char* w8a8_status_str(int status) {
+  switch (status) {
+    case W8A8_OK: return "ok";
+    case W8A8_ERR_NULL: return "a required pointer is NULL";
+    case W8A8_ERR_SHAPE: return "invalid shape (negative, too large, or not a required multiple)";
+    case W8A8_ERR_ALIGN: return "pointer not aligned as required (16 bytes for matrices)";
+    case W8A8_ERR_DTYPE: return "unknown dtype code";
+    case W8A8_ERR_ARG: return "argument out of range";
+    case W8A8_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+w8a8_status_t w8a8_channel_amax(const void* x, int dtype, int64_t rows, int64_t cols,
+                                float* amax, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return W8A8_ERR_DTYPE;
+  if (rows < 0 || cols < 1 || cols % 8 != 0 || rows >= ((int64_t)1 << 40)) return W8A8_ERR_SHAPE;
+  if ((!x && rows) || !amax) return W8A8_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(amax, 4)) return W8A8_ERR_ALIGN;
+  return hip_status(w8a8::launch_channel_amax(x, dtype == W8A8_BF16, rows, cols, amax, stream));
+}
+
+w8a8_status_t w8a8_smooth_factors(const float* amax_x, const float* amax_w, int64_t K,
+                                  double alpha, float* s, float* inv_s, hipStream_t stream) {
+  if (K < 0 || K >= kMaxRows) return W8A8_ERR_SHAPE;
+  if (K && (!amax_x || !amax_w || !s || !inv_s)) return W8A8_ERR_NULL;
+  if (!(alpha >= 0.0 && alpha <= 1.0)) return W8A8_ERR_ARG;  // also rejects NaN
+  if (!aligned(amax_x, 4) || !aligned(amax_w, 4) || !aligned(s, 4) || !aligned(inv_s, 4))
+    return W8A8_ERR_ALIGN;
+  return hip_status(w8a8::launch_smooth_factors(amax_x, amax_w, K, alpha, s, inv_s, stream));
+}
+
+w8a8_status_t w8a8_scale_quant_rows(const void* x, int dtype, int64_t rows, int64_t cols,
+                                    const float* col_scale, int8_t* q, float* row_scale,
+                                    hipStream_t stream) {
+  const w8a8_status_t st = check_quant(x, dtype, rows, cols, col_scale, q, row_scale);
+  if (st != W8A8_OK) return st;
+  return hip_status(w8a8::launch_scale_quant_rows(x, dtype == W8A8_BF16, rows, cols, col_scale,
+                                                  q, row_scale, stream));
+}
+
+w8a8_status_t w8a8_gemm_i32(const int8_t* qa, const int8_t* qb, int32_t* c, int64_t M, int64_t N,
+                            int64_t K, hipStream_t stream) {
+  const w8a8_status_t st = check_gemm(qa, qb, c, M, N, K);
+  if (st != W8A8_OK) return st;
+  return hip_status(w8a8::launch_gemm(qa, qb, M, N, K, nullptr, nullptr, c, 0, stream));
+}
+
+w8a8_status_t w8a8_gemm_dequant(const int8_t* qa, const float* sa, const int8_t* qb,
+                                const float* sb, void* y, int out_dtype, int64_t M, int64_t N,
+                                int64_t K, hipStream_t stream) {
+  w8a8_status_t st = check_gemm(qa, qb, y, M, N, K);
+  if (st != W8A8_OK) return st;
+  if ((!sa && M) || (!sb && N)) return W8A8_ERR_NULL;
+  if (!valid_dtype(out_dtype)) return W8A8_ERR_DTYPE;
+  if (!aligned(sa, 4) || !aligned(sb, 16)) return W8A8_ERR_ALIGN;
+  return hip_status(w8a8::launch_gemm(qa, qb, M, N, K, sa, sb, y, out_dtype == W8A8_BF16 ? 2 : 1,
+                                      stream));
+}
+
+size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K) {
+  if (M < 0 || K < 0) return 0;
+  return round_up((size_t)M * (size_t)K, kWsAlign) + round_up((size_t)M * 4, kWsAlign);
+}
+
+w8a8_status_t w8a8_linear(const void* x, int dtype, const float* inv_s, const int8_t* qw,
+                          const float* sw, void* y, int64_t M, int64_t N, int64_t K,
+                          void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return W8A8_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 0) return W8A8_ERR_SHAPE;
+  if (!workspace || (!sw && N)) return W8A8_ERR_NULL;
+  if (!aligned(workspace, kWsAlign)) return W8A8_ERR_ALIGN;
+  if (ws_bytes < w8a8_linear_workspace_bytes(M, K)) return W8A8_ERR_ARG;
+  int8_t* qx = (int8_t*)workspace;
+  float* sx = (float*)((char*)workspace + round_up((size_t)M * (size_t)K, kWsAlign));
+  w8a8_status_t st = check_quant(x, dtype, M, K, inv_s, qx, sx);
+  if (st != W8A8_OK) return st;
+  st = check_gemm(qx, qw, y, M, N, K);
+  if (st != W8A8_OK) return st;
+  if (!aligned(sw, 16)) return W8A8_ERR_ALIGN;
+  hipError_t e = w8a8::launch_scale_quant_rows(x, dtype == W8A8_BF16, M, K, inv_s, qx, sx, stream);
+  if (e != hipSuccess) return W8A8_ERR_HIP;
+  return hip_status(w8a8::launch_gemm(qx, qw, M, N, K, sx, sw, y, dtype == W8A8_BF16 ? 2 : 1,
+                                      stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,35 @@
+// Internal declarations shared by the HIP sources of libw8a8 (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w8a8 {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// Launchers: arguments are validated by the C ABI layer before these run.
+hipError_t launch_channel_amax(const void* x, bool bf16, int64_t rows, int64_t cols, float* amax,
+                               hipStream_t st);
+hipError_t launch_smooth_factors(const float* ax, const float* aw, int64_t K, double alpha,
+                                 float* s, float* inv_s, hipStream_t st);
+hipError_t launch_scale_quant_rows(const void* x, bool bf16, int64_t rows, int64_t cols,
+                                   const float* col_scale, int8_t* q, float* row_scale,
+                                   hipStream_t st);
+// out_mode: 0 = int32 accumulators, 1 = fp16 dequant, 2 = bf16 dequant
+hipError_t launch_gemm(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N, int64_t K,
+                       const float* sa, const float* sb, void* out, int out_mode,
+                       hipStream_t st);
+
+// Widening of one 16-bit storage value to fp32 (exact).
+__device__ __forceinline__ float widen16(unsigned short h, bool bf16) {
+  if (bf16) return __uint_as_float(((unsigned)h) << 16);
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+}  // namespace w8a8
