@@ -9,55 +9,80 @@
 //   Y[t, k] = out(fp32(fp32(C[t, k]) * sa[t]) * sb[k])    (IEEE fp32, RNE)
 //
 // Operands: qa = activation codes, M x K; qb = weight codes, N x K; both K
-// contiguous ("TN").  Every MFMA is v_mfma_i32_32x32x32_i8 with the weight
-// fragment as its first operand (32 output channels x 32 k) and the activation
+// contiguous.  Every MFMA is v_mfma_i32_32x32x32_i8 with the weight fragment
+// as its first operand (32 output channels x 32 k) and the activation
 // fragment as its second (32 k x 32 tokens), so that each lane's four
 // consecutive accumulator registers hold four consecutive output channels of
 // one token: the epilogue writes 4 fp16 / bf16 (8 B) or 4 int32 (16 B) per
 // lane per register group.  Integer accumulation is exact and order free.
 //
-// Tiling: a 256-thread block (4 waves, one per SIMD) owns a BM x BN output
-// tile (tokens x channels); the waves form a 2 x 2 grid, each with a
-// (BM/2) x (BN/2) register tile of 32 x 32 MFMA blocks, accumulators in the
-// accumulation registers.  The K loop steps 128 bytes at a time through two
-// LDS stages: while the MFMAs consume stage s, the global loads for stage s+1
-// are in flight in registers, then written to the other stage; one barrier per
-// step.  In LDS each tile row is 128 B = 8 chunks of 16 B, and chunk c of row
-// r is stored at chunk slot c ^ ((r >> 1) & 7): the 16 lanes of any quarter
-// wave then touch 16 distinct 16-byte bank groups both when the fragment
-// reads walk down 16 rows at one k and when the stores walk along rows.
+// Block: 256 threads (4 waves, one per SIMD) own a BM x BN output tile
+// (tokens x channels); the waves form a 2 x 2 grid, each holding a
+// (BM/2) x (BN/2) register tile of 32 x 32 MFMA blocks in the accumulation
+// registers.
 //
-// Global loads are buffer loads against a resource that ends at the last valid
-// row of the tile, so rows past M or N read as zero (no clamping, no
-// branches); a K that is not a multiple of 128 zeroes its tail chunks the same
-// way.  Blocks are dispatched round-robin over the 8 XCDs; the tile index is
-// remapped so that each XCD (with its own L2) works on a contiguous run of
-// tiles, ordered token-tile fastest within groups of 8 token tiles, so the
-// CUs of one XCD share both operand panels.
+// K pipeline: K advances 64 bytes per stage through NST = 4 LDS slots.
+// Operand rows go from global memory straight into LDS with buffer loads in
+// LDS mode (16 B per lane, each wave instruction fills 1 KiB of LDS); the
+// prologue fills all four slots and every stage barrier refills the slot just
+// consumed with the stage four ahead, so up to three stages are in flight
+// while one is computed and a wave never holds global data in registers.  Per stage
+// a wave reads its fragments for the two 32-deep k steps with 128-bit LDS
+// reads and issues 2 x (BN/64) x (BM/64) MFMAs.  The fragment reads are
+// software pipelined: the second k step's fragments are read while the first
+// step's MFMAs run, and the next stage's first fragments are read (after the
+// stage barrier) while the second step's MFMAs run.  One barrier per stage;
+// it is a plain s_barrier (no memory fence), with the needed waits explicit:
+// each wave waits for its own LDS-mode loads of the next stage (vmcnt) and
+// for its own LDS reads of the slot that is about to be refilled (lgkmcnt).
+//
+// LDS layout: a tile row is 64 B = 4 chunks of 16 B; four rows share one
+// 256-byte bank window.  Chunk c of row r sits at chunk slot c ^ ((r >> 2) & 3)
+// of that row, so the 16 lanes of a quarter wave reading one k chunk down 16
+// consecutive rows hit 16 distinct 16-byte bank groups.  The loads realize
+// the swizzle by choosing, per lane, which global chunk lands in its slot.
+//
+// Edges: the buffer resource of each operand tile ends at its last valid row,
+// so rows past M or N load as zero; chunks past K use an out-of-range offset
+// and load as zero too.  Blocks are dispatched round-robin over the 8 XCDs;
+// tile indices are remapped so each XCD (own L2) gets a contiguous run of
+// tiles, ordered token-tile fastest in groups of 8 token tiles.
 #include "common.h"
 
 namespace w8a8 {
 
 namespace {
 
-constexpr int kBK = 128;         // bytes of K per LDS stage
-constexpr int kThreads = 256;    // 4 waves
 constexpr int kGroupM = 8;       // token tiles per ordering group
 constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
 constexpr int kOob = 0x40000000;  // voffset that is out of range for every resource here
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const int8_t* base, unsigned bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, (int)kRsrcWord3);
 }
 
-__device__ __forceinline__ v4i load16(rsrc_t r, int voff, int soff) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return (row << 7) + ((chunk ^ ((row >> 1) & 7)) << 4);
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
+}
+
+// Hardware barrier without a memory fence.  The asm memory clobber keeps the
+// compiler from moving LDS or global accesses across it, and the scheduling
+// barriers keep every other instruction (MFMAs included) on its side, so each
+// half-iteration is its own scheduling region.
+__device__ __forceinline__ void block_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 __device__ __forceinline__ unsigned short f32_to_bf16_rne(float f) {
@@ -85,43 +110,98 @@ __device__ __forceinline__ void tile_of(int bid, int m_tiles, int n_tiles, int& 
   tn = in_g / gsize;
 }
 
-// OUT: 0 = int32 C, 1 = fp16 Y, 2 = bf16 Y
-template <int BM, int BN, int OUT>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          amdgpu_waves_per_eu(1, 1))) void
+// Scheduling hint for the compiler: interleave one MFMA with up to one LDS
+// read and one global (LDS-mode) load, so that no wave stalls on a memory
+// queue while its matrix pipe idles.  I counts MFMAs; memory instructions are
+// front-loaded so their latency overlaps the remaining MFMAs.
+template <int I, int NMFMA, int NDS, int NVM>
+__device__ __forceinline__ void interleave() {
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+  if constexpr (I < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+  if constexpr (I < NVM) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one VMEM
+  if constexpr (I + 1 < NMFMA) interleave<I + 1, NMFMA, NDS, NVM>();
+}
+
+// OUT: 0 = int32 C, 1 = fp16 Y, 2 = bf16 Y.  The block has WGM x WGN waves;
+// K advances BK bytes per stage through NST LDS slots.
+template <int BM, int BN, int BK, int NST, int WGM, int WGN, int OUT>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * WGM * WGN, 64 * WGM * WGN),
+                          amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4))) void
 k_gemm_i8(const int8_t* __restrict__ qa, const int8_t* __restrict__ qb, int M, int N, int K,
           const float* __restrict__ sa, const float* __restrict__ sb, void* __restrict__ out,
           int m_tiles, int n_tiles) {
-  constexpr int WM = BM / 2, WN = BN / 2;  // wave tile (tokens, channels)
+  constexpr int NW = WGM * WGN;                 // waves per block
+  constexpr int WM = BM / WGM, WN = BN / WGN;   // wave tile (tokens, channels)
   constexpr int FM = WM / 32, FN = WN / 32;
-  constexpr int LA = BM / 32, LB = BN / 32;  // 16-byte loads per thread per stage
-  constexpr int STAGE = (BM + BN) * kBK;
-  __shared__ __attribute__((aligned(16))) int8_t lds[2 * STAGE];
+  constexpr int CPR = BK / 16;                  // 16-byte chunks per LDS row
+  constexpr int RPW = 16 / CPR;                 // rows per 256-byte bank window
+  constexpr int RPI = 1024 / BK;                // rows filled by one LDS-mode wave load
+  constexpr int KK = BK / 32;                   // 32-deep MFMA k steps per stage
+  constexpr int LA = BM / RPI / NW;             // LDS-mode loads per wave per stage, activations
+  constexpr int LB = BN / RPI / NW;             // ... weights
+  constexpr int L = LA + LB;
+  constexpr int SLOT = (BM + BN) * BK;          // bytes per LDS stage
+  static_assert(LA >= 1 && LB >= 1 && LA * RPI * NW == BM && LB * RPI * NW == BN &&
+                FM >= 1 && FN >= 1 && KK % 2 == 0, "unsupported tile");
+  static_assert(NST >= 2 && (NST - 1) * L < 64, "unsupported pipeline depth");
+  __shared__ __attribute__((aligned(1024))) int8_t lds[NST * SLOT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
 
   int tm, tn;
   tile_of(blockIdx.x, m_tiles, n_tiles, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
-  const rsrc_t ra = make_rsrc(qa + (int64_t)m0 * K, (unsigned)rows_a * (unsigned)K);
-  const rsrc_t rb = make_rsrc(qb + (int64_t)n0 * K, (unsigned)rows_b * (unsigned)K);
+  const rsrc_t ra = make_rsrc(qa + (int64_t)m0 * K, (unsigned)min(BM, M - m0) * (unsigned)K);
+  const rsrc_t rb = make_rsrc(qb + (int64_t)n0 * K, (unsigned)min(BN, N - n0) * (unsigned)K);
 
-  // this thread's load slots: rows i*32 + (tid >> 3), chunk c = tid & 7
-  const int c = tid & 7;
-  const int r_in = tid >> 3;
-  const int st_off = swz(r_in, c);  // + i * 32 * 128 for slot i
-  int voff_a[LA], voff_b[LB];
+  // LDS-mode load i of this wave fills LDS rows (i * NW + wave) * RPI + lane / CPR,
+  // chunk slot lane % CPR, with the global chunk slot ^ ((row / RPW) % CPR).
+  const int lrow = lane / CPR, lslot = lane % CPR;
+  int voff_a[LA], voff_b[LB], kc_a[LA], kc_b[LB];
 #pragma unroll
-  for (int i = 0; i < LA; ++i) voff_a[i] = (i * 32 + r_in) * K + c * 16;
+  for (int i = 0; i < LA; ++i) {
+    const int row = (i * NW + wave) * RPI + lrow;
+    kc_a[i] = (lslot ^ ((row / RPW) % CPR)) << 4;
+    voff_a[i] = row * K + kc_a[i];
+  }
 #pragma unroll
-  for (int i = 0; i < LB; ++i) voff_b[i] = (i * 32 + r_in) * K + c * 16;
+  for (int i = 0; i < LB; ++i) {
+    const int row = (i * NW + wave) * RPI + lrow;
+    kc_b[i] = (lslot ^ ((row / RPW) % CPR)) << 4;
+    voff_b[i] = row * K + kc_b[i];
+  }
 
-  // fragment read offsets (row part; the swizzle depends only on lane & 31)
+  const int nk = (K + BK - 1) / BK;
+
+  // Issue this wave's LDS-mode loads of stage `st`.  A stage past the end
+  // (st >= nk) is issued with out-of-range offsets: it moves no data, keeps
+  // the per-stage load count constant (so one vmcnt value serves every
+  // iteration) and only touches a slot no later stage uses.
+  auto dma = [&](int st) {
+    const int k0 = st * BK;
+    int8_t* slot = lds + (st % NST) * SLOT;
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+      const int vo = (k0 + kc_a[i] >= K) ? kOob : voff_a[i];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (lds_void_t*)(slot + (i * NW + wave) * 1024), 16, vo, k0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      const int vo = (k0 + kc_b[i] >= K) ? kOob : voff_b[i];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb, (lds_void_t*)(slot + BM * BK + (i * NW + wave) * 1024), 16, vo, k0, 0, 0);
+    }
+  };
+
+  // fragment reads: lane reads row (base + (lane & 31)), k chunk 2 * kk + (lane >> 5);
+  // bases are multiples of 32 rows, so the swizzle depends on lane & 31 only
   const int fr = lane & 31, fk = lane >> 5;
-  const int fsw = (fr >> 1) & 7;
+  const int fsw = (fr / RPW) % CPR;
+  const int off_a = (wm * WM + fr) * BK;
+  const int off_b = BM * BK + (wn * WN + fr) * BK;
 
   v16i acc[FN][FM];
 #pragma unroll
@@ -129,53 +209,69 @@ k_gemm_i8(const int8_t* __restrict__ qa, const int8_t* __restrict__ qb, int M, i
 #pragma unroll
     for (int b = 0; b < FM; ++b) acc[a][b] = v16i{};
 
-  const int nk = (K + kBK - 1) / kBK;
-  v4i ga[LA], gb[LB];
-
-  auto gload = [&](int kt) {
-    const int k0 = kt * kBK;
-    const bool tail = (k0 + c * 16) >= K;
+  v4i fb0[FN], fa0[FM], fb1[FN], fa1[FM];
+  auto read_frags = [&](int st, int kk, v4i* fb, v4i* fa) {
+    const int8_t* slot = lds + (st % NST) * SLOT;
+    const int ch = ((2 * kk + fk) ^ fsw) << 4;
 #pragma unroll
-    for (int i = 0; i < LA; ++i) ga[i] = load16(ra, tail ? kOob : voff_a[i], k0);
+    for (int a = 0; a < FN; ++a) fb[a] = *(const v4i*)(slot + off_b + a * 32 * BK + ch);
 #pragma unroll
-    for (int i = 0; i < LB; ++i) gb[i] = load16(rb, tail ? kOob : voff_b[i], k0);
+    for (int b = 0; b < FM; ++b) fa[b] = *(const v4i*)(slot + off_a + b * 32 * BK + ch);
   };
-  auto lstore = [&](int s) {
-    int8_t* base = lds + s * STAGE;
+  auto mfmas = [&](const v4i* fb, const v4i* fa) {
 #pragma unroll
-    for (int i = 0; i < LA; ++i) *(v4i*)(base + i * 32 * kBK + st_off) = ga[i];
-#pragma unroll
-    for (int i = 0; i < LB; ++i) *(v4i*)(base + BM * kBK + i * 32 * kBK + st_off) = gb[i];
-  };
-
-  if (nk > 0) {
-    gload(0);
-    lstore(0);
-    __syncthreads();
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    const int s = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const int8_t* sA = lds + s * STAGE;
-    const int8_t* sB = sA + BM * kBK;
-#pragma unroll
-    for (int kk = 0; kk < kBK / 32; ++kk) {
-      const int ch = ((2 * kk + fk) ^ fsw) << 4;
-      v4i fb[FN], fa[FM];
-#pragma unroll
-      for (int a = 0; a < FN; ++a)
-        fb[a] = *(const v4i*)(sB + ((wn * WN + a * 32 + fr) << 7) + ch);
+    for (int a = 0; a < FN; ++a)
 #pragma unroll
       for (int b = 0; b < FM; ++b)
-        fa[b] = *(const v4i*)(sA + ((wm * WM + b * 32 + fr) << 7) + ch);
+        acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[a], fa[b], acc[a][b], 0, 0, 0);
+  };
+
+  // Pipeline (stage s lives in slot s % NST).  Iteration kt computes stage kt
+  // as KK steps of 32-deep k; the fragments of step kk+1 are read while the
+  // MFMAs of step kk run.  Before the last step the stage barrier is taken:
+  // each wave first waits for its own loads of stage kt+1 (stages kt+2 ..
+  // kt+NST-1 may stay in flight) and for its own reads of slot kt, so after
+  // the barrier stage kt+1 is visible and slot kt is free; the loads of stage
+  // kt+NST go into it while the last step's MFMAs run and the next stage's
+  // first fragments are read.
+  if (nk > 0) {
 #pragma unroll
-      for (int a = 0; a < FN; ++a)
+    for (int st = 0; st < NST; ++st) dma(st);
+    wait_vmcnt<(NST - 1) * L>();  // stage 0 landed
+    block_barrier();
+    read_frags(0, 0, fb0, fa0);
+    for (int kt = 0; kt < nk - 1; ++kt) {
 #pragma unroll
-        for (int b = 0; b < FM; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[a], fa[b], acc[a][b], 0, 0, 0);
+      for (int kk = 0; kk < KK; ++kk) {
+        v4i* cb = (kk & 1) ? fb1 : fb0;
+        v4i* ca = (kk & 1) ? fa1 : fa0;
+        v4i* nb = (kk & 1) ? fb0 : fb1;
+        v4i* na = (kk & 1) ? fa0 : fa1;
+        if (kk + 1 < KK) {
+          read_frags(kt, kk + 1, nb, na);
+          mfmas(cb, ca);
+          interleave<0, FN * FM, FN + FM, 0>();
+        } else {
+          wait_vmcnt<(NST - 2) * L>();  // stage kt+1 landed
+          wait_lgkmcnt0();              // this wave's reads of slot kt are done
+          block_barrier();              // every wave: stage kt+1 landed, slot kt free
+          dma(kt + NST);
+          read_frags(kt + 1, 0, nb, na);
+          mfmas(cb, ca);
+          interleave<0, FN * FM, FN + FM, L>();
+        }
+      }
     }
-    if (kt + 1 < nk) lstore(s ^ 1);
-    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      v4i* cb = (kk & 1) ? fb1 : fb0;
+      v4i* ca = (kk & 1) ? fa1 : fa0;
+      v4i* nb = (kk & 1) ? fb0 : fb1;
+      v4i* na = (kk & 1) ? fa0 : fa1;
+      if (kk + 1 < KK) read_frags(nk - 1, kk + 1, nb, na);
+      mfmas(cb, ca);
+    }
+    wait_vmcnt<0>();  // no LDS-mode load may outlive the block's LDS
   }
 
   // epilogue: lane holds, for register group g, channels n .. n+3 of token m
@@ -217,23 +313,23 @@ k_gemm_i8(const int8_t* __restrict__ qa, const int8_t* __restrict__ qb, int M, i
   }
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int BK, int NST, int WGM, int WGN>
 hipError_t launch_tile(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N, int64_t K,
                        const float* sa, const float* sb, void* out, int mode, hipStream_t st) {
   const int mt = (int)((M + BM - 1) / BM), nt = (int)((N + BN - 1) / BN);
-  const dim3 grid((unsigned)(mt * nt)), block(kThreads);
+  const dim3 grid((unsigned)(mt * nt)), block(64 * WGM * WGN);
   switch (mode) {
     case 0:
-      hipLaunchKernelGGL((k_gemm_i8<BM, BN, 0>), grid, block, 0, st, qa, qb, (int)M, (int)N,
-                         (int)K, sa, sb, out, mt, nt);
+      hipLaunchKernelGGL((k_gemm_i8<BM, BN, BK, NST, WGM, WGN, 0>), grid, block, 0, st, qa, qb, (int)M,
+                         (int)N, (int)K, sa, sb, out, mt, nt);
       break;
     case 1:
-      hipLaunchKernelGGL((k_gemm_i8<BM, BN, 1>), grid, block, 0, st, qa, qb, (int)M, (int)N,
-                         (int)K, sa, sb, out, mt, nt);
+      hipLaunchKernelGGL((k_gemm_i8<BM, BN, BK, NST, WGM, WGN, 1>), grid, block, 0, st, qa, qb, (int)M,
+                         (int)N, (int)K, sa, sb, out, mt, nt);
       break;
     default:
-      hipLaunchKernelGGL((k_gemm_i8<BM, BN, 2>), grid, block, 0, st, qa, qb, (int)M, (int)N,
-                         (int)K, sa, sb, out, mt, nt);
+      hipLaunchKernelGGL((k_gemm_i8<BM, BN, BK, NST, WGM, WGN, 2>), grid, block, 0, st, qa, qb, (int)M,
+                         (int)N, (int)K, sa, sb, out, mt, nt);
       break;
   }
   return hipGetLastError();
@@ -260,10 +356,15 @@ hipError_t launch_gemm(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N,
     const double score = fill * mfill * cands[i].eff;
     if (score > best_score + 1e-9) { best_score = score; best = i; }
   }
+#ifndef GEMM_W256
+#define GEMM_W256 128, 2, 2, 4
+#define GEMM_W256x128 128, 3, 4, 2
+#define GEMM_W128 128, 4, 2, 2
+#endif
   switch (best) {
-    case 0: return launch_tile<256, 256>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
-    case 1: return launch_tile<256, 128>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
-    default: return launch_tile<128, 128>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
+    case 0: return launch_tile<256, 256, GEMM_W256>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
+    case 1: return launch_tile<256, 128, GEMM_W256x128>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
+    default: return launch_tile<128, 128, GEMM_W128>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
   }
 }
 
