@@ -7,16 +7,21 @@
 // HBM-bound streaming kernel.  The absolute value of an fp16 or bf16 number is
 // its bit pattern with the sign bit cleared, and for non-negative finite
 // values the order of the bit patterns (as unsigned integers) is the order of
-// the values.  So the whole reduction runs on integers: AND with 0x7fff7fff
-// and a packed unsigned 16-bit max per pair of elements, exact by construction.
+// the values.  So the reduction runs on integers: AND with 0x7fff7fff and a
+// packed unsigned 16-bit max per pair of elements, exact by construction.
 // The block result is widened to fp32 (exact) and folded into the output with
 // an unsigned atomic max on the fp32 bit pattern, which orders non-negative
 // floats the same way.
 //
-// Work split: a wave reads 64 lanes x 16 B = 512 consecutive columns of one
-// row per load (fully coalesced 1 KiB), the 4 waves of a block take
-// interleaved rows of the same 512-column strip, and each lane keeps U loads
-// in flight.  Blocks split the rows so the grid has a few thousand blocks.
+// Work split: a block owns a strip of 64 columns (128 bytes of every row) and
+// a tall range of rows.  One wave load covers 8 rows x 128 B (8 lanes per row,
+// full cache lines); the 4 waves take interleaved groups of 8 rows and each
+// lane keeps U loads in flight.  At the end the lanes that hold the same
+// columns are folded with cross-lane max, then the 4 waves through LDS, and
+// 64 lanes issue one coalesced atomic max each (one per column).  Row ranges
+// are sized so the grid has about 1024 blocks while each column receives at
+// most a few dozen atomics: the atomics, not the loads, are what a finer
+// split would pay for.
 #include "common.h"
 
 namespace w8a8 {
@@ -26,11 +31,19 @@ namespace {
 constexpr int kAmaxThreads = 256;
 constexpr int kAmaxWaves = kAmaxThreads / kWave;
 constexpr int kAmaxUnroll = 8;
+constexpr int kRowsPerLoad = 8;                                     // rows per wave load
+constexpr int kRowsPerGroup = kRowsPerLoad * kAmaxWaves;            // 32 rows per block step
+constexpr int kRowsPerBatch = kRowsPerGroup * kAmaxUnroll;          // 256 rows in flight
 
 __device__ __forceinline__ unsigned pmax16(unsigned a, unsigned b) {
   u16x2 x = __builtin_bit_cast(u16x2, a);
   u16x2 y = __builtin_bit_cast(u16x2, b);
   return __builtin_bit_cast(unsigned, __builtin_elementwise_max(x, y));
+}
+
+__device__ __forceinline__ v4u vmax(v4u m, v4u v) {
+  return v4u{pmax16(m.x, v.x & 0x7fff7fffu), pmax16(m.y, v.y & 0x7fff7fffu),
+             pmax16(m.z, v.z & 0x7fff7fffu), pmax16(m.w, v.w & 0x7fff7fffu)};
 }
 
 template <bool BF16>
@@ -40,63 +53,53 @@ __global__ __launch_bounds__(kAmaxThreads) void k_channel_amax(const v4u* __rest
                                                                unsigned* __restrict__ amax_bits) {
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
-  const int64_t chunk = (int64_t)blockIdx.x * kWave + lane;  // 16-byte column chunk
+  const int sub = lane / 8;                                   // row within a wave load
+  const int64_t chunk = (int64_t)blockIdx.x * 8 + (lane % 8);  // 16-byte column chunk
   const int64_t r_begin = (int64_t)blockIdx.y * rows_per_block;
   const int64_t r_end = min(rows, r_begin + rows_per_block);
   const bool active = chunk < cols8;
 
-  unsigned m0 = 0, m1 = 0, m2 = 0, m3 = 0;
+  v4u m = {0u, 0u, 0u, 0u};
   if (active) {
     const v4u* p = x + chunk;
-    int64_t r = r_begin + wave;
-    // full groups of U rows per wave, no per-load bounds test
-    for (; r + (int64_t)(kAmaxUnroll - 1) * kAmaxWaves < r_end; r += kAmaxUnroll * kAmaxWaves) {
+    int64_t r = r_begin + wave * kRowsPerLoad + sub;
+    // full batches: U loads per lane, no per-load bounds test
+    for (; r + (int64_t)(kAmaxUnroll - 1) * kRowsPerGroup < r_end; r += kRowsPerBatch) {
       v4u v[kAmaxUnroll];
 #pragma unroll
       for (int u = 0; u < kAmaxUnroll; ++u)
-        v[u] = __builtin_nontemporal_load(p + (r + (int64_t)u * kAmaxWaves) * cols8);
+        v[u] = __builtin_nontemporal_load(p + (r + (int64_t)u * kRowsPerGroup) * cols8);
 #pragma unroll
-      for (int u = 0; u < kAmaxUnroll; ++u) {
-        m0 = pmax16(m0, v[u].x & 0x7fff7fffu);
-        m1 = pmax16(m1, v[u].y & 0x7fff7fffu);
-        m2 = pmax16(m2, v[u].z & 0x7fff7fffu);
-        m3 = pmax16(m3, v[u].w & 0x7fff7fffu);
-      }
+      for (int u = 0; u < kAmaxUnroll; ++u) m = vmax(m, v[u]);
     }
-    for (; r < r_end; r += kAmaxWaves) {
-      v4u v = __builtin_nontemporal_load(p + r * cols8);
-      m0 = pmax16(m0, v.x & 0x7fff7fffu);
-      m1 = pmax16(m1, v.y & 0x7fff7fffu);
-      m2 = pmax16(m2, v.z & 0x7fff7fffu);
-      m3 = pmax16(m3, v.w & 0x7fff7fffu);
+    for (; r < r_end; r += kRowsPerGroup) m = vmax(m, __builtin_nontemporal_load(p + r * cols8));
+  }
+  // fold the 8 row lanes that hold the same chunk (lanes l, l^8, l^16, l^32)
+#pragma unroll
+  for (int off = 8; off < kWave; off <<= 1) {
+    m.x = pmax16(m.x, (unsigned)__shfl_xor((int)m.x, off, kWave));
+    m.y = pmax16(m.y, (unsigned)__shfl_xor((int)m.y, off, kWave));
+    m.z = pmax16(m.z, (unsigned)__shfl_xor((int)m.z, off, kWave));
+    m.w = pmax16(m.w, (unsigned)__shfl_xor((int)m.w, off, kWave));
+  }
+  // fold the waves through LDS: wave w's lanes 0..7 hold its 64 column maxima
+  __shared__ unsigned short part[kAmaxWaves][64];
+  if (lane < 8) {
+    const unsigned w4[4] = {m.x, m.y, m.z, m.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      part[wave][lane * 8 + 2 * i] = (unsigned short)(w4[i] & 0xffffu);
+      part[wave][lane * 8 + 2 * i + 1] = (unsigned short)(w4[i] >> 16);
     }
   }
-
-  // combine the waves of the block through LDS
-  __shared__ uint4 part[kAmaxWaves][kWave];
-  part[wave][lane] = make_uint4(m0, m1, m2, m3);
   __syncthreads();
-  if (wave != 0 || !active) return;
+  if (wave != 0) return;
+  unsigned short b = part[0][lane];
 #pragma unroll
-  for (int w = 1; w < kAmaxWaves; ++w) {
-    uint4 o = part[w][lane];
-    m0 = pmax16(m0, o.x);
-    m1 = pmax16(m1, o.y);
-    m2 = pmax16(m2, o.z);
-    m3 = pmax16(m3, o.w);
-  }
-  const unsigned m[4] = {m0, m1, m2, m3};
-  unsigned* out = amax_bits + chunk * 8;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const unsigned short bits = (unsigned short)(m[i] >> (16 * h));
-      if (bits == 0) continue;  // +0 never raises a non-negative running max
-      const float f = widen16(bits, BF16);
-      atomicMax(out + 2 * i + h, __float_as_uint(f));
-    }
-  }
+  for (int w = 1; w < kAmaxWaves; ++w) b = max(b, part[w][lane]);
+  const int64_t col = (int64_t)blockIdx.x * 64 + lane;
+  if (col < cols8 * 8 && b != 0)  // +0 never raises a non-negative running max
+    atomicMax(amax_bits + col, __float_as_uint(widen16(b, BF16)));
 }
 
 }  // namespace
@@ -105,19 +108,16 @@ hipError_t launch_channel_amax(const void* x, bool bf16, int64_t rows, int64_t c
                                hipStream_t st) {
   if (rows == 0) return hipSuccess;
   const int64_t cols8 = cols / 8;
-  const int64_t strips = (cols8 + kWave - 1) / kWave;
-  // aim for ~4096 blocks; each block covers at least one unrolled group of rows
-  const int64_t min_rows = (int64_t)kAmaxUnroll * kAmaxWaves;
-  int64_t row_blocks = (4096 + strips - 1) / strips;
+  const int64_t strips = (cols8 + 7) / 8;
+  // about 1024 blocks, at most 32 row ranges per strip, at least one 32-row step each
+  int64_t row_blocks = (1024 + strips - 1) / strips;
+  if (row_blocks > 32) row_blocks = 32;
+  const int64_t max_rb = (rows + kRowsPerGroup - 1) / kRowsPerGroup;
+  if (row_blocks > max_rb) row_blocks = max_rb;
+  if (row_blocks < 1) row_blocks = 1;
   int64_t rpb = (rows + row_blocks - 1) / row_blocks;
-  rpb = ((rpb + min_rows - 1) / min_rows) * min_rows;
+  rpb = (rpb + kRowsPerGroup - 1) / kRowsPerGroup * kRowsPerGroup;
   row_blocks = (rows + rpb - 1) / rpb;
-  if (row_blocks > 65535) {
-    row_blocks = 65535;
-    rpb = (rows + row_blocks - 1) / row_blocks;
-    rpb = ((rpb + min_rows - 1) / min_rows) * min_rows;
-    row_blocks = (rows + rpb - 1) / rpb;
-  }
   dim3 grid((unsigned)strips, (unsigned)row_blocks);
   if (bf16)
     hipLaunchKernelGGL(k_channel_amax<true>, grid, dim3(kAmaxThreads), 0, st,

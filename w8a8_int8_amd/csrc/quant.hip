@@ -5,25 +5,32 @@
 // symmetric grid [-127, 127], per-row scales and round-half-even are the
 // readings stated in the library header.  Per row t:
 //   v_j = fp32(x[t, j]) * c_j;  m = max_j |v_j|;  delta = m / 127;  r = 127 / m;
-//   q_j = clamp(rint(v_j * r), -127, 127)
-// Each arrow is one IEEE fp32 operation (no contraction; there is no add to
-// fuse), divisions are the correctly rounded ones, rint is round-half-even.
+//   q_j = round_half_even(v_j * r)   (always within [-127, 127])
+// Each step is one IEEE fp32 operation (no contraction), the divisions are
+// the correctly rounded ones, and the rounding to an integer is done by an
+// fp32 add of 1.5 * 2^23, which rounds to nearest even like rint does.
 //
 // HBM-bound: 2 B read + 1 B written per element (+ 4 B per row).  A group of
 // G threads (a multiple of the 64-wide wavefront, at most 1024) owns a row:
-// thread g holds the 16-byte chunks g, g + G, ... (CPT of them), so every wave
-// load is 1 KiB of consecutive bytes and every wave store 512 B.  The row is
-// kept in registers between the max pass and the quantize pass, so x is read
-// from HBM exactly once.  A block handles R consecutive rows with the same
-// column ownership: the column scales are loaded once per block (they stay
-// L2 resident) and the R rows' loads are all in flight before the first
-// reduction.  The row max is a wave-level butterfly followed by one LDS round
-// across the waves of the block.
+// thread g holds the 16-byte chunks g, g + G, ... (CPT of them, normally 2),
+// so every wave load is 1 KiB of consecutive bytes and every wave store
+// 512 B.  The scaled row slice stays in registers between the max pass and
+// the quantize pass, so x is read from HBM exactly once.  A block handles R
+// consecutive rows with the same column ownership (the column scales are
+// loaded once per block and stay L2 resident) and issues all of its row loads
+// before the first reduction.  The row max is a wave-level butterfly followed
+// by one LDS round across the waves of the block.  Per element the VALU work
+// is about six operations (widen, scale, max, rescale, round, pack/4).
 #include "common.h"
 
 namespace w8a8 {
 
 namespace {
+
+// 1.5 * 2^23: adding it to a float t with |t| < 2^22 rounds t to an integer
+// (to nearest, ties to even, by the fp32 add itself) and leaves that integer
+// in the low mantissa bits, two's complement in the low byte.
+constexpr float kRoundMagic = 12582912.0f;
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -31,14 +38,21 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-__device__ __forceinline__ unsigned pack4(float a, float b, float c, float d) {
-  const unsigned q0 = (unsigned)(int)a & 0xffu, q1 = (unsigned)(int)b & 0xffu;
-  const unsigned q2 = (unsigned)(int)c & 0xffu, q3 = (unsigned)(int)d & 0xffu;
-  return q0 | (q1 << 8) | (q2 << 16) | (q3 << 24);
+// Low bytes of four magic-rounded floats, packed little-endian.
+__device__ __forceinline__ unsigned pack_codes(float a, float b, float c, float d) {
+  const unsigned ua = __float_as_uint(a), ub = __float_as_uint(b);
+  const unsigned uc = __float_as_uint(c), ud = __float_as_uint(d);
+  const unsigned p01 = __builtin_amdgcn_perm(ub, ua, 0x0c0c0400u);  // ua.b0, ub.b0
+  const unsigned p23 = __builtin_amdgcn_perm(ud, uc, 0x0c0c0400u);  // uc.b0, ud.b0
+  return __builtin_amdgcn_perm(p23, p01, 0x05040100u);
 }
 
-__device__ __forceinline__ float code(float v, float r) {
-  return fminf(fmaxf(rintf(v * r), -127.0f), 127.0f);
+// Element e (0..7) of a 16-byte chunk of fp16/bf16 values, widened to fp32.
+template <bool BF16>
+__device__ __forceinline__ float elem(const v4u& c, int e) {
+  const unsigned w = c[e / 2];
+  if (BF16) return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+  return widen16((unsigned short)((e & 1) ? (w >> 16) : (w & 0xffffu)), false);
 }
 
 template <int CPT, int R, bool BF16>
@@ -52,7 +66,19 @@ __global__ __launch_bounds__(1024) void k_scale_quant_rows(const v4u* __restrict
   const int lane = tid % kWave, wave = tid / kWave, nwaves = G / kWave;
   const int64_t row0 = (int64_t)blockIdx.x * R;
 
+  // all of this block's input loads first
   v4u xv[R][CPT];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = i * G + tid;
+      if (c < cols8 && row0 + r < rows)
+        xv[r][i] = __builtin_nontemporal_load(x + (row0 + r) * cols8 + c);
+      else
+        xv[r][i] = v4u{0u, 0u, 0u, 0u};
+    }
+  }
   float sc[CPT][8];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
@@ -66,19 +92,9 @@ __global__ __launch_bounds__(1024) void k_scale_quant_rows(const v4u* __restrict
       for (int e = 0; e < 8; ++e) sc[i][e] = 0.0f;
     }
   }
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = i * G + tid;
-      if (c < cols8 && row0 + r < rows)
-        xv[r][i] = __builtin_nontemporal_load(x + (row0 + r) * cols8 + c);
-      else
-        xv[r][i] = v4u{0u, 0u, 0u, 0u};
-    }
-  }
 
-  // pass 1: row max of |x * c|
+  // pass 1: v = x * c (kept in registers) and the row max of |v|
+  float v[R][CPT][8];
   float m[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -87,8 +103,8 @@ __global__ __launch_bounds__(1024) void k_scale_quant_rows(const v4u* __restrict
     for (int i = 0; i < CPT; ++i) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const unsigned short h = (unsigned short)(xv[r][i][e / 2] >> (16 * (e % 2)));
-        mr = fmaxf(mr, fabsf(widen16(h, BF16) * sc[i][e]));
+        v[r][i][e] = elem<BF16>(xv[r][i], e) * sc[i][e];
+        mr = fmaxf(mr, fabsf(v[r][i][e]));
       }
     }
     m[r] = wave_max(mr);
@@ -106,7 +122,9 @@ __global__ __launch_bounds__(1024) void k_scale_quant_rows(const v4u* __restrict
     m[r] = mr;
   }
 
-  // pass 2: codes
+  // pass 2: codes = round_half_even(v * (127 / m)); m == 0 gives r = 0 and
+  // all-zero codes.  |v * r| <= 127 (1 + 2^-23) for every element of a row,
+  // so the rounded code never leaves [-127, 127] and no clamp is needed.
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int64_t row = row0 + r;
@@ -118,15 +136,15 @@ __global__ __launch_bounds__(1024) void k_scale_quant_rows(const v4u* __restrict
     for (int i = 0; i < CPT; ++i) {
       const int c = i * G + tid;
       if (c >= cols8) continue;
-      float v[8];
+      float t[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const unsigned short h = (unsigned short)(xv[r][i][e / 2] >> (16 * (e % 2)));
-        v[e] = code(widen16(h, BF16) * sc[i][e], rcp);
+        t[e] = v[r][i][e] * rcp;
+        t[e] = t[e] + kRoundMagic;
       }
       uint2 o;
-      o.x = pack4(v[0], v[1], v[2], v[3]);
-      o.y = pack4(v[4], v[5], v[6], v[7]);
+      o.x = pack_codes(t[0], t[1], t[2], t[3]);
+      o.y = pack_codes(t[4], t[5], t[6], t[7]);
       q[row * cols8 + c] = o;
     }
   }
@@ -145,17 +163,6 @@ hipError_t launch_cfg(const void* x, bool bf16, int64_t rows, int cols8, int G,
   return hipGetLastError();
 }
 
-template <int CPT>
-hipError_t launch_rows(const void* x, bool bf16, int64_t rows, int cols8, int G,
-                       const float* col_scale, int8_t* q, float* row_scale, hipStream_t st) {
-  // rows per block: amortize the column-scale loads while keeping >= ~1024 blocks
-  if (rows >= 4 * 1024)
-    return launch_cfg<CPT, 4>(x, bf16, rows, cols8, G, col_scale, q, row_scale, st);
-  if (rows >= 2 * 1024)
-    return launch_cfg<CPT, 2>(x, bf16, rows, cols8, G, col_scale, q, row_scale, st);
-  return launch_cfg<CPT, 1>(x, bf16, rows, cols8, G, col_scale, q, row_scale, st);
-}
-
 }  // namespace
 
 hipError_t launch_scale_quant_rows(const void* x, bool bf16, int64_t rows, int64_t cols,
@@ -163,21 +170,25 @@ hipError_t launch_scale_quant_rows(const void* x, bool bf16, int64_t rows, int64
                                    hipStream_t st) {
   if (rows == 0) return hipSuccess;
   const int cols8 = (int)(cols / 8);
-  // threads per row: about 4 chunks each, a whole number of waves, at most 1024
-  int G = (cols8 + 3) / 4;
+  // Threads per row: two 16-byte chunks each (more for rows past 2048 chunks,
+  // where the block size reaches 1024), a whole number of waves.  Rows per
+  // block: two while a thread holds two chunks, one beyond, which keeps the
+  // fp32 row slice a thread carries between the passes at 32 values or fewer
+  // (more would cost occupancy).
+  int G = (cols8 + 1) / 2;
   G = ((G + kWave - 1) / kWave) * kWave;
   if (G < kWave) G = kWave;
   if (G > 1024) G = 1024;
   const int cpt = (cols8 + G - 1) / G;
   switch (cpt <= 1 ? 1 : cpt) {
-    case 1: return launch_rows<1>(x, bf16, rows, cols8, G, col_scale, q, row_scale, st);
-    case 2: return launch_rows<2>(x, bf16, rows, cols8, G, col_scale, q, row_scale, st);
-    case 3: return launch_rows<3>(x, bf16, rows, cols8, G, col_scale, q, row_scale, st);
-    case 4: return launch_rows<4>(x, bf16, rows, cols8, G, col_scale, q, row_scale, st);
-    case 5: return launch_rows<5>(x, bf16, rows, cols8, G, col_scale, q, row_scale, st);
-    case 6: return launch_rows<6>(x, bf16, rows, cols8, G, col_scale, q, row_scale, st);
-    case 7: return launch_rows<7>(x, bf16, rows, cols8, G, col_scale, q, row_scale, st);
-    case 8: return launch_rows<8>(x, bf16, rows, cols8, G, col_scale, q, row_scale, st);
+    case 1: return launch_cfg<1, 4>(x, bf16, rows, cols8, G, col_scale, q, row_scale, st);
+    case 2: return launch_cfg<2, 2>(x, bf16, rows, cols8, G, col_scale, q, row_scale, st);
+    case 3: return launch_cfg<3, 1>(x, bf16, rows, cols8, G, col_scale, q, row_scale, st);
+    case 4: return launch_cfg<4, 1>(x, bf16, rows, cols8, G, col_scale, q, row_scale, st);
+    case 5: return launch_cfg<5, 1>(x, bf16, rows, cols8, G, col_scale, q, row_scale, st);
+    case 6: return launch_cfg<6, 1>(x, bf16, rows, cols8, G, col_scale, q, row_scale, st);
+    case 7: return launch_cfg<7, 1>(x, bf16, rows, cols8, G, col_scale, q, row_scale, st);
+    case 8: return launch_cfg<8, 1>(x, bf16, rows, cols8, G, col_scale, q, row_scale, st);
     default: return hipErrorInvalidValue;
   }
 }
