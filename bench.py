@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20,
                     help="repetitions per kernel in the per-kernel breakdown pass")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain device copy of this size first (outside the timed "
+                         "region): the reference for scaling hardware byte counters")
     return ap.parse_args()
 
 
@@ -214,6 +217,11 @@ def main():
     dev = "cuda:0"
     wl = synth.WORKLOADS[args.workload]
     n_batches = max(1, min(args.steps + args.warmup, wl.cal_tokens // wl.cal_batch))
+    if args.copy_probe_mib:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+        del src
     layers = [Layer(wl, li, n_batches, args.alpha, dev) for li in range(len(wl.layers))]
     torch.cuda.synchronize()
     print(f"[bench] {wl.name}: {len(layers)} layers, M={wl.M[0]}, buffers ready", file=sys.stderr,
