@@ -160,11 +160,14 @@ def rand_codes(rows, cols, seed):
     return torch.randint(-127, 128, (rows, cols), generator=g, dtype=torch.int8).to(DEV)
 
 
-# shapes cover the three tile configurations (128x128, 256x128, 256x256),
-# ragged M, N and K tails, K = 0 and empty outputs
+# shapes cover the three tile configurations (128x128, 256x128, 256x256), the
+# skinny few-token kernel (M <= 16 and M <= 32), ragged M, N and K tails, K = 0
+# and empty outputs
 GEMM_SHAPES = [(1, 8, 16), (37, 136, 80), (300, 520, 1040), (64, 512, 512),
                (2048, 4096, 256), (4000, 8184, 272), (4096, 8192, 144), (513, 264, 4112),
-               (5, 16, 0), (0, 8, 32), (8, 0, 32)]
+               (5, 16, 0), (0, 8, 32), (8, 0, 32),
+               (1, 4096, 16384), (3, 8, 64), (16, 520, 1040), (17, 136, 80), (32, 264, 4112),
+               (33, 136, 80), (32, 16384, 272)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
@@ -184,7 +187,7 @@ def test_gemm_i32_extremes():
 
 @pytest.mark.parametrize("out", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("M,N,K", [(37, 136, 80), (300, 520, 1040), (2048, 4096, 256),
-                                   (4000, 8184, 272), (5, 16, 0)])
+                                   (4000, 8184, 272), (5, 16, 0), (1, 4104, 4112), (32, 264, 1040)])
 def test_gemm_dequant(out, M, N, K):
     qa, qb = rand_codes(M, K, M + K), rand_codes(N, K, N + 2 * K + 1)
     g = torch.Generator(device="cpu").manual_seed(M * N)

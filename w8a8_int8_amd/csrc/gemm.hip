@@ -313,6 +313,117 @@ k_gemm_i8(const int8_t* __restrict__ qa, const int8_t* __restrict__ qb, int M, i
   }
 }
 
+// Skinny GEMM for few tokens (decode-like M <= 32): the product is weight
+// streaming, so the tiling follows the weight.  A block owns 16 output
+// channels over all of K and all M tokens; its NW waves split K (wave w takes
+// the 64-deep k steps w, w + NW, ...), so the waves of a block read adjacent
+// 64-byte pieces of the same 16 weight rows.  Each step is one
+// v_mfma_i32_16x16x64_i8 per 16 tokens with the weight fragment as the first
+// operand (16 channels x 64 k) and the activation fragment as the second
+// (64 k x 16 tokens).  Operands load straight into registers with buffer
+// loads, U steps in flight per wave; token rows past M and channel rows past N
+// are outside their buffer resources and read as zero without touching
+// memory.  The waves' partial int32 sums are added exactly through LDS, and
+// one wave applies the same dequant epilogue as the tiled kernel (each lane
+// holds 4 consecutive channels of one token).
+template <int MT, int NW, int OUT>
+__global__ __launch_bounds__(64 * NW) void k_gemm_skinny(
+    const int8_t* __restrict__ qa, const int8_t* __restrict__ qb, int M, int N, int K,
+    const float* __restrict__ sa, const float* __restrict__ sb, void* __restrict__ out) {
+  constexpr int U = 8;  // k steps in flight per wave
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n0 = blockIdx.x * 16;
+  const rsrc_t rw = make_rsrc(qb + (int64_t)n0 * K, (unsigned)min(16, N - n0) * (unsigned)K);
+  const rsrc_t rx = make_rsrc(qa, (unsigned)M * (unsigned)K);
+  const int r16 = lane & 15, kq = lane >> 4;  // fragment row, 16-byte k chunk
+  const int voff_w = r16 * K + kq * 16;
+  int voff_x[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) voff_x[t] = (t * 16 + r16) * K + kq * 16;
+
+  v4i acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = v4i{0, 0, 0, 0};
+  const int nsteps = (K + 63) / 64;
+  for (int s0 = wave; s0 < nsteps; s0 += NW * U) {
+    v4i w[U], x[U][MT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int st = s0 + u * NW;
+      const int k0 = st * 64;
+      const bool out_k = st >= nsteps || k0 + kq * 16 >= K;
+      w[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, out_k ? kOob : voff_w, k0, 0);
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        x[u][t] = __builtin_amdgcn_raw_buffer_load_b128(rx, out_k ? kOob : voff_x[t], k0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[u], x[u][t], acc[t], 0, 0, 0);
+  }
+
+  // exact sum of the waves' partial accumulators
+  __shared__ v4i red[NW][MT][64];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) red[wave][t][lane] = acc[t];
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    v4i c = red[0][t][lane];
+#pragma unroll
+    for (int w2 = 1; w2 < NW; ++w2) c += red[w2][t][lane];
+    // lane holds channels n .. n+3 of token m
+    const int m = t * 16 + (lane & 15);
+    const int n = n0 + 4 * (lane >> 4);
+    if (m >= M || n >= N) continue;
+    if (OUT == 0) {
+      *(v4i*)((int32_t*)out + (int64_t)m * N + n) = c;
+    } else {
+      const float am = sa[m];
+      const float4 bn = *(const float4*)(sb + n);
+      const float wv[4] = {bn.x, bn.y, bn.z, bn.w};
+      unsigned short h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float y = (float)c[e];
+        y = y * am;
+        y = y * wv[e];
+        h[e] = OUT == 1 ? f32_to_f16_rne(y) : f32_to_bf16_rne(y);
+      }
+      uint2 o;
+      o.x = (unsigned)h[0] | ((unsigned)h[1] << 16);
+      o.y = (unsigned)h[2] | ((unsigned)h[3] << 16);
+      *(uint2*)((unsigned short*)out + (int64_t)m * N + n) = o;
+    }
+  }
+}
+
+template <int MT>
+hipError_t launch_skinny(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N, int64_t K,
+                         const float* sa, const float* sb, void* out, int mode, hipStream_t st) {
+  constexpr int NW = 8;
+  const dim3 grid((unsigned)((N + 15) / 16)), block(64 * NW);
+  switch (mode) {
+    case 0:
+      hipLaunchKernelGGL((k_gemm_skinny<MT, NW, 0>), grid, block, 0, st, qa, qb, (int)M, (int)N,
+                         (int)K, sa, sb, out);
+      break;
+    case 1:
+      hipLaunchKernelGGL((k_gemm_skinny<MT, NW, 1>), grid, block, 0, st, qa, qb, (int)M, (int)N,
+                         (int)K, sa, sb, out);
+      break;
+    default:
+      hipLaunchKernelGGL((k_gemm_skinny<MT, NW, 2>), grid, block, 0, st, qa, qb, (int)M, (int)N,
+                         (int)K, sa, sb, out);
+      break;
+  }
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int BK, int NST, int WGM, int WGN>
 hipError_t launch_tile(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N, int64_t K,
                        const float* sa, const float* sb, void* out, int mode, hipStream_t st) {
@@ -341,6 +452,11 @@ hipError_t launch_gemm(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N,
                        const float* sa, const float* sb, void* out, int out_mode,
                        hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
+  // Few tokens: weight streaming, handled by the skinny kernel.  Between 17
+  // and 32 tokens it reads two activation fragments per step, and the tiled
+  // kernel is as fast once N alone gives it 128 or more blocks.
+  if (M <= 16) return launch_skinny<1>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
+  if (M <= 32 && N < 16384) return launch_skinny<2>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
   // Pick the tile whose last wave of blocks over 256 CUs is fullest, with a
   // small preference for the larger tile (more MACs per byte of LDS traffic).
   struct Cand { int bm, bn; double eff; };
