@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kAmaxThreads) void k_channel_amax(const v4u* __rest
   if (active) {
     const v4u* p = x + chunk;
     int64_t r = r_begin + wave * kRowsPerLoad + sub;
-    // full batches: U loads per lane, no per-load bounds test
+    // full batches: U loads per lane in flight, no per-load bounds test
     for (; r + (int64_t)(kAmaxUnroll - 1) * kRowsPerGroup < r_end; r += kRowsPerBatch) {
       v4u v[kAmaxUnroll];
 #pragma unroll
@@ -72,7 +72,18 @@ __global__ __launch_bounds__(kAmaxThreads) void k_channel_amax(const v4u* __rest
 #pragma unroll
       for (int u = 0; u < kAmaxUnroll; ++u) m = vmax(m, v[u]);
     }
-    for (; r < r_end; r += kRowsPerGroup) m = vmax(m, __builtin_nontemporal_load(p + r * cols8));
+    // the last partial batch: all of its loads issued together as well (a
+    // row-by-row tail would pay one memory round trip per row group)
+    if (r < r_end) {
+      v4u v[kAmaxUnroll];
+#pragma unroll
+      for (int u = 0; u < kAmaxUnroll; ++u) {
+        const int64_t ru = r + (int64_t)u * kRowsPerGroup;
+        v[u] = ru < r_end ? __builtin_nontemporal_load(p + ru * cols8) : v4u{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < kAmaxUnroll; ++u) m = vmax(m, v[u]);
+    }
   }
   // fold the 8 row lanes that hold the same chunk (lanes l, l^8, l^16, l^32)
 #pragma unroll
