@@ -1,0 +1,120 @@
+"""Seeded random shapes through every entry point, against the CPU oracle.
+
+Shapes are drawn small (the oracle finishes each in well under a second) but
+cover empty inputs, ragged tails of every tile size, the few-token GEMM path,
+zero rows, dead channels and both 16-bit input types.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import w8a8_int8_amd as w8
+from w8a8_int8_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+CASES = 24
+
+
+def bits(t):
+    return synth.to_numpy_bits(t)
+
+
+def dt(t):
+    return "f16" if t.dtype == torch.float16 else "bf16"
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def rand_x(rng, rows, cols, dtype):
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    if cols:
+        idx = rng.choice(cols, size=min(cols, 1 + cols // 64), replace=False)
+        x[:, idx] *= rng.uniform(20, 120, idx.size).astype(np.float32)
+    if rows > 3:
+        x[rng.integers(0, rows)] = 0.0
+    return torch.from_numpy(x).to(dtype).to(DEV)
+
+
+@pytest.mark.parametrize("case", range(CASES))
+def test_fuzz_quant_and_amax(case):
+    rng = np.random.default_rng(1000 + case)
+    dtype = torch.float16 if case % 2 == 0 else torch.bfloat16
+    rows = int(rng.choice([0, 1, 2, 3, int(rng.integers(4, 700))]))
+    cols = 16 * int(rng.integers(0 if case % 5 else 1, 300))
+    x = rand_x(rng, rows, cols, dtype)
+    c = torch.from_numpy(np.exp(rng.uniform(-6, 6, cols)).astype(np.float32)).to(DEV)
+    q, d = w8.scale_quant_rows(x, c)
+    q_or, d_or = oracle.scale_quant_rows(bits(x), dt(x), host(c))
+    assert np.array_equal(host(q), q_or)
+    assert np.array_equal(host(d).view(np.uint32), d_or.view(np.uint32))
+    if cols:
+        start = np.abs(rng.standard_normal(cols)).astype(np.float32) * (case % 3 == 0)
+        amax = w8.channel_amax(x, torch.from_numpy(start.copy()).to(DEV))
+        want = oracle.channel_amax(bits(x), dt(x), amax=start) if rows else start
+        assert np.array_equal(host(amax).view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("case", range(CASES))
+def test_fuzz_gemm(case):
+    rng = np.random.default_rng(2000 + case)
+    M = int(rng.choice([0, 1, int(rng.integers(2, 17)), int(rng.integers(17, 33)),
+                        int(rng.integers(33, 600))]))
+    N = 8 * int(rng.integers(0 if case % 7 else 1, 90))
+    K = 16 * int(rng.integers(0, 90))
+    qa = torch.from_numpy(rng.integers(-127, 128, (M, K), dtype=np.int8)).to(DEV)
+    qb = torch.from_numpy(rng.integers(-127, 128, (N, K), dtype=np.int8)).to(DEV)
+    c_or = oracle.gemm_i32(host(qa), host(qb))
+    assert np.array_equal(host(w8.gemm_i32(qa, qb)), c_or)
+    sa = torch.from_numpy(rng.uniform(1e-4, 0.05, M).astype(np.float32)).to(DEV)
+    sb = torch.from_numpy(rng.uniform(1e-5, 2e-3, N).astype(np.float32)).to(DEV)
+    out = torch.float16 if case % 2 == 0 else torch.bfloat16
+    y = w8.gemm_dequant(qa, sa, qb, sb, out)
+    y_or = oracle.dequant(c_or, host(sa), host(sb), "f16" if case % 2 == 0 else "bf16")
+    assert np.array_equal(bits(y).view(np.uint16), y_or.view(np.uint16))
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_fuzz_linear_pipeline(case):
+    rng = np.random.default_rng(3000 + case)
+    dtype = torch.float16 if case % 2 == 0 else torch.bfloat16
+    K = 16 * int(rng.integers(1, 200))
+    N = 8 * int(rng.integers(1, 120))
+    M = int(rng.choice([1, int(rng.integers(2, 33)), int(rng.integers(33, 500))]))
+    alpha = float(rng.choice([0.0, 0.5, 0.8, 1.0, rng.uniform()]))
+    xc = rand_x(rng, int(rng.integers(1, 400)), K, dtype)
+    w = torch.from_numpy((rng.standard_normal((N, K)) * 0.02).astype(np.float32)).to(dtype).to(DEV)
+    x = rand_x(rng, M, K, dtype)
+    if K > 16:
+        w[:, 3] = 0  # a dead weight channel: s = 1 there
+    amax_x = w8.channel_amax(xc)
+    p = w8.prepare_weight(w, amax_x, alpha)
+    y = w8.linear(x, p["inv_s"], p["qw"], p["sw"])
+    ax = oracle.channel_amax(bits(xc), dt(x))
+    po = oracle.prepare_weight(bits(w), dt(x), ax, alpha)
+    lo = oracle.linear(bits(x), dt(x), po["inv_s"], po["qw"], po["sw"])
+    assert np.array_equal(host(p["s"]).view(np.uint32), po["s"].view(np.uint32))
+    assert np.array_equal(host(p["qw"]), po["qw"])
+    assert np.array_equal(bits(y).view(np.uint16), lo["y"].view(np.uint16))
+
+
+def test_repeat_runs_are_bitwise_identical():
+    """Atomic max order and block scheduling do not change any result."""
+    wl = synth.WORKLOADS["llama2_7b_prefill"]
+    xc = synth.calibration(wl, 1, 2048, chunk=3, device=DEV)
+    w = synth.weights(wl, 1, device=DEV)
+    x = synth.activations(wl, 1, 2048, device=DEV)
+    outs = []
+    for _ in range(3):
+        amax = w8.channel_amax(xc)
+        p = w8.prepare_weight(w, amax, 0.5)
+        outs.append((host(amax), host(p["qw"]), bits(w8.linear(x, p["inv_s"], p["qw"], p["sw"]))))
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
