@@ -11,7 +11,9 @@ of the Llama-2-7B-shaped decoder block (prefill, M = 2048 tokens):
 All inputs are resident in HBM before the timed region.
 
 value = the step's INT8 GEMM work (2 M N K summed over the layers) divided by
-the whole step's wall time, in TOPS.  The roofline object reports the GEMM
+the whole step's wall time, in TOPS.  The per-kernel breakdown also times the
+dense fp16 product of each layer (same tiling on the 16-bit matrix cores) to
+state the W8A8-vs-FP16 speedup at kernel level.  The roofline object reports the GEMM
 kernel (the dominant kernel) against the dense INT8 MFMA peak, with its
 average launch duration taken from HIP events recorded around every GEMM
 launch inside the timed region.  cpu_baseline times the CPU oracle on the
@@ -34,6 +36,7 @@ if ROOT not in sys.path:
 
 PEAK_INT8_TOPS = 5000.0  # MI355X dense INT8 MFMA, 10^12 int ops / s
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+PEAK_DENSE16_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 MFMA
 METRIC = "W8A8 GEMM TOPS + smooth/quant GB/s (% of MI355X peak), Llama-2-7B shapes"
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -162,7 +165,16 @@ def kernel_breakdown(layers, reps):
         t = timed(lambda i: w8.gemm_dequant(L.qx, L.sx, L.qw, L.sw, L.x.dtype, L.y), reps)
         ops = L.gemm_ops()
         d["gemm_dequant"] = dict(us=t * 1e6, TOPS=ops / t / 1e12, frac_mfma=ops / t / 1e12 / PEAK_INT8_TOPS)
+        t16 = timed(lambda i: w8.gemm_float(L.x, L.w, L.y), reps)
+        d["dense16_gemm"] = dict(us=t16 * 1e6, TFLOPS=ops / t16 / 1e12,
+                                 frac_mfma=ops / t16 / 1e12 / PEAK_DENSE16_TFLOPS)
         out[f"{L.name}_{L.K}x{L.N}"] = {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in d.items()}
+    # W8A8 vs the dense 16-bit product on the same shapes, summed over the layers
+    t_w8 = sum(v["gemm_dequant"]["us"] for v in out.values())
+    t_q = sum(v["smooth_quant_act"]["us"] for v in out.values())
+    t_16 = sum(v["dense16_gemm"]["us"] for v in out.values())
+    out["w8a8_vs_dense16"] = {"gemm_speedup": round(t_16 / t_w8, 3),
+                              "gemm_plus_act_quant_speedup": round(t_16 / (t_w8 + t_q), 3)}
     return out
 
 

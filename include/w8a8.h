@@ -164,6 +164,24 @@ w8a8_status_t w8a8_gemm_dequant(const int8_t* qa, const float* sa, const int8_t*
                                 const float* sb, void* y, int out_dtype, int64_t M, int64_t N,
                                 int64_t K, hipStream_t stream);
 
+/*
+ * Dense 16-bit baseline: y = a b^T with fp16 or bf16 operands (dtype), fp32
+ * accumulation and a round-to-nearest-even conversion of every accumulator
+ * to dtype.  This is the FP16 product that the page measures W8A8 against
+ * (section "パフォーマンスベンチマーク(A100-80GB)", speed table); it runs on the
+ * 16-bit matrix cores with the same tiling as the INT8 kernel, so the two can
+ * be timed against each other on the same shapes.
+ *
+ *   a  [M x K], b [N x K] (weight layout), y [M x N], all of dtype, 16-byte aligned.
+ *   M >= 0, N >= 0, 0 <= K <= 1048576, K % 8 == 0, N % 8 == 0.  K == 0 writes zeros.
+ *   The order of the fp32 accumulation is unspecified: before the final
+ *   rounding each output is within K * 2^-24 * sum_j |a[t, j] b[k, j]| of the
+ *   exact sum.
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, HIP.
+ */
+w8a8_status_t w8a8_gemm_float(const void* a, const void* b, void* y, int dtype, int64_t M,
+                              int64_t N, int64_t K, hipStream_t stream);
+
 /* Bytes of workspace w8a8_linear needs for M tokens of K channels
  * (the INT8 activations and their per-token scales, each 256-byte aligned). */
 size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K);

@@ -4,7 +4,7 @@ Only tests/, the smoke check in __graft_entry__.py and bench.py's CPU
 baseline leg import this package.
 """
 from .smoothquant import *  # noqa: F401,F403
-from .smoothquant import (QMAX, apply_col_scale, channel_amax, dequant, gemm_i32,
+from .smoothquant import (QMAX, apply_col_scale, channel_amax, dequant, gemm_float, gemm_i32,
                           linear, narrow, prepare_weight, quantize_rows,
                           round_to_bf16, scale_quant_rows, smooth_factor,
                           smooth_factors, smooth_fp64, widen)

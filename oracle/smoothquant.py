@@ -229,6 +229,24 @@ def dequant(c: np.ndarray, sa, sb, out_dtype: str) -> np.ndarray:
     return narrow(y, out_dtype)
 
 
+# ------------------------------------------------- dense 16-bit baseline
+
+
+def gemm_float(a, b, dtype: str):
+    """The FP16 (or bf16) product the page compares W8A8 against (section
+    "パフォーマンスベンチマーク(A100-80GB)"): y = a @ b.T for 16-bit operands.
+
+    Returns (y64, bound): the product in fp64 (each 16-bit product is exact in
+    fp64, the sum carries at most K * 2^-53 relative rounding) and
+    sum_j |a[t, j] b[k, j]|, the scale of the accumulation error a
+    reduced-precision sum may add.
+    Pinned by test_gemm_float_* (integer-valued operands: exact).
+    """
+    a64 = widen(a, dtype).astype(np.float64)
+    b64 = widen(b, dtype).astype(np.float64)
+    return a64 @ b64.T, np.abs(a64) @ np.abs(b64).T
+
+
 # ------------------------------------------------------ composed flows
 
 

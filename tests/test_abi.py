@@ -36,7 +36,7 @@ def declared_symbols():
 def test_library_loads_and_exports_header_symbols():
     lib = _lib.load()
     syms = declared_symbols()
-    assert len(syms) == 9
+    assert len(syms) == 10
     for s in syms:
         assert hasattr(lib, s), s
         assert s in _lib.PROTOTYPES, s
@@ -139,3 +139,15 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError, match="no fallback"):
         _lib.load()
+
+
+@cpu_only
+def test_gemm_float_rejects():
+    g = _lib.load().w8a8_gemm_float
+    assert g(0, P, P, 0, 4, 8, 16, 0) == ENULL
+    assert g(P, P, P, 2, 4, 8, 16, 0) == EDTYPE
+    assert g(P, P, P, 0, 4, 8, 12, 0) == ESHAPE  # K % 8
+    assert g(P, P, P, 0, 4, 12, 16, 0) == ESHAPE  # N % 8
+    assert g(P, P, P, 0, 4, 8, (1 << 20) + 8, 0) == ESHAPE
+    assert g(PODD, P, P, 0, 4, 8, 16, 0) == EALIGN
+    assert g(0, P, 0, 0, 0, 8, 16, 0) == OK  # empty output: no launch

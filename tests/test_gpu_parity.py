@@ -324,3 +324,29 @@ def test_workload_layer(name, li, alpha):
     ms = sorted(wl.M)
     for a, b in zip(ms, ms[1:]):
         assert np.array_equal(ys[a].view(np.uint16), ys[b][:a].view(np.uint16))
+
+
+# ------------------------------------------- dense 16-bit baseline (fp16/bf16)
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("M,N,K", [(37, 136, 80), (300, 520, 1040), (2048, 4096, 256),
+                                   (4000, 8184, 272), (5, 16, 0), (1, 264, 4104),
+                                   (2048, 12288, 4096)])
+def test_gemm_float(dtype, M, N, K):
+    """fp32-accumulated dense product: within K 2^-24 sum|a b| of the exact
+    value before the final rounding, plus one unit of the output format."""
+    g = torch.Generator(device="cpu").manual_seed(M + N + K)
+    a = torch.randn((M, K), generator=g).to(dtype).to(DEV)
+    b = (torch.randn((N, K), generator=g) * 0.05).to(dtype).to(DEV)
+    y = w8.gemm_float(a, b)
+    name = dt_name(a)
+    y64, bound = oracle.gemm_float(np_bits(a), np_bits(b), name)
+    got = y_values(np_bits(y), name)
+    if name == "f16":
+        ulp = np.spacing(np.abs(y64).astype(np.float16)).astype(np.float64)
+    else:
+        e = np.floor(np.log2(np.maximum(np.abs(y64), 2.0 ** -126)))
+        ulp = 2.0 ** (e - 7)
+    tol = K * 2.0 ** -24 * bound + ulp
+    assert (np.abs(got - y64) <= tol).all()

@@ -349,3 +349,31 @@ def test_linear_end_to_end_error_bound_and_method_sanity():
         assert (np.abs(y - y64) <= bound).all()
         errs[alpha] = np.abs(y - y64).mean()
     assert errs[0.5] < errs[None] / 2
+
+
+# ------------------------------------------------------- dense 16-bit baseline
+
+
+def test_gemm_float_integer_operands_exact():
+    """Integer-valued fp16/bf16 operands: every product and sum is an integer,
+    so the fp64 result must equal the Python-integer sum."""
+    for dtype in ("f16", "bf16"):
+        a_i = rng.integers(-100, 101, (5, 48))
+        b_i = rng.integers(-100, 101, (7, 48))
+        if dtype == "f16":
+            a, b = a_i.astype(np.float16), b_i.astype(np.float16)
+        else:
+            a, b = _bf16_bits(a_i.astype(np.float32)), _bf16_bits(b_i.astype(np.float32))
+        y, bound = oracle.gemm_float(a, b, dtype)
+        for i in range(5):
+            for j in range(7):
+                assert y[i, j] == sum(int(a_i[i, t]) * int(b_i[j, t]) for t in range(48))
+                assert bound[i, j] == sum(abs(int(a_i[i, t]) * int(b_i[j, t])) for t in range(48))
+
+
+def test_gemm_float_matches_int_gemm_on_codes():
+    """On INT8 codes (exact in fp16) the dense baseline and the INT8 product agree."""
+    qa = rng.integers(-127, 128, (6, 64), dtype=np.int8)
+    qb = rng.integers(-127, 128, (9, 64), dtype=np.int8)
+    y, _ = oracle.gemm_float(qa.astype(np.float16), qb.astype(np.float16), "f16")
+    assert np.array_equal(y.astype(np.int64), oracle.gemm_i32(qa, qb).astype(np.int64))

@@ -138,6 +138,21 @@ def gemm_dequant(qa: torch.Tensor, sa: torch.Tensor, qb: torch.Tensor, sb: torch
     return y
 
 
+def gemm_float(a: torch.Tensor, b: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Dense 16-bit baseline y = a @ b.T (fp16 or bf16 operands, fp32 accumulation)."""
+    _dev(a, b)
+    M, K = a.shape
+    N = b.shape[0]
+    _need(b, a.dtype, (N, K))
+    y = torch.empty((M, N), dtype=a.dtype, device=a.device) if y is None else y
+    _dev(y)
+    _need(y, a.dtype, (M, N))
+    lib = _lib.load()
+    _lib.check("w8a8_gemm_float", lib.w8a8_gemm_float(
+        _ptr(a), _ptr(b), _ptr(y), _dtype_code(a), M, N, K, _stream()))
+    return y
+
+
 def linear_workspace_bytes(M: int, K: int) -> int:
     return int(_lib.load().w8a8_linear_workspace_bytes(M, K))
 

@@ -114,6 +114,18 @@ w8a8_status_t w8a8_gemm_dequant(const int8_t* qa, const float* sa, const int8_t*
                                       stream));
 }
 
+w8a8_status_t w8a8_gemm_float(const void* a, const void* b, void* y, int dtype, int64_t M,
+                              int64_t N, int64_t K, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return W8A8_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 0 || M >= kMaxRows || N >= kMaxRows || K > ((int64_t)1 << 20) ||
+      K % 8 != 0 || N % 8 != 0)
+    return W8A8_ERR_SHAPE;
+  if ((!a && M * K) || (!b && N * K) || (!y && M * N)) return W8A8_ERR_NULL;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(y, 16)) return W8A8_ERR_ALIGN;
+  return hip_status(w8a8::launch_gemm((const int8_t*)a, (const int8_t*)b, M, N, K, nullptr,
+                                      nullptr, y, dtype == W8A8_BF16 ? 4 : 3, stream));
+}
+
 size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K) {
   if (M < 0 || K < 0) return 0;
   return round_up((size_t)M * (size_t)K, kWsAlign) + round_up((size_t)M * 4, kWsAlign);

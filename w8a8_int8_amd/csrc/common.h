@@ -21,7 +21,9 @@ hipError_t launch_smooth_factors(const float* ax, const float* aw, int64_t K, do
 hipError_t launch_scale_quant_rows(const void* x, bool bf16, int64_t rows, int64_t cols,
                                    const float* col_scale, int8_t* q, float* row_scale,
                                    hipStream_t st);
-// out_mode: 0 = int32 accumulators, 1 = fp16 dequant, 2 = bf16 dequant
+// out_mode: 0 = int32 accumulators, 1 = fp16 dequant, 2 = bf16 dequant (int8
+// operands, K in bytes); 3 = fp16, 4 = bf16 dense product (16-bit operands,
+// K in elements, fp32 accumulation)
 hipError_t launch_gemm(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N, int64_t K,
                        const float* sa, const float* sb, void* out, int out_mode,
                        hipStream_t st);

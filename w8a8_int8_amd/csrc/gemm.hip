@@ -58,6 +58,41 @@ constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format 
 constexpr int kOob = 0x40000000;  // voffset that is out of range for every resource here
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// OUT selects operands, accumulation and epilogue of the tiled kernel:
+//   0: int8 operands, int32 accumulators stored as they are
+//   1: int8 operands, int32 accumulators dequantized to fp16
+//   2: int8 operands, int32 accumulators dequantized to bf16
+//   3: fp16 operands, fp32 accumulators rounded to fp16 (the dense baseline)
+//   4: bf16 operands, fp32 accumulators rounded to bf16 (the dense baseline)
+// Both operand kinds occupy 32 bytes of K per row per 32 x 32 MFMA in the same
+// 16-bytes-per-lane register layout, so the byte-addressed pipeline is shared.
+template <int OUT>
+struct MmaKind {
+  typedef v16i acc_t;
+  __device__ static __forceinline__ acc_t mma(v4i a, v4i b, acc_t c) {
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct MmaKind<3> {
+  typedef v16f acc_t;
+  __device__ static __forceinline__ acc_t mma(v4i a, v4i b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a),
+                                                  __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+  }
+};
+template <>
+struct MmaKind<4> {
+  typedef v16f acc_t;
+  __device__ static __forceinline__ acc_t mma(v4i a, v4i b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a),
+                                                   __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+  }
+};
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const int8_t* base, unsigned bytes) {
@@ -122,8 +157,8 @@ __device__ __forceinline__ void interleave() {
   if constexpr (I + 1 < NMFMA) interleave<I + 1, NMFMA, NDS, NVM>();
 }
 
-// OUT: 0 = int32 C, 1 = fp16 Y, 2 = bf16 Y.  The block has WGM x WGN waves;
-// K advances BK bytes per stage through NST LDS slots.
+// OUT as in MmaKind.  The block has WGM x WGN waves; K (in bytes per row)
+// advances BK bytes per stage through NST LDS slots.
 template <int BM, int BN, int BK, int NST, int WGM, int WGN, int OUT>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WGM * WGN, 64 * WGM * WGN),
                           amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4))) void
@@ -203,11 +238,12 @@ k_gemm_i8(const int8_t* __restrict__ qa, const int8_t* __restrict__ qb, int M, i
   const int off_a = (wm * WM + fr) * BK;
   const int off_b = BM * BK + (wn * WN + fr) * BK;
 
-  v16i acc[FN][FM];
+  typedef typename MmaKind<OUT>::acc_t acc_t;
+  acc_t acc[FN][FM];
 #pragma unroll
   for (int a = 0; a < FN; ++a)
 #pragma unroll
-    for (int b = 0; b < FM; ++b) acc[a][b] = v16i{};
+    for (int b = 0; b < FM; ++b) acc[a][b] = acc_t{};
 
   v4i fb0[FN], fa0[FM], fb1[FN], fa1[FM];
   auto read_frags = [&](int st, int kk, v4i* fb, v4i* fa) {
@@ -223,7 +259,7 @@ k_gemm_i8(const int8_t* __restrict__ qa, const int8_t* __restrict__ qb, int M, i
     for (int a = 0; a < FN; ++a)
 #pragma unroll
       for (int b = 0; b < FM; ++b)
-        acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[a], fa[b], acc[a][b], 0, 0, 0);
+        acc[a][b] = MmaKind<OUT>::mma(fb[a], fa[b], acc[a][b]);
   };
 
   // Pipeline (stage s lives in slot s % NST).  Iteration kt computes stage kt
@@ -281,17 +317,26 @@ k_gemm_i8(const int8_t* __restrict__ qa, const int8_t* __restrict__ qb, int M, i
     const int m = m0 + wm * WM + b * 32 + (lane & 31);
     if (m >= M) continue;
     float am = 0.0f;
-    if (OUT != 0) am = sa[m];
+    if (OUT == 1 || OUT == 2) am = sa[m];
 #pragma unroll
     for (int a = 0; a < FN; ++a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int n = n0 + wn * WN + a * 32 + g * 8 + hi * 4;
         if (n >= N) continue;
-        const v16i& C = acc[a][b];
+        const acc_t& C = acc[a][b];
         if (OUT == 0) {
-          v4i o = {C[4 * g + 0], C[4 * g + 1], C[4 * g + 2], C[4 * g + 3]};
+          v4i o = {(int)C[4 * g + 0], (int)C[4 * g + 1], (int)C[4 * g + 2], (int)C[4 * g + 3]};
           *(v4i*)((int32_t*)out + (int64_t)m * N + n) = o;
+        } else if (OUT >= 3) {
+          unsigned short h[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            h[e] = OUT == 3 ? f32_to_f16_rne((float)C[4 * g + e]) : f32_to_bf16_rne((float)C[4 * g + e]);
+          uint2 o;
+          o.x = (unsigned)h[0] | ((unsigned)h[1] << 16);
+          o.y = (unsigned)h[2] | ((unsigned)h[3] << 16);
+          *(uint2*)((unsigned short*)out + (int64_t)m * N + n) = o;
         } else {
           const float4 bn = *(const float4*)(sb + n);
           const float w[4] = {bn.x, bn.y, bn.z, bn.w};
@@ -438,8 +483,16 @@ hipError_t launch_tile(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N,
       hipLaunchKernelGGL((k_gemm_i8<BM, BN, BK, NST, WGM, WGN, 1>), grid, block, 0, st, qa, qb, (int)M,
                          (int)N, (int)K, sa, sb, out, mt, nt);
       break;
-    default:
+    case 2:
       hipLaunchKernelGGL((k_gemm_i8<BM, BN, BK, NST, WGM, WGN, 2>), grid, block, 0, st, qa, qb, (int)M,
+                         (int)N, (int)K, sa, sb, out, mt, nt);
+      break;
+    case 3:
+      hipLaunchKernelGGL((k_gemm_i8<BM, BN, BK, NST, WGM, WGN, 3>), grid, block, 0, st, qa, qb, (int)M,
+                         (int)N, (int)K, sa, sb, out, mt, nt);
+      break;
+    default:
+      hipLaunchKernelGGL((k_gemm_i8<BM, BN, BK, NST, WGM, WGN, 4>), grid, block, 0, st, qa, qb, (int)M,
                          (int)N, (int)K, sa, sb, out, mt, nt);
       break;
   }
@@ -452,11 +505,15 @@ hipError_t launch_gemm(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N,
                        const float* sa, const float* sb, void* out, int out_mode,
                        hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
+  // fp16 / bf16 operands: K counts elements; the tiled kernel works in bytes
+  const bool dense16 = out_mode >= 3;
+  if (dense16) K *= 2;
   // Few tokens: weight streaming, handled by the skinny kernel.  Between 17
   // and 32 tokens it reads two activation fragments per step, and the tiled
   // kernel is as fast once N alone gives it 128 or more blocks.
-  if (M <= 16) return launch_skinny<1>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
-  if (M <= 32 && N < 16384) return launch_skinny<2>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
+  if (!dense16 && M <= 16) return launch_skinny<1>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
+  if (!dense16 && M <= 32 && N < 16384)
+    return launch_skinny<2>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
   // Pick the tile whose last wave of blocks over 256 CUs is fullest, with a
   // small preference for the larger tile (more MACs per byte of LDS traffic).
   struct Cand { int bm, bn; double eff; };
