@@ -8,3 +8,5 @@ from .smoothquant import (QMAX, apply_col_scale, channel_amax, dequant, gemm_flo
                           linear, narrow, prepare_weight, quantize_rows,
                           round_to_bf16, scale_quant_rows, smooth_factor,
                           smooth_factors, smooth_fp64, widen)
+from .smoothquant import (E4M3_MAX, e4m3_to_float, e4m3_value, gemm_e4m3,
+                          quantize_rows_e4m3, round_to_e4m3, scale_quant_rows_e4m3)

@@ -247,6 +247,101 @@ def gemm_float(a, b, dtype: str):
     return a64 @ b64.T, np.abs(a64) @ np.abs(b64).T
 
 
+# ------------------------------------------------------ FP8 (E4M3) variant
+
+E4M3_MAX = 448.0  # largest finite E4M3 value (1.75 * 2^8)
+
+
+def e4m3_value(code: int) -> float:
+    """Value of one 8-bit E4M3 code (OCP FP8: 1 sign, 4 exponent bits with bias
+    7, 3 mantissa bits; exponent field 0 is subnormal; 0x7f / 0xff are NaN and
+    there is no infinity)."""
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def round_to_e4m3(v32: np.ndarray) -> np.ndarray:
+    """float32 -> E4M3 codes (uint8), round to nearest, ties to even.
+
+    The page notes that the smoothing transform carries over to low-bit float
+    formats (FAQ on FP4 / Blackwell); this is the FP8 grid of that variant.
+    Written from the format: a finite |v| in binade [2^E, 2^(E+1)) has spacing
+    2^(E-3) (subnormal spacing 2^-9 below 2^-6); the code is |v| / spacing
+    rounded half-to-even, re-encoded as exponent and mantissa.  Inputs are
+    finite with |v| < 464 (the midpoint above 448), which the quantizer
+    guarantees.  Pinned by test_e4m3_*.
+    """
+    v = np.asarray(v32, dtype=np.float32).astype(np.float64)
+    a = np.abs(v)
+    assert np.all(a < 464.0)
+    _, e = np.frexp(a)  # a = f * 2^e with f in [0.5, 1)
+    E = np.maximum(e - 1, -6)  # binade exponent, subnormals share -6
+    spacing = np.ldexp(1.0, E - 3)
+    k = np.rint(a / spacing)  # exact division by a power of two; rint is half-to-even
+    q = k * spacing  # the rounded magnitude (may step up into the next binade)
+    codes = np.zeros(v.shape, dtype=np.uint8)
+    for idx in np.ndindex(v.shape):
+        mag = q[idx]
+        if mag == 0.0:
+            c = 0
+        elif mag < 2.0 ** -6:
+            c = int(round(mag / 2.0 ** -9))  # exact: an integer 1..7
+        else:
+            ex = int(np.floor(np.log2(mag)))
+            man = mag / 2.0 ** ex - 1.0
+            c = ((ex + 7) << 3) | int(round(man * 8))
+        if v[idx] < 0 or (v[idx] == 0 and np.signbit(v[idx])):
+            c |= 0x80
+        codes[idx] = c
+    return codes
+
+
+def e4m3_to_float(codes: np.ndarray) -> np.ndarray:
+    table = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+    return table[np.asarray(codes, dtype=np.uint8)]
+
+
+def quantize_rows_e4m3(v32: np.ndarray):
+    """Per-row FP8 (E4M3) quantization, the FP8 counterpart of quantize_rows:
+    delta = RN32(amax / 448), r = RN32(448 / amax), code = E4M3(RN32(v * r)).
+    A zero row gives zero codes and delta = 0.  Returns (codes uint8, delta).
+    Pinned by test_quantize_e4m3_*.
+    """
+    v32 = np.asarray(v32, dtype=np.float32)
+    rows = v32.shape[0]
+    q = np.zeros(v32.shape, dtype=np.uint8)
+    delta = np.zeros(rows, dtype=np.float32)
+    for t in range(rows):
+        m = np.float32(np.abs(v32[t]).max()) if v32.shape[1] else np.float32(0)
+        if m == 0:
+            continue
+        delta[t] = m / np.float32(E4M3_MAX)
+        r = np.float32(E4M3_MAX) / m
+        q[t] = round_to_e4m3((v32[t] * r).astype(np.float32))
+    return q, delta
+
+
+def scale_quant_rows_e4m3(x, dtype: str, col_scale):
+    """Per-column scale then per-row FP8 quantization (FP8 form of steps 2b/3)."""
+    return quantize_rows_e4m3(apply_col_scale(widen(x, dtype), col_scale))
+
+
+def gemm_e4m3(qa: np.ndarray, qb: np.ndarray):
+    """C = decode(qa) @ decode(qb).T in fp64, and sum |a b| (the scale of the
+    accumulation error an fp32 sum may add).  Every E4M3 product is exact in
+    fp64.  Pinned by test_gemm_e4m3_brute_force.
+    """
+    a = e4m3_to_float(qa)
+    b = e4m3_to_float(qb)
+    return a @ b.T, np.abs(a) @ np.abs(b).T
+
+
 # ------------------------------------------------------ composed flows
 
 

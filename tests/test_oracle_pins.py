@@ -377,3 +377,89 @@ def test_gemm_float_matches_int_gemm_on_codes():
     qb = rng.integers(-127, 128, (9, 64), dtype=np.int8)
     y, _ = oracle.gemm_float(qa.astype(np.float16), qb.astype(np.float16), "f16")
     assert np.array_equal(y.astype(np.int64), oracle.gemm_i32(qa, qb).astype(np.int64))
+
+
+# ------------------------------------------------------------ FP8 (E4M3)
+
+
+def _e4m3_finite_values():
+    vals = []
+    for c in range(256):
+        v = oracle.e4m3_value(c)
+        if not math.isnan(v):
+            vals.append((c, Fraction(v)))
+    return vals
+
+
+def test_e4m3_grid_facts():
+    vals = dict(_e4m3_finite_values())
+    assert len(vals) == 254  # 0x7f and 0xff are NaN
+    assert vals[0x7E] == 448 and vals[0x08] == Fraction(1, 64) and vals[0x01] == Fraction(1, 512)
+    assert vals[0x38] == 1 and vals[0x39] == Fraction(9, 8) and vals[0xB8] == -1
+
+
+def test_e4m3_roundtrip_every_code():
+    for c, v in _e4m3_finite_values():
+        got = int(oracle.round_to_e4m3(np.array([float(v)], np.float32))[0])
+        if v == 0:
+            assert got in (0x00, 0x80) and float(v) == 0
+        else:
+            assert got == c
+
+
+def test_e4m3_nearest_code_brute_force_and_ties():
+    finite = [(c, v) for c, v in _e4m3_finite_values() if c not in (0x80,)]
+
+    def nearest(x: Fraction) -> int:
+        best = None
+        for c, v in finite:
+            d = abs(x - v)
+            if best is None or d < best[0] or (d == best[0] and (c & 1) == 0):
+                best = (d, c)
+        return best[1]
+
+    xs = list(rng.uniform(-460, 460, 400)) + list(rng.uniform(-2, 2, 300)) + \
+        list(rng.uniform(-0.02, 0.02, 200))
+    # crafted ties: midpoints between neighbours go to the even mantissa
+    xs += [1 + 1 / 16, 1 + 3 / 16, -(1 + 1 / 16), 3 / 1024, 5 / 1024, 440.0, 456.0 - 1e-3]
+    x32 = np.array(xs, np.float32)
+    got = oracle.round_to_e4m3(x32)
+    for x, g in zip(x32, got):
+        want = nearest(Fraction(float(x)))
+        if float(x) == 0:
+            continue
+        if want & 0x7F == 0:  # rounds to zero: keeps the sign of x
+            want = 0x80 if x < 0 else 0x00
+        assert int(g) == want, (float(x), int(g), want)
+    assert int(oracle.round_to_e4m3(np.array([1 + 1 / 16], np.float32))[0]) == 0x38  # tie -> 1.0
+    assert int(oracle.round_to_e4m3(np.array([1 + 3 / 16], np.float32))[0]) == 0x3A  # tie -> 1.25
+
+
+def test_quantize_e4m3_range_and_bound():
+    v = (rng.standard_normal((60, 96)) * np.exp(rng.uniform(-6, 6, (60, 1)))).astype(np.float32)
+    v[4] = 0
+    q, d = oracle.quantize_rows_e4m3(v)
+    assert d[4] == 0 and not q[4].any()
+    vals = oracle.e4m3_to_float(q)
+    assert np.isfinite(vals).all() and np.abs(vals).max() <= 448
+    for t in range(60):
+        if t == 4:
+            continue
+        assert np.abs(vals[t]).max() == 448  # the amax element maps to +-448
+        # relative rounding of E4M3 is at most 2^-4 (normals) plus the scale roundings
+        err = np.abs(v[t].astype(float) - vals[t] * float(d[t]))
+        assert (err <= np.abs(v[t]) * (2 ** -4 + 2 ** -20) + float(d[t]) * 2 ** -10).all()
+
+
+def test_gemm_e4m3_brute_force():
+    qa = rng.integers(0, 256, (4, 40)).astype(np.uint8)
+    qb = rng.integers(0, 256, (5, 40)).astype(np.uint8)
+    qa[(qa & 0x7F) == 0x7F] = 0x38  # no NaN codes
+    qb[(qb & 0x7F) == 0x7F] = 0x38
+    c, bound = oracle.gemm_e4m3(qa, qb)
+    vals = {cc: Fraction(oracle.e4m3_value(cc)) for cc in range(256) if (cc & 0x7F) != 0x7F}
+    for i in range(4):
+        for j in range(5):
+            exact = sum(vals[int(qa[i, t])] * vals[int(qb[j, t])] for t in range(40))
+            assert Fraction(c[i, j]) == exact
+            assert Fraction(bound[i, j]) == sum(abs(vals[int(qa[i, t])] * vals[int(qb[j, t])]) for t in range(40))
