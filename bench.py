@@ -37,6 +37,7 @@ if ROOT not in sys.path:
 PEAK_INT8_TOPS = 5000.0  # MI355X dense INT8 MFMA, 10^12 int ops / s
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 PEAK_DENSE16_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA
 METRIC = "W8A8 GEMM TOPS + smooth/quant GB/s (% of MI355X peak), Llama-2-7B shapes"
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -168,6 +169,17 @@ def kernel_breakdown(layers, reps):
         t16 = timed(lambda i: w8.gemm_float(L.x, L.w, L.y), reps)
         d["dense16_gemm"] = dict(us=t16 * 1e6, TFLOPS=ops / t16 / 1e12,
                                  frac_mfma=ops / t16 / 1e12 / PEAK_DENSE16_TFLOPS)
+        # FP8 (E4M3) form of the same layer: codes from the same smoothed tensors
+        qw8, sw8 = w8.scale_quant_rows_e4m3(L.w, L.s)
+        qx8, sx8 = w8.scale_quant_rows_e4m3(L.x, L.inv_s)
+        t = timed(lambda i: w8.scale_quant_rows_e4m3(L.x, L.inv_s, qx8, sx8), reps)
+        by = L.x.numel() * 3 + 4 * (L.M + L.K)
+        d["smooth_quant_act_e4m3"] = dict(us=t * 1e6, GBs=by / t / 1e9,
+                                          frac_hbm=by / t / 1e9 / PEAK_HBM_GBS)
+        t8 = timed(lambda i: w8.gemm_dequant_e4m3(qx8, sx8, qw8, sw8, L.x.dtype, L.y), reps)
+        d["gemm_dequant_e4m3"] = dict(us=t8 * 1e6, TFLOPS=ops / t8 / 1e12,
+                                      frac_mfma=ops / t8 / 1e12 / PEAK_FP8_TFLOPS)
+        del qw8, sw8, qx8, sx8
         out[f"{L.name}_{L.K}x{L.N}"] = {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in d.items()}
     # W8A8 vs the dense 16-bit product on the same shapes, summed over the layers
     t_w8 = sum(v["gemm_dequant"]["us"] for v in out.values())
@@ -175,6 +187,8 @@ def kernel_breakdown(layers, reps):
     t_16 = sum(v["dense16_gemm"]["us"] for v in out.values())
     out["w8a8_vs_dense16"] = {"gemm_speedup": round(t_16 / t_w8, 3),
                               "gemm_plus_act_quant_speedup": round(t_16 / (t_w8 + t_q), 3)}
+    t_8 = sum(v["gemm_dequant_e4m3"]["us"] for v in out.values() if "gemm_dequant_e4m3" in v)
+    out["e4m3_vs_int8"] = {"gemm_time_ratio": round(t_8 / t_w8, 3)}
     return out
 
 

@@ -15,6 +15,8 @@
  *   4. INT8 x INT8 -> INT32 product                    w8a8_gemm_i32 (diagnostic)
  *   5. dequantize with per-token x per-channel scales  w8a8_gemm_dequant (fuses 4+5)
  *   runtime forward = 3 + 4 + 5                         w8a8_linear
+ *   FP8 (E4M3) form of 2/3 and 4+5                      w8a8_scale_quant_rows_e4m3,
+ *                                                       w8a8_gemm_dequant_e4m3
  *
  * Conventions shared by every entry point
  *   - Layout: all matrices are row-major and contiguous.  Activations are
@@ -181,6 +183,45 @@ w8a8_status_t w8a8_gemm_dequant(const int8_t* qa, const float* sa, const int8_t*
  */
 w8a8_status_t w8a8_gemm_float(const void* a, const void* b, void* y, int dtype, int64_t M,
                               int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * FP8 variant of steps 2 and 3: as w8a8_scale_quant_rows, but each row is
+ * quantized to OCP FP8 E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits, largest finite value 448, no infinity) instead of INT8.  The jisaku.com
+ * glossary page on quantization calibration (GPTQ / AWQ / SmoothQuant / QuaRot)
+ * lists "FP8 SmoothQuant" among its methods, and the SmoothQuant page's FAQ
+ * (FP4 and the Blackwell generation) notes that the smoothing transform
+ * carries over to low-bit float formats.  For each row t:
+ *   v_j = fp32(x[t, j]) * col_scale[j]
+ *   m   = max_j |v_j|;  row_scale[t] = m / 448;  r = 448 / m
+ *   q[t, j] = E4M3(v_j * r), round to nearest, ties to even
+ * (|v_j * r| never exceeds 448 by more than fp32 rounding, so no code
+ * saturates or is NaN).  A row with m == 0 gets row_scale 0 and +0 codes
+ * (0x00, or 0x80 where v_j is -0).
+ *
+ *   q  [rows x cols] uint8 E4M3 codes, 16-byte aligned; other arguments and
+ *      rules as w8a8_scale_quant_rows.
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, HIP.
+ */
+w8a8_status_t w8a8_scale_quant_rows_e4m3(const void* x, int dtype, int64_t rows, int64_t cols,
+                                         const float* col_scale, uint8_t* q, float* row_scale,
+                                         hipStream_t stream);
+
+/*
+ * FP8 variant of steps 4 + 5: y[t, k] = out(fp32(fp32(C[t, k]) * sa[t]) * sb[k])
+ * with C[t, k] = sum_j e4m3(qa[t, j]) * e4m3(qb[k, j]) accumulated in fp32 on
+ * the FP8 matrix cores (pages as w8a8_scale_quant_rows_e4m3).  Each product of
+ * two E4M3 values is exact; the order of the fp32 accumulation is
+ * unspecified, so C is within K * 2^-24 * sum_j |a_j b_j| of the exact sum.
+ *
+ *   qa [M x K], qb [N x K] uint8 E4M3 codes (from w8a8_scale_quant_rows_e4m3;
+ *   no NaN codes), 16-byte aligned; sa, sb, y, out_dtype and the shape rules
+ *   as w8a8_gemm_dequant.
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, HIP.
+ */
+w8a8_status_t w8a8_gemm_dequant_e4m3(const uint8_t* qa, const float* sa, const uint8_t* qb,
+                                     const float* sb, void* y, int out_dtype, int64_t M, int64_t N,
+                                     int64_t K, hipStream_t stream);
 
 /* Bytes of workspace w8a8_linear needs for M tokens of K channels
  * (the INT8 activations and their per-token scales, each 256-byte aligned). */

@@ -36,7 +36,7 @@ def declared_symbols():
 def test_library_loads_and_exports_header_symbols():
     lib = _lib.load()
     syms = declared_symbols()
-    assert len(syms) == 10
+    assert len(syms) == 12
     for s in syms:
         assert hasattr(lib, s), s
         assert s in _lib.PROTOTYPES, s
@@ -151,3 +151,22 @@ def test_gemm_float_rejects():
     assert g(P, P, P, 0, 4, 8, (1 << 20) + 8, 0) == ESHAPE
     assert g(PODD, P, P, 0, 4, 8, 16, 0) == EALIGN
     assert g(0, P, 0, 0, 0, 8, 16, 0) == OK  # empty output: no launch
+
+
+@cpu_only
+def test_e4m3_entry_points_reject():
+    lib = _lib.load()
+    f = lib.w8a8_scale_quant_rows_e4m3
+    assert f(0, 0, 4, 16, P, P, P, 0) == ENULL
+    assert f(0, 0, 0, 16, P, 0, 0, 0) == OK  # no rows: nothing to do, no launch
+    assert f(P, 2, 4, 16, P, P, P, 0) == EDTYPE
+    assert f(P, 0, 4, 24, P, P, P, 0) == ESHAPE  # cols % 16
+    assert f(P, 0, 4, 16, P, PODD, P, 0) == EALIGN
+    d = lib.w8a8_gemm_dequant_e4m3
+    assert d(P, 0, P, P, P, 0, 4, 8, 16, 0) == ENULL
+    assert d(P, P, P, P, P, 3, 4, 8, 16, 0) == EDTYPE
+    assert d(P, P, P, P, P, 0, 4, 8, 24, 0) == ESHAPE  # K % 16
+    assert d(P, P, P, P, P, 0, 4, 9, 16, 0) == ESHAPE  # N % 8
+    assert d(PODD, P, P, P, P, 0, 4, 8, 16, 0) == EALIGN
+    assert d(P, P, P, PODD, P, 0, 4, 8, 16, 0) == EALIGN
+    assert d(0, 0, P, P, 0, 0, 0, 8, 16, 0) == OK  # no tokens: no launch

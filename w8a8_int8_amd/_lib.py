@@ -21,6 +21,9 @@ PROTOTYPES = {
     "w8a8_scale_quant_rows": (c_int, [c_vp, c_int, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp]),
     "w8a8_gemm_i32": (c_int, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_vp]),
     "w8a8_gemm_dequant": (c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_vp]),
+    "w8a8_scale_quant_rows_e4m3": (c_int, [c_vp, c_int, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp]),
+    "w8a8_gemm_dequant_e4m3": (c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64,
+                                       c_vp]),
     "w8a8_gemm_float": (c_int, [c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_vp]),
     "w8a8_linear_workspace_bytes": (c_size, [c_i64, c_i64]),
     "w8a8_linear": (c_int, [c_vp, c_int, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_vp, c_size,

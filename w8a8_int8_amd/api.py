@@ -138,6 +138,46 @@ def gemm_dequant(qa: torch.Tensor, sa: torch.Tensor, qb: torch.Tensor, sb: torch
     return y
 
 
+def scale_quant_rows_e4m3(x: torch.Tensor, col_scale: torch.Tensor,
+                          q: Optional[torch.Tensor] = None,
+                          row_scale: Optional[torch.Tensor] = None):
+    """(q uint8 E4M3 codes rows x cols, row_scale fp32[rows]) of x * col_scale per row."""
+    _dev(x, col_scale)
+    rows, cols = x.shape
+    _need(col_scale, torch.float32, (cols,))
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device) if q is None else q
+    row_scale = (torch.empty(rows, dtype=torch.float32, device=x.device)
+                 if row_scale is None else row_scale)
+    _dev(q, row_scale)
+    _need(q, torch.uint8, (rows, cols))
+    _need(row_scale, torch.float32, (rows,))
+    lib = _lib.load()
+    _lib.check("w8a8_scale_quant_rows_e4m3", lib.w8a8_scale_quant_rows_e4m3(
+        _ptr(x), _dtype_code(x), rows, cols, _ptr(col_scale), _ptr(q), _ptr(row_scale),
+        _stream()))
+    return q, row_scale
+
+
+def gemm_dequant_e4m3(qa: torch.Tensor, sa: torch.Tensor, qb: torch.Tensor, sb: torch.Tensor,
+                      out_dtype: torch.dtype = torch.float16,
+                      y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """FP8 form of gemm_dequant: qa, qb hold E4M3 codes (uint8), fp32 accumulation."""
+    _dev(qa, sa, qb, sb)
+    M, K = qa.shape
+    N = qb.shape[0]
+    _need(qa, torch.uint8, (M, K))
+    _need(qb, torch.uint8, (N, K))
+    _need(sa, torch.float32, (M,))
+    _need(sb, torch.float32, (N,))
+    y = torch.empty((M, N), dtype=out_dtype, device=qa.device) if y is None else y
+    _dev(y)
+    _need(y, out_dtype, (M, N))
+    lib = _lib.load()
+    _lib.check("w8a8_gemm_dequant_e4m3", lib.w8a8_gemm_dequant_e4m3(
+        _ptr(qa), _ptr(sa), _ptr(qb), _ptr(sb), _ptr(y), _DT[out_dtype], M, N, K, _stream()))
+    return y
+
+
 def gemm_float(a: torch.Tensor, b: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Dense 16-bit baseline y = a @ b.T (fp16 or bf16 operands, fp32 accumulation)."""
     _dev(a, b)

@@ -92,7 +92,16 @@ w8a8_status_t w8a8_scale_quant_rows(const void* x, int dtype, int64_t rows, int6
   const w8a8_status_t st = check_quant(x, dtype, rows, cols, col_scale, q, row_scale);
   if (st != W8A8_OK) return st;
   return hip_status(w8a8::launch_scale_quant_rows(x, dtype == W8A8_BF16, rows, cols, col_scale,
-                                                  q, row_scale, stream));
+                                                  q, row_scale, 0, stream));
+}
+
+w8a8_status_t w8a8_scale_quant_rows_e4m3(const void* x, int dtype, int64_t rows, int64_t cols,
+                                         const float* col_scale, uint8_t* q, float* row_scale,
+                                         hipStream_t stream) {
+  const w8a8_status_t st = check_quant(x, dtype, rows, cols, col_scale, (const int8_t*)q, row_scale);
+  if (st != W8A8_OK) return st;
+  return hip_status(w8a8::launch_scale_quant_rows(x, dtype == W8A8_BF16, rows, cols, col_scale,
+                                                  q, row_scale, 1, stream));
 }
 
 w8a8_status_t w8a8_gemm_i32(const int8_t* qa, const int8_t* qb, int32_t* c, int64_t M, int64_t N,
@@ -112,6 +121,18 @@ w8a8_status_t w8a8_gemm_dequant(const int8_t* qa, const float* sa, const int8_t*
   if (!aligned(sa, 4) || !aligned(sb, 16)) return W8A8_ERR_ALIGN;
   return hip_status(w8a8::launch_gemm(qa, qb, M, N, K, sa, sb, y, out_dtype == W8A8_BF16 ? 2 : 1,
                                       stream));
+}
+
+w8a8_status_t w8a8_gemm_dequant_e4m3(const uint8_t* qa, const float* sa, const uint8_t* qb,
+                                     const float* sb, void* y, int out_dtype, int64_t M, int64_t N,
+                                     int64_t K, hipStream_t stream) {
+  w8a8_status_t st = check_gemm((const int8_t*)qa, (const int8_t*)qb, y, M, N, K);
+  if (st != W8A8_OK) return st;
+  if ((!sa && M) || (!sb && N)) return W8A8_ERR_NULL;
+  if (!valid_dtype(out_dtype)) return W8A8_ERR_DTYPE;
+  if (!aligned(sa, 4) || !aligned(sb, 16)) return W8A8_ERR_ALIGN;
+  return hip_status(w8a8::launch_gemm((const int8_t*)qa, (const int8_t*)qb, M, N, K, sa, sb, y,
+                                      out_dtype == W8A8_BF16 ? 6 : 5, stream));
 }
 
 w8a8_status_t w8a8_gemm_float(const void* a, const void* b, void* y, int dtype, int64_t M,
@@ -146,7 +167,7 @@ w8a8_status_t w8a8_linear(const void* x, int dtype, const float* inv_s, const in
   st = check_gemm(qx, qw, y, M, N, K);
   if (st != W8A8_OK) return st;
   if (!aligned(sw, 16)) return W8A8_ERR_ALIGN;
-  hipError_t e = w8a8::launch_scale_quant_rows(x, dtype == W8A8_BF16, M, K, inv_s, qx, sx, stream);
+  hipError_t e = w8a8::launch_scale_quant_rows(x, dtype == W8A8_BF16, M, K, inv_s, qx, sx, 0, stream);
   if (e != hipSuccess) return W8A8_ERR_HIP;
   return hip_status(w8a8::launch_gemm(qx, qw, M, N, K, sx, sw, y, dtype == W8A8_BF16 ? 2 : 1,
                                       stream));

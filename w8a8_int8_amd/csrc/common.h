@@ -18,12 +18,14 @@ hipError_t launch_channel_amax(const void* x, bool bf16, int64_t rows, int64_t c
                                hipStream_t st);
 hipError_t launch_smooth_factors(const float* ax, const float* aw, int64_t K, double alpha,
                                  float* s, float* inv_s, hipStream_t st);
+// fmt: 0 = symmetric INT8 codes, 1 = FP8 E4M3 codes
 hipError_t launch_scale_quant_rows(const void* x, bool bf16, int64_t rows, int64_t cols,
-                                   const float* col_scale, int8_t* q, float* row_scale,
+                                   const float* col_scale, void* q, float* row_scale, int fmt,
                                    hipStream_t st);
 // out_mode: 0 = int32 accumulators, 1 = fp16 dequant, 2 = bf16 dequant (int8
 // operands, K in bytes); 3 = fp16, 4 = bf16 dense product (16-bit operands,
-// K in elements, fp32 accumulation)
+// K in elements, fp32 accumulation); 5 = fp16, 6 = bf16 dequant of FP8 E4M3
+// operands (K in bytes, fp32 accumulation)
 hipError_t launch_gemm(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N, int64_t K,
                        const float* sa, const float* sb, void* out, int out_mode,
                        hipStream_t st);

@@ -68,31 +68,53 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 //   2: int8 operands, int32 accumulators dequantized to bf16
 //   3: fp16 operands, fp32 accumulators rounded to fp16 (the dense baseline)
 //   4: bf16 operands, fp32 accumulators rounded to bf16 (the dense baseline)
-// Both operand kinds occupy 32 bytes of K per row per 32 x 32 MFMA in the same
-// 16-bytes-per-lane register layout, so the byte-addressed pipeline is shared.
+//   5: FP8 E4M3 operands, fp32 accumulators dequantized to fp16
+//   6: FP8 E4M3 operands, fp32 accumulators dequantized to bf16
+// A fragment is FR 16-byte chunks per lane: the 32 x 32 MFMAs for int8, fp16
+// and bf16 take 32 bytes of K per row (FR = 1), the FP8 one 64 bytes (FR = 2);
+// the byte-addressed LDS pipeline is the same for all of them.
+typedef int v8i __attribute__((ext_vector_type(8)));
 template <int OUT>
 struct MmaKind {
+  static constexpr int FR = 1;
   typedef v16i acc_t;
-  __device__ static __forceinline__ acc_t mma(v4i a, v4i b, acc_t c) {
-    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+  __device__ static __forceinline__ acc_t mma(const v4i* a, const v4i* b, acc_t c) {
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a[0], b[0], c, 0, 0, 0);
   }
 };
 template <>
 struct MmaKind<3> {
+  static constexpr int FR = 1;
   typedef v16f acc_t;
-  __device__ static __forceinline__ acc_t mma(v4i a, v4i b, acc_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a),
-                                                  __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+  __device__ static __forceinline__ acc_t mma(const v4i* a, const v4i* b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a[0]),
+                                                  __builtin_bit_cast(v8h, b[0]), c, 0, 0, 0);
   }
 };
 template <>
 struct MmaKind<4> {
+  static constexpr int FR = 1;
   typedef v16f acc_t;
-  __device__ static __forceinline__ acc_t mma(v4i a, v4i b, acc_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a),
-                                                   __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+  __device__ static __forceinline__ acc_t mma(const v4i* a, const v4i* b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a[0]),
+                                                   __builtin_bit_cast(v8bf, b[0]), c, 0, 0, 0);
   }
 };
+struct MmaE4m3 {
+  static constexpr int FR = 2;
+  typedef v16f acc_t;
+  // format selectors 0 / 0: both operands FP8 E4M3, no block scales
+  __device__ static __forceinline__ acc_t mma(const v4i* a, const v4i* b, acc_t c) {
+    const v8i a8 = __builtin_shufflevector(a[0], a[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    const v8i b8 = __builtin_shufflevector(b[0], b[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 0, 0, 0, 0, 0, 0);
+  }
+};
+template <>
+struct MmaKind<5> : MmaE4m3 {};
+template <>
+struct MmaKind<6> : MmaE4m3 {};
+
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const int8_t* base, unsigned bytes) {
@@ -171,7 +193,8 @@ k_gemm_i8(const int8_t* __restrict__ qa, const int8_t* __restrict__ qb, int M, i
   constexpr int CPR = BK / 16;                  // 16-byte chunks per LDS row
   constexpr int RPW = 16 / CPR;                 // rows per 256-byte bank window
   constexpr int RPI = 1024 / BK;                // rows filled by one LDS-mode wave load
-  constexpr int KK = BK / 32;                   // 32-deep MFMA k steps per stage
+  constexpr int FR = MmaKind<OUT>::FR;          // 16-byte chunks per fragment
+  constexpr int KK = BK / (32 * FR);            // MFMA k steps per stage
   constexpr int LA = BM / RPI / NW;             // LDS-mode loads per wave per stage, activations
   constexpr int LB = BN / RPI / NW;             // ... weights
   constexpr int L = LA + LB;
@@ -245,21 +268,25 @@ k_gemm_i8(const int8_t* __restrict__ qa, const int8_t* __restrict__ qb, int M, i
 #pragma unroll
     for (int b = 0; b < FM; ++b) acc[a][b] = acc_t{};
 
-  v4i fb0[FN], fa0[FM], fb1[FN], fa1[FM];
+  // fragment f of a lane is chunks FR * (2 * kk + fk) + f of its row (f < FR)
+  v4i fb0[FN * FR], fa0[FM * FR], fb1[FN * FR], fa1[FM * FR];
   auto read_frags = [&](int st, int kk, v4i* fb, v4i* fa) {
     const int8_t* slot = lds + (st % NST) * SLOT;
-    const int ch = ((2 * kk + fk) ^ fsw) << 4;
 #pragma unroll
-    for (int a = 0; a < FN; ++a) fb[a] = *(const v4i*)(slot + off_b + a * 32 * BK + ch);
+    for (int f = 0; f < FR; ++f) {
+      const int ch = ((FR * (2 * kk + fk) + f) ^ fsw) << 4;
 #pragma unroll
-    for (int b = 0; b < FM; ++b) fa[b] = *(const v4i*)(slot + off_a + b * 32 * BK + ch);
+      for (int a = 0; a < FN; ++a) fb[a * FR + f] = *(const v4i*)(slot + off_b + a * 32 * BK + ch);
+#pragma unroll
+      for (int b = 0; b < FM; ++b) fa[b * FR + f] = *(const v4i*)(slot + off_a + b * 32 * BK + ch);
+    }
   };
   auto mfmas = [&](const v4i* fb, const v4i* fa) {
 #pragma unroll
     for (int a = 0; a < FN; ++a)
 #pragma unroll
       for (int b = 0; b < FM; ++b)
-        acc[a][b] = MmaKind<OUT>::mma(fb[a], fa[b], acc[a][b]);
+        acc[a][b] = MmaKind<OUT>::mma(fb + a * FR, fa + b * FR, acc[a][b]);
   };
 
   // Pipeline (stage s lives in slot s % NST).  Iteration kt computes stage kt
@@ -286,7 +313,7 @@ k_gemm_i8(const int8_t* __restrict__ qa, const int8_t* __restrict__ qb, int M, i
         if (kk + 1 < KK) {
           read_frags(kt, kk + 1, nb, na);
           mfmas(cb, ca);
-          interleave<0, FN * FM, FN + FM, 0>();
+          interleave<0, FN * FM, FR * (FN + FM), 0>();
         } else {
           wait_vmcnt<(NST - 2) * L>();  // stage kt+1 landed
           wait_lgkmcnt0();              // this wave's reads of slot kt are done
@@ -294,7 +321,7 @@ k_gemm_i8(const int8_t* __restrict__ qa, const int8_t* __restrict__ qb, int M, i
           dma(kt + NST);
           read_frags(kt + 1, 0, nb, na);
           mfmas(cb, ca);
-          interleave<0, FN * FM, FN + FM, L>();
+          interleave<0, FN * FM, FR * (FN + FM), L>();
         }
       }
     }
@@ -317,7 +344,7 @@ k_gemm_i8(const int8_t* __restrict__ qa, const int8_t* __restrict__ qb, int M, i
     const int m = m0 + wm * WM + b * 32 + (lane & 31);
     if (m >= M) continue;
     float am = 0.0f;
-    if (OUT == 1 || OUT == 2) am = sa[m];
+    if (OUT == 1 || OUT == 2 || OUT == 5 || OUT == 6) am = sa[m];
 #pragma unroll
     for (int a = 0; a < FN; ++a) {
 #pragma unroll
@@ -328,7 +355,7 @@ k_gemm_i8(const int8_t* __restrict__ qa, const int8_t* __restrict__ qb, int M, i
         if (OUT == 0) {
           v4i o = {(int)C[4 * g + 0], (int)C[4 * g + 1], (int)C[4 * g + 2], (int)C[4 * g + 3]};
           *(v4i*)((int32_t*)out + (int64_t)m * N + n) = o;
-        } else if (OUT >= 3) {
+        } else if (OUT == 3 || OUT == 4) {
           unsigned short h[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e)
@@ -346,7 +373,7 @@ k_gemm_i8(const int8_t* __restrict__ qa, const int8_t* __restrict__ qb, int M, i
             float y = (float)C[4 * g + e];
             y = y * am;
             y = y * w[e];
-            h[e] = OUT == 1 ? f32_to_f16_rne(y) : f32_to_bf16_rne(y);
+            h[e] = (OUT == 1 || OUT == 5) ? f32_to_f16_rne(y) : f32_to_bf16_rne(y);
           }
           uint2 o;
           o.x = (unsigned)h[0] | ((unsigned)h[1] << 16);
@@ -491,8 +518,16 @@ hipError_t launch_tile(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N,
       hipLaunchKernelGGL((k_gemm_i8<BM, BN, BK, NST, WGM, WGN, 3>), grid, block, 0, st, qa, qb, (int)M,
                          (int)N, (int)K, sa, sb, out, mt, nt);
       break;
-    default:
+    case 4:
       hipLaunchKernelGGL((k_gemm_i8<BM, BN, BK, NST, WGM, WGN, 4>), grid, block, 0, st, qa, qb, (int)M,
+                         (int)N, (int)K, sa, sb, out, mt, nt);
+      break;
+    case 5:
+      hipLaunchKernelGGL((k_gemm_i8<BM, BN, BK, NST, WGM, WGN, 5>), grid, block, 0, st, qa, qb, (int)M,
+                         (int)N, (int)K, sa, sb, out, mt, nt);
+      break;
+    default:
+      hipLaunchKernelGGL((k_gemm_i8<BM, BN, BK, NST, WGM, WGN, 6>), grid, block, 0, st, qa, qb, (int)M,
                          (int)N, (int)K, sa, sb, out, mt, nt);
       break;
   }
@@ -505,14 +540,15 @@ hipError_t launch_gemm(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N,
                        const float* sa, const float* sb, void* out, int out_mode,
                        hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
-  // fp16 / bf16 operands: K counts elements; the tiled kernel works in bytes
-  const bool dense16 = out_mode >= 3;
-  if (dense16) K *= 2;
+  // fp16 / bf16 operands: K counts elements; the tiled kernel works in bytes.
+  // The skinny few-token kernel serves the INT8 modes only.
+  const bool tiled_only = out_mode >= 3;
+  if (out_mode == 3 || out_mode == 4) K *= 2;
   // Few tokens: weight streaming, handled by the skinny kernel.  Between 17
   // and 32 tokens it reads two activation fragments per step, and the tiled
   // kernel is as fast once N alone gives it 128 or more blocks.
-  if (!dense16 && M <= 16) return launch_skinny<1>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
-  if (!dense16 && M <= 32 && N < 16384)
+  if (!tiled_only && M <= 16) return launch_skinny<1>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
+  if (!tiled_only && M <= 32 && N < 16384)
     return launch_skinny<2>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
   // Pick the tile whose last wave of blocks over 256 CUs is fullest, with a
   // small preference for the larger tile (more MACs per byte of LDS traffic).

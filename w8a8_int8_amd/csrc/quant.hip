@@ -1,4 +1,4 @@
-// Per-column scale followed by per-row symmetric INT8 quantization.
+// Per-column scale followed by per-row symmetric INT8 (or FP8 E4M3) quantization.
 //
 // Method: jisaku.com glossary page "SmoothQuant", section "平滑化変換の数学"
 // (X~ = X s^-1, W~ = s W) and section "Activation外れ値問題" (INT8 range); the
@@ -21,6 +21,10 @@
 // before the first reduction.  The row max is a wave-level butterfly followed
 // by one LDS round across the waves of the block.  Per element the VALU work
 // is about six operations (widen, scale, max, rescale, round, pack/4).
+//
+// The FP8 variant (same smoothing, FP8 E4M3 grid as the page's remark on
+// low-bit float formats allows) differs only in the grid maximum (448) and in
+// the rounding: the hardware conversion to E4M3, round to nearest even.
 #include "common.h"
 
 namespace w8a8 {
@@ -55,7 +59,28 @@ __device__ __forceinline__ float elem(const v4u& c, int e) {
   return widen16((unsigned short)((e & 1) ? (w >> 16) : (w & 0xffffu)), false);
 }
 
-template <int CPT, int R, bool BF16>
+// |v| above 448 (by at most the fp32 rounding of v * (448 / m)) rounds to 448
+// on the E4M3 grid; clamp it explicitly so the conversion never sees an
+// out-of-range input.  The sign, including that of zero, is kept.
+__device__ __forceinline__ float clamp_e4m3(float v) {
+  return fabsf(v) > 448.0f ? copysignf(448.0f, v) : v;
+}
+
+// Four FP8 (E4M3) codes of a, b, c, d packed little-endian.  The hardware
+// conversion rounds to nearest even and keeps the sign of zero, like the
+// format's definition (checked bit for bit against it).
+__device__ __forceinline__ unsigned pack_e4m3(float a, float b, float c, float d) {
+  a = clamp_e4m3(a);
+  b = clamp_e4m3(b);
+  c = clamp_e4m3(c);
+  d = clamp_e4m3(d);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (unsigned)w;
+}
+
+// FMT 0: symmetric INT8 codes (grid max 127); FMT 1: FP8 E4M3 codes (max 448).
+template <int CPT, int R, bool BF16, int FMT>
 __global__ __launch_bounds__(1024) void k_scale_quant_rows(const v4u* __restrict__ x, int64_t rows,
                                                            int cols8,
                                                            const float4* __restrict__ col_scale,
@@ -130,8 +155,9 @@ __global__ __launch_bounds__(1024) void k_scale_quant_rows(const v4u* __restrict
     const int64_t row = row0 + r;
     if (row >= rows) break;
     const float mr = m[r];
-    const float rcp = mr > 0.0f ? 127.0f / mr : 0.0f;
-    if (tid == 0) row_scale[row] = mr > 0.0f ? mr / 127.0f : 0.0f;
+    constexpr float kGridMax = FMT == 0 ? 127.0f : 448.0f;
+    const float rcp = mr > 0.0f ? kGridMax / mr : 0.0f;
+    if (tid == 0) row_scale[row] = mr > 0.0f ? mr / kGridMax : 0.0f;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = i * G + tid;
@@ -140,33 +166,50 @@ __global__ __launch_bounds__(1024) void k_scale_quant_rows(const v4u* __restrict
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         t[e] = v[r][i][e] * rcp;
-        t[e] = t[e] + kRoundMagic;
+        if (FMT == 0) t[e] = t[e] + kRoundMagic;
       }
       uint2 o;
-      o.x = pack_codes(t[0], t[1], t[2], t[3]);
-      o.y = pack_codes(t[4], t[5], t[6], t[7]);
+      if (FMT == 0) {
+        o.x = pack_codes(t[0], t[1], t[2], t[3]);
+        o.y = pack_codes(t[4], t[5], t[6], t[7]);
+      } else {
+        o.x = pack_e4m3(t[0], t[1], t[2], t[3]);
+        o.y = pack_e4m3(t[4], t[5], t[6], t[7]);
+      }
       q[row * cols8 + c] = o;
     }
   }
 }
 
 template <int CPT, int R>
-hipError_t launch_cfg(const void* x, bool bf16, int64_t rows, int cols8, int G,
-                      const float* col_scale, int8_t* q, float* row_scale, hipStream_t st) {
+hipError_t launch_cfg(const void* x, bool bf16, int fmt, int64_t rows, int cols8, int G,
+                      const float* col_scale, void* q, float* row_scale, hipStream_t st) {
   const unsigned blocks = (unsigned)((rows + R - 1) / R);
-  if (bf16)
-    hipLaunchKernelGGL((k_scale_quant_rows<CPT, R, true>), dim3(blocks), dim3(G), 0, st,
-                       (const v4u*)x, rows, cols8, (const float4*)col_scale, (uint2*)q, row_scale);
-  else
-    hipLaunchKernelGGL((k_scale_quant_rows<CPT, R, false>), dim3(blocks), dim3(G), 0, st,
-                       (const v4u*)x, rows, cols8, (const float4*)col_scale, (uint2*)q, row_scale);
+  const v4u* xv = (const v4u*)x;
+  const float4* cs = (const float4*)col_scale;
+  uint2* qv = (uint2*)q;
+  if (fmt == 0) {
+    if (bf16)
+      hipLaunchKernelGGL((k_scale_quant_rows<CPT, R, true, 0>), dim3(blocks), dim3(G), 0, st, xv,
+                         rows, cols8, cs, qv, row_scale);
+    else
+      hipLaunchKernelGGL((k_scale_quant_rows<CPT, R, false, 0>), dim3(blocks), dim3(G), 0, st, xv,
+                         rows, cols8, cs, qv, row_scale);
+  } else {
+    if (bf16)
+      hipLaunchKernelGGL((k_scale_quant_rows<CPT, R, true, 1>), dim3(blocks), dim3(G), 0, st, xv,
+                         rows, cols8, cs, qv, row_scale);
+    else
+      hipLaunchKernelGGL((k_scale_quant_rows<CPT, R, false, 1>), dim3(blocks), dim3(G), 0, st, xv,
+                         rows, cols8, cs, qv, row_scale);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_scale_quant_rows(const void* x, bool bf16, int64_t rows, int64_t cols,
-                                   const float* col_scale, int8_t* q, float* row_scale,
+                                   const float* col_scale, void* q, float* row_scale, int fmt,
                                    hipStream_t st) {
   if (rows == 0) return hipSuccess;
   const int cols8 = (int)(cols / 8);
@@ -181,14 +224,14 @@ hipError_t launch_scale_quant_rows(const void* x, bool bf16, int64_t rows, int64
   if (G > 1024) G = 1024;
   const int cpt = (cols8 + G - 1) / G;
   switch (cpt <= 1 ? 1 : cpt) {
-    case 1: return launch_cfg<1, 4>(x, bf16, rows, cols8, G, col_scale, q, row_scale, st);
-    case 2: return launch_cfg<2, 2>(x, bf16, rows, cols8, G, col_scale, q, row_scale, st);
-    case 3: return launch_cfg<3, 1>(x, bf16, rows, cols8, G, col_scale, q, row_scale, st);
-    case 4: return launch_cfg<4, 1>(x, bf16, rows, cols8, G, col_scale, q, row_scale, st);
-    case 5: return launch_cfg<5, 1>(x, bf16, rows, cols8, G, col_scale, q, row_scale, st);
-    case 6: return launch_cfg<6, 1>(x, bf16, rows, cols8, G, col_scale, q, row_scale, st);
-    case 7: return launch_cfg<7, 1>(x, bf16, rows, cols8, G, col_scale, q, row_scale, st);
-    case 8: return launch_cfg<8, 1>(x, bf16, rows, cols8, G, col_scale, q, row_scale, st);
+    case 1: return launch_cfg<1, 4>(x, bf16, fmt, rows, cols8, G, col_scale, q, row_scale, st);
+    case 2: return launch_cfg<2, 2>(x, bf16, fmt, rows, cols8, G, col_scale, q, row_scale, st);
+    case 3: return launch_cfg<3, 1>(x, bf16, fmt, rows, cols8, G, col_scale, q, row_scale, st);
+    case 4: return launch_cfg<4, 1>(x, bf16, fmt, rows, cols8, G, col_scale, q, row_scale, st);
+    case 5: return launch_cfg<5, 1>(x, bf16, fmt, rows, cols8, G, col_scale, q, row_scale, st);
+    case 6: return launch_cfg<6, 1>(x, bf16, fmt, rows, cols8, G, col_scale, q, row_scale, st);
+    case 7: return launch_cfg<7, 1>(x, bf16, fmt, rows, cols8, G, col_scale, q, row_scale, st);
+    case 8: return launch_cfg<8, 1>(x, bf16, fmt, rows, cols8, G, col_scale, q, row_scale, st);
     default: return hipErrorInvalidValue;
   }
 }
