@@ -6,8 +6,8 @@ and is never on the product path.
 
 It is the plain, slow, step-by-step definition of what the path computes,
 written from the jisaku.com glossary page "SmoothQuant" (cited below by section
-name) and, where that page is silent, from the readings listed in the design
-notes (R-numbers).  Every floating-point step that decides an INT8 code is done
+name); where that page is silent, each docstring states the reading taken.
+Every floating-point step that decides an INT8 code is done
 in IEEE fp32 (numpy float32 ufuncs: one correctly rounded operation each, no
 fused multiply-add); the smoothing factors are formed in fp64 and rounded once
 to fp32.  Integer results (codes, accumulators) are exact.
@@ -25,7 +25,7 @@ import math
 
 import numpy as np
 
-QMAX = 127  # symmetric INT8 grid [-127, 127] (R2)
+QMAX = 127  # symmetric INT8 grid [-127, 127]: -128 is never produced
 
 
 # ---------------------------------------------------------------- dtypes
@@ -53,7 +53,7 @@ def round_to_bf16(v: np.ndarray) -> np.ndarray:
 
     Written from the IEEE definition: keep the upper 16 bits of the fp32
     pattern, rounding by the discarded lower 16 bits (above half: up; exactly
-    half: up only if the kept last bit is 1).  Inputs are finite (R18).
+    half: up only if the kept last bit is 1).  Inputs are finite.
     Pinned by tests/test_oracle_pins.py::test_round_to_bf16_*.
     """
     bits = np.ascontiguousarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
@@ -64,7 +64,7 @@ def round_to_bf16(v: np.ndarray) -> np.ndarray:
 
 
 def narrow(v: np.ndarray, dtype: str) -> np.ndarray:
-    """float32 -> output storage dtype with round to nearest even (R11, R12)."""
+    """float32 -> output storage dtype (the activation dtype) with round to nearest even."""
     if dtype == "f16":
         return v.astype(np.float16)  # numpy's conversion is correctly rounded
     if dtype == "bf16":
@@ -81,7 +81,7 @@ def channel_amax(x, dtype: str, amax=None) -> np.ndarray:
     Section "ハイパーパラメータ α" uses max(|X_j|) (over calibration tokens,
     channel j) and max(|W_j|) (over output channels, input channel j); the
     usage example's ``get_act_scales`` collects the activation statistic.  For
-    X (T x K) and for W (N x K) this is the max over axis 0 (R4).  ``amax``
+    X (T x K) and for W (N x K) this is the max over axis 0.  ``amax``
     (float32[K]) is the running value from earlier batches; the max is exact
     and order free, so batches may be folded in any order.
     Pinned by test_channel_amax_* (brute force, resumability, membership).
@@ -99,8 +99,8 @@ def smooth_factor(a: float, b: float, alpha: float) -> float:
     """s_j = max|X_j|**alpha / max|W_j|**(1 - alpha) (section "ハイパーパラメータ α").
 
     Formed in fp64 with the C library's pow and one division, then rounded
-    once to fp32 (R5).  A channel whose activation or weight maximum is zero
-    gets s = 1 (R6).
+    once to fp32 (the page does not fix the precision).  A channel whose
+    activation or weight maximum is zero gets s = 1, so there is no inf/NaN.
     Pinned by test_smooth_factor_alpha_limits / _alpha_half / _balance / _dead.
     """
     if a == 0.0 or b == 0.0:
@@ -109,7 +109,7 @@ def smooth_factor(a: float, b: float, alpha: float) -> float:
 
 
 def smooth_factors(amax_x, amax_w, alpha: float):
-    """Vector form of :func:`smooth_factor` plus inv_s = RN32(1 / s) (R7).
+    """Vector form of :func:`smooth_factor` plus inv_s = RN32(1 / s), the stored reciprocal.
 
     Returns (s, inv_s), both float32[K].
     """
@@ -141,9 +141,10 @@ def smooth_fp64(x64: np.ndarray, w64: np.ndarray, s: np.ndarray):
 def apply_col_scale(v32: np.ndarray, c) -> np.ndarray:
     """v[t, j] * c[j] in fp32, one rounding per element.
 
-    With c = inv_s on activations this is X diag(s)^-1 (R7: multiply by the
-    stored reciprocal); with c = s on weights it is the fold diag(s) W, kept in
-    fp32 and not rounded to the model dtype (R8).
+    With c = inv_s on activations this is X diag(s)^-1 (a multiplication by
+    the stored reciprocal, not a per-element division); with c = s on weights
+    it is the fold diag(s) W, kept in fp32 and not rounded to the model dtype
+    before it is quantized.
     """
     return (np.asarray(v32, dtype=np.float32) * np.asarray(c, dtype=np.float32)[None, :]).astype(np.float32)
 
@@ -152,13 +153,14 @@ def apply_col_scale(v32: np.ndarray, c) -> np.ndarray:
 
 
 def quantize_rows(v32: np.ndarray):
-    """Symmetric per-row INT8 quantization (R2, R3, R9, R10).
+    """Symmetric per-row INT8 quantization.
 
     For each row: amax = max |v|; delta = RN32(amax / 127) is the stored
     dequant scale; r = RN32(127 / amax); code = clamp(RNE(RN32(v * r)),
     -127, 127).  A zero row gives all-zero codes and delta = 0.  Section
     "Activation外れ値問題" gives the INT8 range; the symmetric grid, the
-    per-row granularity and round-half-even are readings R2, R3, R9.
+    per-row (per-token / per-output-channel) granularity and round-half-even
+    are readings where the page is silent.
     Returns (q int8[rows, cols], delta float32[rows]).
     Pinned by test_quantize_* (exhaustive nearest code, ties, range, bound).
     """
@@ -215,7 +217,7 @@ def gemm_i32(qa: np.ndarray, qb: np.ndarray) -> np.ndarray:
 
 
 def dequant(c: np.ndarray, sa, sb, out_dtype: str) -> np.ndarray:
-    """Y[t, k] = out(RN32(RN32(f32(C[t, k]) * sa[t]) * sb[k])) (R11).
+    """Y[t, k] = out(RN32(RN32(f32(C[t, k]) * sa[t]) * sb[k])), left to right, no FMA.
 
     f32(C) rounds the int32 accumulator to nearest even; each product is one
     fp32 rounding, applied left to right; the final conversion to fp16 / bf16

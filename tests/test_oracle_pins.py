@@ -150,7 +150,8 @@ def test_smooth_factor_balance():
 
 def test_smooth_factor_alpha_semantics():
     """alpha = 1 normalises the activation channels (all difficulty goes to W);
-    alpha = 0 normalises the weight channels (reading R1 of the page's labels)."""
+    alpha = 0 normalises the weight channels (the printed formula governs where
+    the page's labels of the two limits contradict it)."""
     a, b = _rand_amax(50), _rand_amax(50)
     s1, _ = oracle.smooth_factors(a, b, 1.0)
     assert np.allclose(a.astype(float) / s1, 1.0)
@@ -463,3 +464,19 @@ def test_gemm_e4m3_brute_force():
             exact = sum(vals[int(qa[i, t])] * vals[int(qb[j, t])] for t in range(40))
             assert Fraction(c[i, j]) == exact
             assert Fraction(bound[i, j]) == sum(abs(vals[int(qa[i, t])] * vals[int(qb[j, t])]) for t in range(40))
+
+
+def test_e4m3_every_midpoint():
+    """Each midpoint between neighbouring finite E4M3 magnitudes rounds to the
+    neighbour with the even code (ties to even), and the fp32 values just
+    either side of it round to the nearer neighbour; both signs."""
+    pos = sorted((v, c) for c, v in _e4m3_finite_values() if c < 0x80)
+    for (v0, c0), (v1, c1) in zip(pos, pos[1:]):
+        mid = (v0 + v1) / 2
+        m32 = np.float32(float(mid))
+        assert Fraction(float(m32)) == mid  # exact in fp32
+        even = c0 if c0 % 2 == 0 else c1
+        below = np.nextafter(m32, np.float32(0))
+        above = np.nextafter(m32, np.float32(1000))
+        got = oracle.round_to_e4m3(np.array([m32, below, above, -m32, -below, -above], np.float32))
+        assert [int(g) for g in got] == [even, c0, c1, even | 0x80, c0 | 0x80, c1 | 0x80], (mid, c0, c1)
