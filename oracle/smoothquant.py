@@ -344,6 +344,61 @@ def gemm_e4m3(qa: np.ndarray, qb: np.ndarray):
     return a @ b.T, np.abs(a) @ np.abs(b).T
 
 
+# ------------------------------------- smoothing folded into an RMS norm
+#
+# The page's X~ = X s^-1 (section "平滑化変換の数学") is a per-channel
+# multiplication; where X is the output of an RMS normalisation (the norm in
+# front of the attention and MLP projections of LLaMA-family decoders) it can
+# be folded into that norm's per-channel weight gamma.  The fold itself is an
+# extension beyond the page.  Reading taken: the per-token quantizer is
+# invariant to a positive factor common to a row, so the norm's 1 / rms(x_t)
+# moves from the elements into the row's scale; the codes are those of
+# x * RN32(gamma * inv_s), and the row scale is RN32(m / 127) / rms(x_t).
+
+
+def rms_inv(x, dtype: str, eps: float) -> np.ndarray:
+    """r_t = 1 / sqrt(mean_j x[t, j]^2 + eps), in fp64 (float64[rows]).
+
+    The sum of squares is math.fsum's correctly rounded sum of the exact
+    squares (each fp16 / bf16 square is exact in fp64), so r is within a few
+    fp64 ulps of the real value; a zero row with eps = 0 gives +inf.
+    Pinned by test_rms_inv_*.
+    """
+    x64 = widen(x, dtype).astype(np.float64)
+    K = x64.shape[1]
+    out = np.empty(x64.shape[0], dtype=np.float64)
+    for t in range(x64.shape[0]):
+        v = math.fsum((x64[t] * x64[t]).tolist()) / K + float(eps)
+        out[t] = math.inf if v == 0.0 else 1.0 / math.sqrt(v)
+    return out
+
+
+def rmsnorm_fp64(x, dtype: str, gamma, eps: float) -> np.ndarray:
+    """The plain RMS normalisation x[t, j] * r_t * gamma_j, in fp64."""
+    r = rms_inv(x, dtype, eps)
+    return widen(x, dtype).astype(np.float64) * r[:, None] * np.asarray(gamma, np.float64)[None, :]
+
+
+def rmsnorm_smooth_quant_rows(x, dtype: str, gamma, inv_s, eps: float):
+    """Per-token INT8 of RMSNorm(x; gamma) * inv_s with the smoothing folded in.
+
+    g_j = RN32(gamma_j * inv_s_j) is the folded norm weight; the codes and
+    m / 127 are those of scale_quant_rows(x, g); the row scale is
+    delta_t = RN32(m_t / 127) * r_t, returned in fp64 (the reference the
+    device's fp32 evaluation is held to).  A zero row has delta 0.
+    Returns (q int8[rows, cols], delta float64[rows]).
+    Pinned by test_rmsnorm_quant_* (against the plain fp64 definition within
+    the quantization bound, closed forms, scale invariance).
+    """
+    g = (np.asarray(gamma, np.float32) * np.asarray(inv_s, np.float32)).astype(np.float32)
+    q, d = scale_quant_rows(x, dtype, g)
+    r = rms_inv(x, dtype, eps)
+    delta = np.zeros(len(d), dtype=np.float64)
+    nz = d > 0
+    delta[nz] = d[nz].astype(np.float64) * r[nz]
+    return q, delta
+
+
 # ------------------------------------------------------ composed flows
 
 

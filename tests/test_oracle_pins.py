@@ -480,3 +480,64 @@ def test_e4m3_every_midpoint():
         above = np.nextafter(m32, np.float32(1000))
         got = oracle.round_to_e4m3(np.array([m32, below, above, -m32, -below, -above], np.float32))
         assert [int(g) for g in got] == [even, c0, c1, even | 0x80, c0 | 0x80, c1 | 0x80], (mid, c0, c1)
+
+
+# ------------------------------------------- smoothing folded into an RMS norm
+
+
+def test_rms_inv_closed_forms():
+    x = np.array([[2.0] * 8, [-0.25] * 8, [3.0, 4.0] * 4, [0.0] * 8], np.float16)
+    r = oracle.rms_inv(x, "f16", 0.0)
+    assert r[0] == 0.5 and r[1] == 4.0
+    assert r[2] == 1.0 / math.sqrt(12.5)
+    assert r[3] == math.inf
+    r = oracle.rms_inv(x, "f16", 0.75)
+    assert r[3] == 1.0 / math.sqrt(0.75) and r[0] == 1.0 / math.sqrt(4.75)
+
+
+def test_rms_inv_against_decimal():
+    from decimal import Decimal, getcontext
+    getcontext().prec = 50
+    x = (rng.standard_normal((6, 40)) * np.exp(rng.uniform(-4, 4, (6, 1)))).astype(np.float16)
+    eps = 1e-6
+    r = oracle.rms_inv(x, "f16", eps)
+    for t in range(6):
+        ms = sum(Fraction(float(v)) ** 2 for v in x[t]) / 40 + Fraction(eps)
+        want = 1 / (Decimal(ms.numerator) / Decimal(ms.denominator)).sqrt()
+        assert abs(Decimal(r[t]) - want) <= abs(want) * Decimal(2) ** -51
+
+
+def _rms_case(rows, cols, seed):
+    g = np.random.default_rng(seed)
+    x = g.standard_normal((rows, cols)) * np.exp(g.uniform(-3, 3, (rows, 1)))
+    x[:, g.choice(cols, 3, replace=False)] *= 60.0  # outlier channels
+    gamma = g.uniform(0.2, 2.0, cols).astype(np.float32)
+    inv_s = np.exp(g.uniform(-4, 2, cols)).astype(np.float32)
+    return x.astype(np.float16), gamma, inv_s
+
+
+def test_rmsnorm_quant_matches_plain_definition():
+    """Dequantized codes against the plain fp64 RMSNorm(x; gamma) * inv_s:
+    within half a quantization step (the quantizer's bound) plus the two fp32
+    roundings of the fold and the scaling."""
+    x, gamma, inv_s = _rms_case(24, 96, 7)
+    for eps in (0.0, 1e-5, 3.0):
+        q, delta = oracle.rmsnorm_smooth_quant_rows(x, "f16", gamma, inv_s, eps)
+        plain = oracle.rmsnorm_fp64(x, "f16", gamma, eps) * inv_s.astype(np.float64)[None, :]
+        deq = q.astype(np.float64) * delta[:, None]
+        tol = delta[:, None] / 2 * (1 + 2.0 ** -13) + np.abs(plain) * 2.0 ** -22
+        assert (np.abs(deq - plain) <= tol).all()
+        assert (np.abs(q).max(axis=1) == 127).all()
+
+
+def test_rmsnorm_quant_scale_invariance_and_zero_row():
+    x, gamma, inv_s = _rms_case(10, 64, 9)
+    x[3] = 0
+    q1, d1 = oracle.rmsnorm_smooth_quant_rows(x, "f16", gamma, inv_s, 0.0)
+    x2 = (x.astype(np.float32) * 4).astype(np.float16)  # exact: a power of two, no overflow
+    q2, d2 = oracle.rmsnorm_smooth_quant_rows(x2, "f16", gamma, inv_s, 0.0)
+    assert np.array_equal(q1, q2) and np.array_equal(d1, d2)
+    assert not q1[3].any() and d1[3] == 0.0
+    # the codes are those of the smoothing quantizer with the folded weight
+    qs, ds = oracle.scale_quant_rows(x, "f16", (gamma * inv_s).astype(np.float32))
+    assert np.array_equal(q1, qs)
