@@ -100,7 +100,8 @@ class Layer:
         self.cal = [synth.calibration(wl, li, wl.cal_batch, chunk=i, device=dev)
                     for i in range(n_batches)]
         self.w = synth.weights(wl, li, device=dev)
-        self.x = synth.activations(wl, li, self.M, device=dev)
+        self.x_all = synth.activations(wl, li, max(wl.M), device=dev)
+        self.x = self.x_all[:self.M]
         f32 = dict(dtype=torch.float32, device=dev)
         self.amax_x = torch.zeros(self.K, **f32)
         self.amax_w = torch.zeros(self.K, **f32)
@@ -115,6 +116,12 @@ class Layer:
 
     def gemm_ops(self):
         return 2.0 * self.M * self.N * self.K
+
+    def gemm_bytes(self, M=None):
+        """Algorithmic HBM bytes of one GEMM launch: both INT8 operands once,
+        the 16-bit output once, the two scale vectors."""
+        M = self.M if M is None else M
+        return float(M * self.K + self.N * self.K + 2 * M * self.N + 4 * (M + self.N))
 
     def step(self, i, ev=None):
         w8 = self.w8
@@ -169,6 +176,12 @@ def kernel_breakdown(layers, reps):
         t16 = timed(lambda i: w8.gemm_float(L.x, L.w, L.y), reps)
         d["dense16_gemm"] = dict(us=t16 * 1e6, TFLOPS=ops / t16 / 1e12,
                                  frac_mfma=ops / t16 / 1e12 / PEAK_DENSE16_TFLOPS)
+        # the smoothing folded into the RMS norm in front of the layer (x taken as the norm's input)
+        g = w8.fold_norm_weight(torch.ones(L.K, dtype=torch.float32, device=L.x.device), L.inv_s)
+        t = timed(lambda i: w8.rmsnorm_quant_rows(L.x, g, 1e-5, L.qx, L.sx), reps)
+        by = L.x.numel() * 3 + 4 * (L.M + L.K)
+        d["rmsnorm_smooth_quant_act"] = dict(us=t * 1e6, GBs=by / t / 1e9,
+                                             frac_hbm=by / t / 1e9 / PEAK_HBM_GBS)
         # FP8 (E4M3) form of the same layer: codes from the same smoothed tensors
         qw8, sw8 = w8.scale_quant_rows_e4m3(L.w, L.s)
         qx8, sx8 = w8.scale_quant_rows_e4m3(L.x, L.inv_s)
@@ -189,6 +202,48 @@ def kernel_breakdown(layers, reps):
                               "gemm_plus_act_quant_speedup": round(t_16 / (t_w8 + t_q), 3)}
     t_8 = sum(v["gemm_dequant_e4m3"]["us"] for v in out.values() if "gemm_dequant_e4m3" in v)
     out["e4m3_vs_int8"] = {"gemm_time_ratio": round(t_8 / t_w8, 3)}
+    return out
+
+
+def decode_sweep(wl, layers, reps):
+    """Every token count of a few-token workload through each layer: the
+    runtime forward (smooth + quant, then the GEMM), and the GEMM alone against
+    the HBM roofline (it streams the INT8 weight once)."""
+    import torch
+
+    w8 = layers[0].w8
+    out = {}
+    for L in layers:
+        for M in wl.M:
+            x = L.x_all[:M]
+            y = torch.empty((M, L.N), dtype=L.x.dtype, device=L.x.device)
+            ws = torch.empty(max(w8.linear_workspace_bytes(M, L.K), 1), dtype=torch.uint8,
+                             device=L.x.device)
+            qx = ws[:M * L.K].view(torch.int8).view(M, L.K)
+            off = (M * L.K + 255) // 256 * 256
+            sx = ws[off:off + 4 * M].view(torch.float32)
+            w8.linear(x, L.inv_s, L.qw, L.sw, y, ws)
+
+            def run(fn, n=reps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                fn()
+                torch.cuda.synchronize()
+                a.record()
+                for _ in range(n):
+                    fn()
+                b.record()
+                b.synchronize()
+                return a.elapsed_time(b) / n * 1e-3
+
+            t_lin = run(lambda: w8.linear(x, L.inv_s, L.qw, L.sw, y, ws))
+            t_g = run(lambda: w8.gemm_dequant(qx, sx, L.qw, L.sw, L.x.dtype, y))
+            by = L.gemm_bytes(M)
+            out[f"{L.name}_{L.K}x{L.N}_M{M}"] = {
+                "linear_us": round(t_lin * 1e6, 3),
+                "gemm_us": round(t_g * 1e6, 3),
+                "gemm_GBs": round(by / t_g / 1e9, 1),
+                "gemm_frac_hbm": round(by / t_g / 1e9 / PEAK_HBM_GBS, 4),
+            }
     return out
 
 
@@ -279,9 +334,14 @@ def main():
     gemm_launch_avg = sum(gemm_s) / (len(gemm_s) * len(layers))
     ops_per_launch = ops_per_step / len(layers)
     achieved = ops_per_launch / gemm_launch_avg / 1e12
+    # few tokens (decode): the GEMM streams the weight and is HBM-bound
+    decode = wl.M[0] <= 32
+    bytes_per_launch = sum(L.gemm_bytes() for L in layers) / len(layers)
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
 
     kernels = kernel_breakdown(layers, args.kernel_reps)
+    if decode:
+        kernels["decode_sweep"] = decode_sweep(wl, layers, max(args.kernel_reps, 20))
     print("[bench] per-kernel pass done", file=sys.stderr, flush=True)
 
     traffic = pmc_traffic(wl.name)
@@ -315,6 +375,16 @@ def main():
             "frac": round(achieved / PEAK_INT8_TOPS, 4),
             "traffic": traffic,
             "ops_per_launch": ops_per_launch,
+            "avg_launch_us": round(gemm_launch_avg * 1e6, 3),
+        } if not decode else {
+            "kernel": "gemm_dequant (k_gemm_skinny)",
+            "bound": "hbm",
+            "achieved": round(bytes_per_launch / gemm_launch_avg / 1e9, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(bytes_per_launch / gemm_launch_avg / 1e9 / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": bytes_per_launch,
             "avg_launch_us": round(gemm_launch_avg * 1e6, 3),
         },
         "kernels": kernels,

@@ -12,6 +12,8 @@
  *      fold s into W and quantize W per output channel w8a8_channel_amax (on W)
  *                                                       + w8a8_scale_quant_rows
  *   3. X diag(s)^-1 and per-token INT8 quantization    w8a8_scale_quant_rows
+ *      ... folded into the RMS norm that produces X     w8a8_fold_norm_weight (offline)
+ *                                                       + w8a8_rmsnorm_quant_rows
  *   4. INT8 x INT8 -> INT32 product                    w8a8_gemm_i32 (diagnostic)
  *   5. dequantize with per-token x per-channel scales  w8a8_gemm_dequant (fuses 4+5)
  *   runtime forward = 3 + 4 + 5                         w8a8_linear
@@ -133,6 +135,48 @@ w8a8_status_t w8a8_smooth_factors(const float* amax_x, const float* amax_w, int6
 w8a8_status_t w8a8_scale_quant_rows(const void* x, int dtype, int64_t rows, int64_t cols,
                                     const float* col_scale, int8_t* q, float* row_scale,
                                     hipStream_t stream);
+
+/*
+ * Offline half of folding step 3 into the RMS normalisation that produces X
+ * (LLaMA-family decoders normalise the hidden state h before each projection:
+ * X = h / rms(h) * gamma).  Page section "平滑化変換の数学": X~ = X s^-1 is a
+ * per-channel factor, so it folds into the norm's per-channel weight (the fold
+ * is an extension beyond the page): g_j = gamma_j * inv_s_j, one fp32
+ * rounding, computed once per layer like the weight fold.
+ *
+ *   gamma, inv_s  [K] fp32; g [K] fp32 output; it may be the same array as
+ *                 either input (each element is read before it is written).
+ *   K >= 0.
+ * Errors: NULL, SHAPE, ALIGN (4-byte), HIP.
+ */
+w8a8_status_t w8a8_fold_norm_weight(const float* gamma, const float* inv_s, int64_t K, float* g,
+                                    hipStream_t stream);
+
+/*
+ * Runtime half: RMS normalisation with the folded weight g, smoothing and
+ * per-token INT8 in one pass over h.  The per-token quantizer is unchanged by
+ * a positive factor common to a row, so 1 / rms only enters the row scale.
+ * For each row t (fp32, each step one rounding):
+ *   v_j = fp32(h[t, j]) * g[j];  m = max_j |v_j|;  r = 127 / m
+ *   q[t, j] = round_half_even(v_j * r)
+ *   ms = (sum_j h[t, j]^2) / cols   (fp32 sum, order unspecified)
+ *   row_scale[t] = (m / 127) * (1 / sqrt(ms + eps))      (0 when m == 0)
+ * so that q[t, j] * row_scale[t] approximates (h / rms(h) * gamma)[t, j] * inv_s[j].
+ * The codes equal those of w8a8_scale_quant_rows(h, g) bit for bit;
+ * row_scale is within (cols / 2 + 6) * 2^-24 relative of its value with an
+ * exact sum of squares.  Traffic: that of w8a8_scale_quant_rows; the
+ * normalised activations are never written.
+ *
+ *   h          [rows x cols] fp16/bf16 (dtype), 16-byte aligned: the norm's input.
+ *   g          [cols] fp32 folded norm weight (w8a8_fold_norm_weight), 16-byte aligned.
+ *   eps        finite, >= 0.
+ *   q, row_scale  outputs as in w8a8_scale_quant_rows.
+ *   rows >= 0, cols % 16 == 0, cols <= 65536, cols >= 16 when rows > 0.
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, ARG (eps negative, NaN or infinite), HIP.
+ */
+w8a8_status_t w8a8_rmsnorm_quant_rows(const void* h, int dtype, int64_t rows, int64_t cols,
+                                      const float* g, float eps, int8_t* q, float* row_scale,
+                                      hipStream_t stream);
 
 /*
  * Step 4 alone (a diagnostic / test entry point): C = qa qb^T in exact int32.

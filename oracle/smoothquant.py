@@ -379,19 +379,23 @@ def rmsnorm_fp64(x, dtype: str, gamma, eps: float) -> np.ndarray:
     return widen(x, dtype).astype(np.float64) * r[:, None] * np.asarray(gamma, np.float64)[None, :]
 
 
-def rmsnorm_smooth_quant_rows(x, dtype: str, gamma, inv_s, eps: float):
-    """Per-token INT8 of RMSNorm(x; gamma) * inv_s with the smoothing folded in.
+def fold_norm_weight(gamma, inv_s) -> np.ndarray:
+    """g_j = RN32(gamma_j * inv_s_j): the smoothing's X s^-1 folded into the
+    per-channel weight of the norm that produces X."""
+    return (np.asarray(gamma, np.float32) * np.asarray(inv_s, np.float32)).astype(np.float32)
 
-    g_j = RN32(gamma_j * inv_s_j) is the folded norm weight; the codes and
-    m / 127 are those of scale_quant_rows(x, g); the row scale is
-    delta_t = RN32(m_t / 127) * r_t, returned in fp64 (the reference the
+
+def rmsnorm_smooth_quant_rows(x, dtype: str, g, eps: float):
+    """Per-token INT8 of RMSNorm(x; gamma) * inv_s, given the folded g.
+
+    The codes and m / 127 are those of scale_quant_rows(x, g); the row scale
+    is delta_t = RN32(m_t / 127) * r_t, returned in fp64 (the reference the
     device's fp32 evaluation is held to).  A zero row has delta 0.
     Returns (q int8[rows, cols], delta float64[rows]).
     Pinned by test_rmsnorm_quant_* (against the plain fp64 definition within
     the quantization bound, closed forms, scale invariance).
     """
-    g = (np.asarray(gamma, np.float32) * np.asarray(inv_s, np.float32)).astype(np.float32)
-    q, d = scale_quant_rows(x, dtype, g)
+    q, d = scale_quant_rows(x, dtype, np.asarray(g, np.float32))
     r = rms_inv(x, dtype, eps)
     delta = np.zeros(len(d), dtype=np.float64)
     nz = d > 0

@@ -36,7 +36,7 @@ def declared_symbols():
 def test_library_loads_and_exports_header_symbols():
     lib = _lib.load()
     syms = declared_symbols()
-    assert len(syms) == 12
+    assert len(syms) == 14
     for s in syms:
         assert hasattr(lib, s), s
         assert s in _lib.PROTOTYPES, s
@@ -170,3 +170,23 @@ def test_e4m3_entry_points_reject():
     assert d(PODD, P, P, P, P, 0, 4, 8, 16, 0) == EALIGN
     assert d(P, P, P, PODD, P, 0, 4, 8, 16, 0) == EALIGN
     assert d(0, 0, P, P, 0, 0, 0, 8, 16, 0) == OK  # no tokens: no launch
+
+
+@cpu_only
+def test_rmsnorm_quant_rows_rejects():
+    lib = _lib.load()
+    f = lib.w8a8_rmsnorm_quant_rows
+    assert f(P, 0, 4, 16, 0, 1e-5, P, P, 0) == ENULL  # g
+    assert f(P, 3, 4, 16, P, 1e-5, P, P, 0) == EDTYPE
+    assert f(P, 0, 4, 24, P, 1e-5, P, P, 0) == ESHAPE
+    assert f(P, 0, 4, 0, P, 1e-5, P, P, 0) == ESHAPE  # empty rows have no mean
+    assert f(P, 0, 4, 16, PODD, 1e-5, P, P, 0) == EALIGN
+    assert f(P, 0, 4, 16, P, -1e-5, P, P, 0) == EARG
+    assert f(P, 0, 4, 16, P, float("nan"), P, P, 0) == EARG
+    assert f(P, 0, 4, 16, P, float("inf"), P, P, 0) == EARG
+    assert f(0, 0, 0, 16, P, 1e-5, 0, 0, 0) == OK  # no rows: no launch
+    fold = lib.w8a8_fold_norm_weight
+    assert fold(P, 0, 8, P, 0) == ENULL
+    assert fold(P, P, -1, P, 0) == ESHAPE
+    assert fold(P, P, 8, P + 2, 0) == EALIGN
+    assert fold(0, 0, 0, 0, 0) == OK

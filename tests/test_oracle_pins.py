@@ -522,7 +522,7 @@ def test_rmsnorm_quant_matches_plain_definition():
     roundings of the fold and the scaling."""
     x, gamma, inv_s = _rms_case(24, 96, 7)
     for eps in (0.0, 1e-5, 3.0):
-        q, delta = oracle.rmsnorm_smooth_quant_rows(x, "f16", gamma, inv_s, eps)
+        q, delta = oracle.rmsnorm_smooth_quant_rows(x, "f16", oracle.fold_norm_weight(gamma, inv_s), eps)
         plain = oracle.rmsnorm_fp64(x, "f16", gamma, eps) * inv_s.astype(np.float64)[None, :]
         deq = q.astype(np.float64) * delta[:, None]
         tol = delta[:, None] / 2 * (1 + 2.0 ** -13) + np.abs(plain) * 2.0 ** -22
@@ -533,9 +533,10 @@ def test_rmsnorm_quant_matches_plain_definition():
 def test_rmsnorm_quant_scale_invariance_and_zero_row():
     x, gamma, inv_s = _rms_case(10, 64, 9)
     x[3] = 0
-    q1, d1 = oracle.rmsnorm_smooth_quant_rows(x, "f16", gamma, inv_s, 0.0)
+    g = oracle.fold_norm_weight(gamma, inv_s)
+    q1, d1 = oracle.rmsnorm_smooth_quant_rows(x, "f16", g, 0.0)
     x2 = (x.astype(np.float32) * 4).astype(np.float16)  # exact: a power of two, no overflow
-    q2, d2 = oracle.rmsnorm_smooth_quant_rows(x2, "f16", gamma, inv_s, 0.0)
+    q2, d2 = oracle.rmsnorm_smooth_quant_rows(x2, "f16", g, 0.0)
     assert np.array_equal(q1, q2) and np.array_equal(d1, d2)
     assert not q1[3].any() and d1[3] == 0.0
     # the codes are those of the smoothing quantizer with the folded weight

@@ -19,6 +19,9 @@ PROTOTYPES = {
     "w8a8_channel_amax": (c_int, [c_vp, c_int, c_i64, c_i64, c_vp, c_vp]),
     "w8a8_smooth_factors": (c_int, [c_vp, c_vp, c_i64, ctypes.c_double, c_vp, c_vp, c_vp]),
     "w8a8_scale_quant_rows": (c_int, [c_vp, c_int, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp]),
+    "w8a8_fold_norm_weight": (c_int, [c_vp, c_vp, c_i64, c_vp, c_vp]),
+    "w8a8_rmsnorm_quant_rows": (c_int, [c_vp, c_int, c_i64, c_i64, c_vp, ctypes.c_float, c_vp, c_vp,
+                                        c_vp]),
     "w8a8_gemm_i32": (c_int, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_vp]),
     "w8a8_gemm_dequant": (c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_vp]),
     "w8a8_scale_quant_rows_e4m3": (c_int, [c_vp, c_int, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp]),

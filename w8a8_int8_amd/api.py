@@ -103,6 +103,46 @@ def scale_quant_rows(x: torch.Tensor, col_scale: torch.Tensor,
     return q, row_scale
 
 
+def fold_norm_weight(gamma: torch.Tensor, inv_s: torch.Tensor,
+                     g: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """g = gamma * inv_s (fp32): the smoothing folded into an RMS norm's weight."""
+    _dev(gamma, inv_s)
+    K = gamma.shape[0]
+    _need(gamma, torch.float32, (K,))
+    _need(inv_s, torch.float32, (K,))
+    g = torch.empty(K, dtype=torch.float32, device=gamma.device) if g is None else g
+    _dev(g)
+    _need(g, torch.float32, (K,))
+    lib = _lib.load()
+    _lib.check("w8a8_fold_norm_weight", lib.w8a8_fold_norm_weight(
+        _ptr(gamma), _ptr(inv_s), K, _ptr(g), _stream()))
+    return g
+
+
+def rmsnorm_quant_rows(h: torch.Tensor, g: torch.Tensor, eps: float,
+                       q: Optional[torch.Tensor] = None,
+                       row_scale: Optional[torch.Tensor] = None):
+    """Per-token INT8 of RMSNorm(h) with the folded weight g = gamma * inv_s.
+
+    Returns (q int8 rows x cols, row_scale fp32[rows]); q * row_scale[:, None]
+    approximates h / rms(h) * gamma * inv_s.
+    """
+    _dev(h, g)
+    rows, cols = h.shape
+    _need(g, torch.float32, (cols,))
+    q = torch.empty((rows, cols), dtype=torch.int8, device=h.device) if q is None else q
+    row_scale = (torch.empty(rows, dtype=torch.float32, device=h.device)
+                 if row_scale is None else row_scale)
+    _dev(q, row_scale)
+    _need(q, torch.int8, (rows, cols))
+    _need(row_scale, torch.float32, (rows,))
+    lib = _lib.load()
+    _lib.check("w8a8_rmsnorm_quant_rows", lib.w8a8_rmsnorm_quant_rows(
+        _ptr(h), _dtype_code(h), rows, cols, _ptr(g), float(eps), _ptr(q), _ptr(row_scale),
+        _stream()))
+    return q, row_scale
+
+
 def gemm_i32(qa: torch.Tensor, qb: torch.Tensor, c: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Exact int32 C = qa @ qb.T for qa (M x K) and qb (N x K) int8."""
     _dev(qa, qb)

@@ -92,7 +92,7 @@ w8a8_status_t w8a8_scale_quant_rows(const void* x, int dtype, int64_t rows, int6
   const w8a8_status_t st = check_quant(x, dtype, rows, cols, col_scale, q, row_scale);
   if (st != W8A8_OK) return st;
   return hip_status(w8a8::launch_scale_quant_rows(x, dtype == W8A8_BF16, rows, cols, col_scale,
-                                                  q, row_scale, 0, stream));
+                                                  false, 0.0f, q, row_scale, 0, stream));
 }
 
 w8a8_status_t w8a8_scale_quant_rows_e4m3(const void* x, int dtype, int64_t rows, int64_t cols,
@@ -101,7 +101,26 @@ w8a8_status_t w8a8_scale_quant_rows_e4m3(const void* x, int dtype, int64_t rows,
   const w8a8_status_t st = check_quant(x, dtype, rows, cols, col_scale, (const int8_t*)q, row_scale);
   if (st != W8A8_OK) return st;
   return hip_status(w8a8::launch_scale_quant_rows(x, dtype == W8A8_BF16, rows, cols, col_scale,
-                                                  q, row_scale, 1, stream));
+                                                  false, 0.0f, q, row_scale, 1, stream));
+}
+
+w8a8_status_t w8a8_fold_norm_weight(const float* gamma, const float* inv_s, int64_t K, float* g,
+                                    hipStream_t stream) {
+  if (K < 0 || K >= kMaxRows) return W8A8_ERR_SHAPE;
+  if (K && (!gamma || !inv_s || !g)) return W8A8_ERR_NULL;
+  if (!aligned(gamma, 4) || !aligned(inv_s, 4) || !aligned(g, 4)) return W8A8_ERR_ALIGN;
+  return hip_status(w8a8::launch_fold(gamma, inv_s, K, g, stream));
+}
+
+w8a8_status_t w8a8_rmsnorm_quant_rows(const void* h, int dtype, int64_t rows, int64_t cols,
+                                      const float* g, float eps, int8_t* q, float* row_scale,
+                                      hipStream_t stream) {
+  const w8a8_status_t st = check_quant(h, dtype, rows, cols, g, q, row_scale);
+  if (st != W8A8_OK) return st;
+  if (!(eps >= 0.0f && eps <= 3.0e38f)) return W8A8_ERR_ARG;  // also rejects NaN and +inf
+  if (cols == 0 && rows) return W8A8_ERR_SHAPE;                // the mean of an empty row
+  return hip_status(w8a8::launch_scale_quant_rows(h, dtype == W8A8_BF16, rows, cols, g, true, eps,
+                                                  q, row_scale, 0, stream));
 }
 
 w8a8_status_t w8a8_gemm_i32(const int8_t* qa, const int8_t* qb, int32_t* c, int64_t M, int64_t N,
@@ -167,7 +186,8 @@ w8a8_status_t w8a8_linear(const void* x, int dtype, const float* inv_s, const in
   st = check_gemm(qx, qw, y, M, N, K);
   if (st != W8A8_OK) return st;
   if (!aligned(sw, 16)) return W8A8_ERR_ALIGN;
-  hipError_t e = w8a8::launch_scale_quant_rows(x, dtype == W8A8_BF16, M, K, inv_s, qx, sx, 0, stream);
+  hipError_t e = w8a8::launch_scale_quant_rows(x, dtype == W8A8_BF16, M, K, inv_s, false, 0.0f, qx,
+                                               sx, 0, stream);
   if (e != hipSuccess) return W8A8_ERR_HIP;
   return hip_status(w8a8::launch_gemm(qx, qw, M, N, K, sx, sw, y, dtype == W8A8_BF16 ? 2 : 1,
                                       stream));

@@ -18,10 +18,13 @@ hipError_t launch_channel_amax(const void* x, bool bf16, int64_t rows, int64_t c
                                hipStream_t st);
 hipError_t launch_smooth_factors(const float* ax, const float* aw, int64_t K, double alpha,
                                  float* s, float* inv_s, hipStream_t st);
-// fmt: 0 = symmetric INT8 codes, 1 = FP8 E4M3 codes
+// fmt: 0 = symmetric INT8 codes, 1 = FP8 E4M3 codes.  norm (INT8 only): the
+// rows are RMS-norm inputs and col_scale the folded norm weight; the row scale
+// is divided by the row's rms (with eps).
 hipError_t launch_scale_quant_rows(const void* x, bool bf16, int64_t rows, int64_t cols,
-                                   const float* col_scale, void* q, float* row_scale, int fmt,
-                                   hipStream_t st);
+                                   const float* col_scale, bool norm, float eps, void* q,
+                                   float* row_scale, int fmt, hipStream_t st);
+hipError_t launch_fold(const float* a, const float* b, int64_t n, float* out, hipStream_t st);
 // out_mode: 0 = int32 accumulators, 1 = fp16 dequant, 2 = bf16 dequant (int8
 // operands, K in bytes); 3 = fp16, 4 = bf16 dense product (16-bit operands,
 // K in elements, fp32 accumulation); 5 = fp16, 6 = bf16 dequant of FP8 E4M3

@@ -79,11 +79,24 @@ __device__ __forceinline__ unsigned pack_e4m3(float a, float b, float c, float d
   return (unsigned)w;
 }
 
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
 // FMT 0: symmetric INT8 codes (grid max 127); FMT 1: FP8 E4M3 codes (max 448).
-template <int CPT, int R, bool BF16, int FMT>
+// NORM: the row is the input of an RMS norm whose weight carries the
+// smoothing (col_scale = the folded RN32(gamma_j * inv_s_j)); the row scale
+// is RN32(m / 127) times 1 / sqrt(RN32(sum_j x_j^2 / cols) + eps).  The
+// per-token quantizer does not change under a positive factor common to the
+// row, so the norm's factor only enters the scale; the codes are those of
+// x * g.
+template <int CPT, int R, bool BF16, int FMT, bool NORM>
 __global__ __launch_bounds__(1024) void k_scale_quant_rows(const v4u* __restrict__ x, int64_t rows,
                                                            int cols8,
                                                            const float4* __restrict__ col_scale,
+                                                           float eps,
                                                            uint2* __restrict__ q,
                                                            float* __restrict__ row_scale) {
   const int tid = threadIdx.x;
@@ -120,24 +133,33 @@ __global__ __launch_bounds__(1024) void k_scale_quant_rows(const v4u* __restrict
 
   // pass 1: v = x * c (kept in registers) and the row max of |v|
   float v[R][CPT][8];
-  float m[R];
+  float m[R], ss[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    float mr = 0.0f;
+    float mr = 0.0f, sr = 0.0f;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        v[r][i][e] = elem<BF16>(xv[r][i], e) * sc[i][e];
+        const float xe = elem<BF16>(xv[r][i], e);
+        v[r][i][e] = xe * sc[i][e];
         mr = fmaxf(mr, fabsf(v[r][i][e]));
+        // the square of a 16-bit value is exact in fp32, so the fused form
+        // rounds once, like the separate multiply and add would
+        if (NORM) sr = __builtin_fmaf(xe, xe, sr);
       }
     }
     m[r] = wave_max(mr);
+    ss[r] = NORM ? wave_sum(sr) : 0.0f;
   }
   __shared__ float red[R][16];
+  __shared__ float red2[R][16];
   if (lane == 0) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) red[r][wave] = m[r];
+    for (int r = 0; r < R; ++r) {
+      red[r][wave] = m[r];
+      if (NORM) red2[r][wave] = ss[r];
+    }
   }
   __syncthreads();
 #pragma unroll
@@ -145,6 +167,11 @@ __global__ __launch_bounds__(1024) void k_scale_quant_rows(const v4u* __restrict
     float mr = red[r][0];
     for (int w = 1; w < nwaves; ++w) mr = fmaxf(mr, red[r][w]);
     m[r] = mr;
+    if (NORM) {
+      float sr = red2[r][0];
+      for (int w = 1; w < nwaves; ++w) sr += red2[r][w];
+      ss[r] = sr;
+    }
   }
 
   // pass 2: codes = round_half_even(v * (127 / m)); m == 0 gives r = 0 and
@@ -157,7 +184,14 @@ __global__ __launch_bounds__(1024) void k_scale_quant_rows(const v4u* __restrict
     const float mr = m[r];
     constexpr float kGridMax = FMT == 0 ? 127.0f : 448.0f;
     const float rcp = mr > 0.0f ? kGridMax / mr : 0.0f;
-    if (tid == 0) row_scale[row] = mr > 0.0f ? mr / kGridMax : 0.0f;
+    if (tid == 0) {
+      float d = mr > 0.0f ? mr / kGridMax : 0.0f;
+      if (NORM && mr > 0.0f) {
+        const float ms = ss[r] / (float)(cols8 * 8);
+        d = d * (1.0f / sqrtf(ms + eps));
+      }
+      row_scale[row] = d;
+    }
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = i * G + tid;
@@ -181,27 +215,27 @@ __global__ __launch_bounds__(1024) void k_scale_quant_rows(const v4u* __restrict
   }
 }
 
+template <int CPT, int R, bool BF16, int FMT, bool NORM>
+void launch_one(const void* x, int64_t rows, int cols8, int G, const float* cs, float eps, void* q,
+                float* row_scale, hipStream_t st) {
+  const unsigned blocks = (unsigned)((rows + R - 1) / R);
+  hipLaunchKernelGGL((k_scale_quant_rows<CPT, R, BF16, FMT, NORM>), dim3(blocks), dim3(G), 0, st,
+                     (const v4u*)x, rows, cols8, (const float4*)cs, eps, (uint2*)q, row_scale);
+}
+
 template <int CPT, int R>
 hipError_t launch_cfg(const void* x, bool bf16, int fmt, int64_t rows, int cols8, int G,
-                      const float* col_scale, void* q, float* row_scale, hipStream_t st) {
-  const unsigned blocks = (unsigned)((rows + R - 1) / R);
-  const v4u* xv = (const v4u*)x;
-  const float4* cs = (const float4*)col_scale;
-  uint2* qv = (uint2*)q;
-  if (fmt == 0) {
-    if (bf16)
-      hipLaunchKernelGGL((k_scale_quant_rows<CPT, R, true, 0>), dim3(blocks), dim3(G), 0, st, xv,
-                         rows, cols8, cs, qv, row_scale);
-    else
-      hipLaunchKernelGGL((k_scale_quant_rows<CPT, R, false, 0>), dim3(blocks), dim3(G), 0, st, xv,
-                         rows, cols8, cs, qv, row_scale);
+                      const float* cs, bool norm, float eps, void* q, float* row_scale,
+                      hipStream_t st) {
+  if (norm) {  // RMS norm fold (INT8 only)
+    if (bf16) launch_one<CPT, R, true, 0, true>(x, rows, cols8, G, cs, eps, q, row_scale, st);
+    else launch_one<CPT, R, false, 0, true>(x, rows, cols8, G, cs, eps, q, row_scale, st);
+  } else if (fmt == 0) {
+    if (bf16) launch_one<CPT, R, true, 0, false>(x, rows, cols8, G, cs, eps, q, row_scale, st);
+    else launch_one<CPT, R, false, 0, false>(x, rows, cols8, G, cs, eps, q, row_scale, st);
   } else {
-    if (bf16)
-      hipLaunchKernelGGL((k_scale_quant_rows<CPT, R, true, 1>), dim3(blocks), dim3(G), 0, st, xv,
-                         rows, cols8, cs, qv, row_scale);
-    else
-      hipLaunchKernelGGL((k_scale_quant_rows<CPT, R, false, 1>), dim3(blocks), dim3(G), 0, st, xv,
-                         rows, cols8, cs, qv, row_scale);
+    if (bf16) launch_one<CPT, R, true, 1, false>(x, rows, cols8, G, cs, eps, q, row_scale, st);
+    else launch_one<CPT, R, false, 1, false>(x, rows, cols8, G, cs, eps, q, row_scale, st);
   }
   return hipGetLastError();
 }
@@ -209,8 +243,8 @@ hipError_t launch_cfg(const void* x, bool bf16, int fmt, int64_t rows, int cols8
 }  // namespace
 
 hipError_t launch_scale_quant_rows(const void* x, bool bf16, int64_t rows, int64_t cols,
-                                   const float* col_scale, void* q, float* row_scale, int fmt,
-                                   hipStream_t st) {
+                                   const float* col_scale, bool norm, float eps, void* q,
+                                   float* row_scale, int fmt, hipStream_t st) {
   if (rows == 0) return hipSuccess;
   const int cols8 = (int)(cols / 8);
   // Threads per row: two 16-byte chunks each (more for rows past 2048 chunks,
@@ -224,14 +258,22 @@ hipError_t launch_scale_quant_rows(const void* x, bool bf16, int64_t rows, int64
   if (G > 1024) G = 1024;
   const int cpt = (cols8 + G - 1) / G;
   switch (cpt <= 1 ? 1 : cpt) {
-    case 1: return launch_cfg<1, 4>(x, bf16, fmt, rows, cols8, G, col_scale, q, row_scale, st);
-    case 2: return launch_cfg<2, 2>(x, bf16, fmt, rows, cols8, G, col_scale, q, row_scale, st);
-    case 3: return launch_cfg<3, 1>(x, bf16, fmt, rows, cols8, G, col_scale, q, row_scale, st);
-    case 4: return launch_cfg<4, 1>(x, bf16, fmt, rows, cols8, G, col_scale, q, row_scale, st);
-    case 5: return launch_cfg<5, 1>(x, bf16, fmt, rows, cols8, G, col_scale, q, row_scale, st);
-    case 6: return launch_cfg<6, 1>(x, bf16, fmt, rows, cols8, G, col_scale, q, row_scale, st);
-    case 7: return launch_cfg<7, 1>(x, bf16, fmt, rows, cols8, G, col_scale, q, row_scale, st);
-    case 8: return launch_cfg<8, 1>(x, bf16, fmt, rows, cols8, G, col_scale, q, row_scale, st);
+    case 1: return launch_cfg<1, 4>(x, bf16, fmt, rows, cols8, G, col_scale, norm, eps, q,
+                                          row_scale, st);
+    case 2: return launch_cfg<2, 2>(x, bf16, fmt, rows, cols8, G, col_scale, norm, eps, q,
+                                          row_scale, st);
+    case 3: return launch_cfg<3, 1>(x, bf16, fmt, rows, cols8, G, col_scale, norm, eps, q,
+                                          row_scale, st);
+    case 4: return launch_cfg<4, 1>(x, bf16, fmt, rows, cols8, G, col_scale, norm, eps, q,
+                                          row_scale, st);
+    case 5: return launch_cfg<5, 1>(x, bf16, fmt, rows, cols8, G, col_scale, norm, eps, q,
+                                          row_scale, st);
+    case 6: return launch_cfg<6, 1>(x, bf16, fmt, rows, cols8, G, col_scale, norm, eps, q,
+                                          row_scale, st);
+    case 7: return launch_cfg<7, 1>(x, bf16, fmt, rows, cols8, G, col_scale, norm, eps, q,
+                                          row_scale, st);
+    case 8: return launch_cfg<8, 1>(x, bf16, fmt, rows, cols8, G, col_scale, norm, eps, q,
+                                          row_scale, st);
     default: return hipErrorInvalidValue;
   }
 }

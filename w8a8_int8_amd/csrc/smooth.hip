@@ -35,7 +35,22 @@ __global__ __launch_bounds__(256) void k_smooth_factors(const float* __restrict_
   inv_s[j] = 1.0f / sj;
 }
 
+// out_j = a_j * b_j, one fp32 rounding: the folded weight of a per-channel
+// scale (the smoothing's inv_s) and the per-channel weight it folds into.
+__global__ __launch_bounds__(256) void k_fold(const float* __restrict__ a,
+                                              const float* __restrict__ b, int64_t n,
+                                              float* __restrict__ out) {
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j < n) out[j] = a[j] * b[j];
+}
+
 }  // namespace
+
+hipError_t launch_fold(const float* a, const float* b, int64_t n, float* out, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fold, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a, b, n, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_smooth_factors(const float* ax, const float* aw, int64_t K, double alpha,
                                  float* s, float* inv_s, hipStream_t st) {
