@@ -207,17 +207,22 @@ def kernel_breakdown(layers, reps):
 
 def decode_sweep(wl, layers, reps):
     """Every token count of a few-token workload through each layer: the
-    runtime forward (smooth + quant, then the GEMM), and the GEMM alone against
-    the HBM roofline (it streams the INT8 weight once)."""
+    runtime forward (smooth + quant, then the split-K GEMM) and the unsplit
+    GEMM kernel alone, against the HBM roofline (both stream the INT8 weight
+    once).  The calls rotate over copies of the weight totalling >= 512 MB, so
+    that the 256 MB last-level cache cannot serve it, and run from a captured
+    HIP graph, so that host-side launch cost does not enter."""
     import torch
 
     w8 = layers[0].w8
     out = {}
     for L in layers:
+        copies = max(2, min(16, -(-(512 << 20) // (L.N * L.K))))
+        qws = [L.qw] + [L.qw.clone() for _ in range(copies - 1)]
         for M in wl.M:
             x = L.x_all[:M]
             y = torch.empty((M, L.N), dtype=L.x.dtype, device=L.x.device)
-            ws = torch.empty(max(w8.linear_workspace_bytes(M, L.K), 1), dtype=torch.uint8,
+            ws = torch.empty(max(w8.linear_workspace_bytes(M, L.N, L.K), 1), dtype=torch.uint8,
                              device=L.x.device)
             qx = ws[:M * L.K].view(torch.int8).view(M, L.K)
             off = (M * L.K + 255) // 256 * 256
@@ -225,25 +230,35 @@ def decode_sweep(wl, layers, reps):
             w8.linear(x, L.inv_s, L.qw, L.sw, y, ws)
 
             def run(fn, n=reps):
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                fn()
+                # few-token kernels are shorter than a Python-side launch: time
+                # n calls captured in one HIP graph, replayed twice
+                fn(0)
                 torch.cuda.synchronize()
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph):
+                    for i in range(n):
+                        fn(i)
+                graph.replay()
+                torch.cuda.synchronize()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record()
-                for _ in range(n):
-                    fn()
+                graph.replay()
                 b.record()
                 b.synchronize()
                 return a.elapsed_time(b) / n * 1e-3
 
-            t_lin = run(lambda: w8.linear(x, L.inv_s, L.qw, L.sw, y, ws))
-            t_g = run(lambda: w8.gemm_dequant(qx, sx, L.qw, L.sw, L.x.dtype, y))
+            t_lin = run(lambda i: w8.linear(x, L.inv_s, qws[i % copies], L.sw, y, ws))
+            t_q = run(lambda i: w8.scale_quant_rows(x, L.inv_s, qx, sx))
+            t_g = run(lambda i: w8.gemm_dequant(qx, sx, qws[i % copies], L.sw, L.x.dtype, y))
             by = L.gemm_bytes(M)
             out[f"{L.name}_{L.K}x{L.N}_M{M}"] = {
                 "linear_us": round(t_lin * 1e6, 3),
-                "gemm_us": round(t_g * 1e6, 3),
-                "gemm_GBs": round(by / t_g / 1e9, 1),
-                "gemm_frac_hbm": round(by / t_g / 1e9 / PEAK_HBM_GBS, 4),
+                "act_quant_us": round(t_q * 1e6, 3),
+                "linear_gemm_GBs": round(by / (t_lin - t_q) / 1e9, 1) if t_lin > t_q else None,
+                "unsplit_gemm_us": round(t_g * 1e6, 3),
+                "unsplit_gemm_GBs": round(by / t_g / 1e9, 1),
             }
+        del qws
     return out
 
 

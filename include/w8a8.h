@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define W8A8_ABI_VERSION 1
+#define W8A8_ABI_VERSION 2
 
 /* Largest K for which 127 * 127 * K fits int32, so that every accumulator
  * (and every partial sum) of the INT8 product is exact in int32. */
@@ -267,20 +267,26 @@ w8a8_status_t w8a8_gemm_dequant_e4m3(const uint8_t* qa, const float* sa, const u
                                      const float* sb, void* y, int out_dtype, int64_t M, int64_t N,
                                      int64_t K, hipStream_t stream);
 
-/* Bytes of workspace w8a8_linear needs for M tokens of K channels
- * (the INT8 activations and their per-token scales, each 256-byte aligned). */
-size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K);
+/* Bytes of workspace w8a8_linear needs for M tokens, K input and N output
+ * channels: the INT8 activations and their per-token scales, then, for
+ * 17 <= M <= 32 when the product is split along K, the int32 partial sums
+ * (S x M x N); each part 256-byte aligned.  0 for negative sizes. */
+size_t w8a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
  * Runtime forward of one smoothed W8A8 linear layer (steps 3 + 4 + 5):
  * (qX, sx) = scale_quant_rows(x, inv_s) into the workspace, then
- * y = gemm_dequant(qX, sx, qw, sw).  Two launches on `stream`, no host sync.
+ * y = gemm_dequant(qX, sx, qw, sw).  No host sync.  For 17 <= M <= 32
+ * (decode batches) the product may be split along K over more blocks: each
+ * block adds its int32 partial sums exactly, a second kernel adds the S slices
+ * (integer addition, exact) and applies the same epilogue, so y is
+ * bit-identical to gemm_dequant's.
  *
  *   x          [M x K] fp16/bf16 activations (dtype; y has the same dtype).
  *   inv_s      [K] fp32 reciprocal smoothing factors, 16-byte aligned.
  *   qw, sw     [N x K] int8 folded weight codes and [N] fp32 scales (16-byte aligned).
  *   y          [M x N] output.
- *   workspace  device buffer of ws_bytes >= w8a8_linear_workspace_bytes(M, K),
+ *   workspace  device buffer of ws_bytes >= w8a8_linear_workspace_bytes(M, N, K),
  *              256-byte aligned; its contents on return are the INT8
  *              activations (M x K) followed by their scales.
  *   Shape rules: those of both steps (K % 16 == 0, K <= 65536, N % 8 == 0).

@@ -40,7 +40,7 @@ def test_library_loads_and_exports_header_symbols():
     for s in syms:
         assert hasattr(lib, s), s
         assert s in _lib.PROTOTYPES, s
-    assert lib.w8a8_abi_version() == 1
+    assert lib.w8a8_abi_version() == 2
 
 
 def test_status_strings():
@@ -53,10 +53,14 @@ def test_status_strings():
 
 def test_workspace_bytes():
     lib = _lib.load()
-    assert lib.w8a8_linear_workspace_bytes(0, 0) == 0
-    assert lib.w8a8_linear_workspace_bytes(1, 16) == 256 + 256
-    assert lib.w8a8_linear_workspace_bytes(2048, 4096) == 2048 * 4096 + 2048 * 4
-    assert lib.w8a8_linear_workspace_bytes(-1, 16) == 0
+    assert lib.w8a8_linear_workspace_bytes(0, 0, 0) == 0
+    assert lib.w8a8_linear_workspace_bytes(1, 8, 16) == 256 + 256  # one split: no partials
+    assert lib.w8a8_linear_workspace_bytes(2048, 4096, 4096) == 2048 * 4096 + 2048 * 4
+    assert lib.w8a8_linear_workspace_bytes(-1, 8, 16) == 0
+    # 32 tokens: 4096 outputs are 64 blocks of 64 channels, so K = 16384 splits four ways
+    assert lib.w8a8_linear_workspace_bytes(32, 4096, 16384) == 32 * 16384 + 256 + 4 * 32 * 4096 * 4
+    assert lib.w8a8_linear_workspace_bytes(32, 16384, 4096) == 32 * 4096 + 256  # 256 blocks: no split
+    assert lib.w8a8_linear_workspace_bytes(16, 4096, 16384) == 16 * 16384 + 256  # unsplit kernel
 
 
 @cpu_only
@@ -125,7 +129,7 @@ def test_gemm_rejects():
 @cpu_only
 def test_linear_rejects():
     lin = _lib.load().w8a8_linear
-    need = _lib.load().w8a8_linear_workspace_bytes(4, 16)
+    need = _lib.load().w8a8_linear_workspace_bytes(4, 8, 16)
     assert lin(P, 0, P, P, P, P, 4, 8, 16, 0, need, 0) == ENULL
     assert lin(P, 5, P, P, P, P, 4, 8, 16, P, need, 0) == EDTYPE
     assert lin(P, 0, P, P, P, P, 4, 8, 16, P, need - 1, 0) == EARG

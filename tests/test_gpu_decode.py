@@ -1,0 +1,97 @@
+"""GPU parity of the runtime forward at few tokens (M <= 32): the skinny
+kernel up to 16 tokens, and from 17 to 32 the INT8 product split along K into
+int32 partial slices that a second kernel sums exactly.  Integer accumulation
+is order free, so the output must equal the oracle's bit for bit, and equal
+the unsplit gemm_dequant path's.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import w8a8_int8_amd as w8
+from w8a8_int8_amd import _lib, synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+_LAYERS = {}
+
+
+def layer(N, K, dtype, seed):
+    key = (N, K, dtype, seed)
+    if key not in _LAYERS:
+        _LAYERS.clear()  # keep one layer's weights resident at a time
+        _LAYERS[key] = _make_layer(N, K, dtype, seed)
+    return _LAYERS[key]
+
+
+def _make_layer(N, K, dtype, seed):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    w = (torch.randn((N, K), generator=g) * 0.02).to(dtype).to(DEV)
+    xc = torch.randn((64, K), generator=g)
+    if K:
+        xc[:, torch.randperm(K, generator=g)[:4]] *= 60.0
+    xc = xc.to(dtype).to(DEV)
+    p = w8.prepare_weight(w, w8.channel_amax(xc), 0.5)
+    p["qw_host"] = host(p["qw"])
+    return p
+
+
+@pytest.mark.parametrize("M", [1, 5, 8, 16, 17, 31, 32])
+@pytest.mark.parametrize("N,K", [(4096, 16384), (16384, 4096), (12288, 4096), (136, 80),
+                                 (520, 1040), (264, 65536), (8, 16), (4104, 4112)])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_linear_decode_split_k(dtype, N, K, M):
+    p = layer(N, K, dtype, N + K)
+    g = torch.Generator(device="cpu").manual_seed(M * 7 + N)
+    x = torch.randn((M, K), generator=g)
+    x[:, :3] *= 50.0
+    x = x.to(dtype).to(DEV)
+    ws = torch.zeros(w8.linear_workspace_bytes(M, N, K), dtype=torch.uint8, device=DEV)
+    y = w8.linear(x, p["inv_s"], p["qw"], p["sw"], workspace=ws)
+    qx = ws[:M * K].view(torch.int8).view(M, K)
+    off = (M * K + 255) // 256 * 256
+    sx = ws[off:off + 4 * M].view(torch.float32)
+    # the unsplit kernel on the same codes gives the same bits
+    y2 = w8.gemm_dequant(qx, sx, p["qw"], p["sw"], dtype)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    name = "f16" if dtype == torch.float16 else "bf16"
+    qx_or, sx_or = oracle.scale_quant_rows(synth.to_numpy_bits(x), name, host(p["inv_s"]))
+    assert np.array_equal(host(qx), qx_or)
+    c = oracle.gemm_i32(qx_or, p["qw_host"])
+    y_or = oracle.dequant(c, sx_or, host(p["sw"]), name)
+    assert np.array_equal(synth.to_numpy_bits(y).view(np.uint16), y_or.view(np.uint16))
+
+
+def test_linear_decode_repeat_calls_bit_identical():
+    """The partial slices are overwritten on every call: a second call with
+    other activations, then the first again, reproduces the first output."""
+    N, K, M = 4096, 16384, 32
+    p = layer(N, K, torch.float16, 3)
+    g = torch.Generator(device="cpu").manual_seed(9)
+    xa = torch.randn((M, K), generator=g).half().to(DEV)
+    xb = (torch.randn((M, K), generator=g) * 3).half().to(DEV)
+    ws = torch.empty(w8.linear_workspace_bytes(M, N, K), dtype=torch.uint8, device=DEV)
+    ya = w8.linear(xa, p["inv_s"], p["qw"], p["sw"], workspace=ws).clone()
+    w8.linear(xb, p["inv_s"], p["qw"], p["sw"], workspace=ws)
+    ya2 = w8.linear(xa, p["inv_s"], p["qw"], p["sw"], workspace=ws)
+    assert torch.equal(ya.view(torch.int16), ya2.view(torch.int16))
+
+
+def test_linear_workspace_too_small_is_rejected():
+    N, K, M = 4096, 16384, 32
+    p = layer(N, K, torch.float16, 5)
+    x = torch.zeros((M, K), dtype=torch.float16, device=DEV)
+    need = w8.linear_workspace_bytes(M, N, K)
+    ws = torch.empty(need - 256, dtype=torch.uint8, device=DEV)
+    with pytest.raises(_lib.W8A8Error, match="status 5"):
+        w8.linear(x, p["inv_s"], p["qw"], p["sw"], workspace=ws)

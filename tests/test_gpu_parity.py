@@ -304,7 +304,7 @@ def test_workload_layer(name, li, alpha):
     ys = {}
     for M in wl.M:
         x = x_all[:M].contiguous()
-        ws = torch.empty(w8.linear_workspace_bytes(M, L.K), dtype=torch.uint8, device=DEV)
+        ws = torch.empty(w8.linear_workspace_bytes(M, L.N, L.K), dtype=torch.uint8, device=DEV)
         y = w8.linear(x, p["inv_s"], p["qw"], p["sw"], workspace=ws)
         qx = ws[:M * L.K].view(torch.int8).view(M, L.K)
         off = (M * L.K + 255) // 256 * 256

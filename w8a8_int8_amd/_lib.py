@@ -28,12 +28,12 @@ PROTOTYPES = {
     "w8a8_gemm_dequant_e4m3": (c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64,
                                        c_vp]),
     "w8a8_gemm_float": (c_int, [c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_vp]),
-    "w8a8_linear_workspace_bytes": (c_size, [c_i64, c_i64]),
+    "w8a8_linear_workspace_bytes": (c_size, [c_i64, c_i64, c_i64]),
     "w8a8_linear": (c_int, [c_vp, c_int, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_vp, c_size,
                             c_vp]),
 }
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 W8A8_F16, W8A8_BF16 = 0, 1
 
 _lib = None

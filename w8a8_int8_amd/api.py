@@ -233,8 +233,8 @@ def gemm_float(a: torch.Tensor, b: torch.Tensor, y: Optional[torch.Tensor] = Non
     return y
 
 
-def linear_workspace_bytes(M: int, K: int) -> int:
-    return int(_lib.load().w8a8_linear_workspace_bytes(M, K))
+def linear_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(_lib.load().w8a8_linear_workspace_bytes(M, N, K))
 
 
 def linear(x: torch.Tensor, inv_s: torch.Tensor, qw: torch.Tensor, sw: torch.Tensor,
@@ -250,7 +250,7 @@ def linear(x: torch.Tensor, inv_s: torch.Tensor, qw: torch.Tensor, sw: torch.Ten
     y = torch.empty((M, N), dtype=x.dtype, device=x.device) if y is None else y
     _dev(y)
     _need(y, x.dtype, (M, N))
-    need = linear_workspace_bytes(M, K)
+    need = linear_workspace_bytes(M, N, K)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     _dev(workspace)

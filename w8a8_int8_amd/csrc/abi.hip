@@ -166,9 +166,20 @@ w8a8_status_t w8a8_gemm_float(const void* a, const void* b, void* y, int dtype, 
                                       nullptr, y, dtype == W8A8_BF16 ? 4 : 3, stream));
 }
 
-size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K) {
-  if (M < 0 || K < 0) return 0;
-  return round_up((size_t)M * (size_t)K, kWsAlign) + round_up((size_t)M * 4, kWsAlign);
+// 17 to 32 tokens take the split-K path, whose int32 partial slices follow
+// the INT8 activations and their scales in the workspace.
+static bool linear_splitk(int64_t M, int64_t N, int64_t K) {
+  return w8a8::splitk_plan(M, N, K).steps_per_split > 0;
+}
+
+size_t w8a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0) return 0;
+  size_t b = round_up((size_t)M * (size_t)K, kWsAlign) + round_up((size_t)M * 4, kWsAlign);
+  if (linear_splitk(M, N, K)) {
+    const int s = w8a8::splitk_plan(M, N, K).splits;
+    if (s > 1) b += round_up((size_t)s * (size_t)M * (size_t)N * 4, kWsAlign);
+  }
+  return b;
 }
 
 w8a8_status_t w8a8_linear(const void* x, int dtype, const float* inv_s, const int8_t* qw,
@@ -178,9 +189,11 @@ w8a8_status_t w8a8_linear(const void* x, int dtype, const float* inv_s, const in
   if (M < 0 || N < 0 || K < 0) return W8A8_ERR_SHAPE;
   if (!workspace || (!sw && N)) return W8A8_ERR_NULL;
   if (!aligned(workspace, kWsAlign)) return W8A8_ERR_ALIGN;
-  if (ws_bytes < w8a8_linear_workspace_bytes(M, K)) return W8A8_ERR_ARG;
+  if (ws_bytes < w8a8_linear_workspace_bytes(M, N, K)) return W8A8_ERR_ARG;
   int8_t* qx = (int8_t*)workspace;
-  float* sx = (float*)((char*)workspace + round_up((size_t)M * (size_t)K, kWsAlign));
+  const size_t off_sx = round_up((size_t)M * (size_t)K, kWsAlign);
+  float* sx = (float*)((char*)workspace + off_sx);
+  int32_t* part = (int32_t*)((char*)workspace + off_sx + round_up((size_t)M * 4, kWsAlign));
   w8a8_status_t st = check_quant(x, dtype, M, K, inv_s, qx, sx);
   if (st != W8A8_OK) return st;
   st = check_gemm(qx, qw, y, M, N, K);
@@ -189,6 +202,9 @@ w8a8_status_t w8a8_linear(const void* x, int dtype, const float* inv_s, const in
   hipError_t e = w8a8::launch_scale_quant_rows(x, dtype == W8A8_BF16, M, K, inv_s, false, 0.0f, qx,
                                                sx, 0, stream);
   if (e != hipSuccess) return W8A8_ERR_HIP;
+  if (linear_splitk(M, N, K))
+    return hip_status(w8a8::launch_gemm_splitk(qx, qw, M, N, K, sx, sw, y, dtype == W8A8_BF16, part,
+                                               stream));
   return hip_status(w8a8::launch_gemm(qx, qw, M, N, K, sx, sw, y, dtype == W8A8_BF16 ? 2 : 1,
                                       stream));
 }

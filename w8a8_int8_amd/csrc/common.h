@@ -25,6 +25,18 @@ hipError_t launch_scale_quant_rows(const void* x, bool bf16, int64_t rows, int64
                                    const float* col_scale, bool norm, float eps, void* q,
                                    float* row_scale, int fmt, hipStream_t st);
 hipError_t launch_fold(const float* a, const float* b, int64_t n, float* out, hipStream_t st);
+// Split-K few-token GEMM with the dequant epilogue (17 <= M <= 32): S int32
+// partial slices of M x N in `partials` (S from splitk_plan), summed exactly
+// by a second kernel.  With S == 1 there is one launch and `partials` is unused.
+constexpr int kSplitkCT = 4;  // 16-channel weight fragments per block
+struct SplitkPlan {
+  int splits;
+  int steps_per_split;  // 64-deep k steps per split; 0: shape not served
+};
+SplitkPlan splitk_plan(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_splitk(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N, int64_t K,
+                              const float* sa, const float* sb, void* y, bool bf16,
+                              int32_t* partials, hipStream_t st);
 // out_mode: 0 = int32 accumulators, 1 = fp16 dequant, 2 = bf16 dequant (int8
 // operands, K in bytes); 3 = fp16, 4 = bf16 dense product (16-bit operands,
 // K in elements, fp32 accumulation); 5 = fp16, 6 = bf16 dequant of FP8 E4M3

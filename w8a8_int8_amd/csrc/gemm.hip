@@ -47,6 +47,8 @@
 // and load as zero too.  Blocks are dispatched round-robin over the 8 XCDs;
 // tile indices are remapped so each XCD (own L2) gets a contiguous run of
 // tiles, ordered token-tile fastest in groups of 8 token tiles.
+#include <algorithm>
+
 #include "common.h"
 
 namespace w8a8 {
@@ -496,6 +498,146 @@ hipError_t launch_skinny(const int8_t* qa, const int8_t* qb, int64_t M, int64_t 
   return hipGetLastError();
 }
 
+// Split-K few-token GEMM (the runtime forward's path for 17 <= M <= 32, where
+// the skinny kernel's per-16-channel re-reading of the activations costs more
+// than splitting K; measured slower than the skinny kernel below 17).  A block
+// owns 16 * CT output channels and one of S contiguous ranges of 64-deep k
+// steps; its NW waves take the steps of that range in turn.  Per step a wave
+// loads CT weight fragments and MT activation fragments straight into
+// registers and issues CT * MT v_mfma_i32_16x16x64_i8, so each activation
+// fragment serves CT weight fragments (the skinny kernel re-reads the whole
+// activation once per 16 channels).  The waves' int32 partials add exactly
+// through LDS.  With S == 1 the block applies the dequant epilogue itself;
+// otherwise it stores its int32 partial slice (rows < M) and
+// k_splitk_reduce adds the S slices exactly and dequantizes.
+template <int MT, int CT, int U, int OUT>
+__global__ __launch_bounds__(512) void k_gemm_splitk(const int8_t* __restrict__ qa,
+                                                     const int8_t* __restrict__ qb, int M, int N,
+                                                     int K, int steps_per_split,
+                                                     const float* __restrict__ sa,
+                                                     const float* __restrict__ sb,
+                                                     void* __restrict__ out) {
+  constexpr int NW = 8;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n0 = blockIdx.x * 16 * CT;
+  const int split = blockIdx.y;
+  const int nsteps = (K + 63) / 64;
+  const int st0 = split * steps_per_split;
+  const int st1 = min(nsteps, st0 + steps_per_split);
+  const rsrc_t rw = make_rsrc(qb + (int64_t)n0 * K, (unsigned)min(16 * CT, N - n0) * (unsigned)K);
+  const rsrc_t rx = make_rsrc(qa, (unsigned)M * (unsigned)K);
+  const int r16 = lane & 15, kq = lane >> 4;  // fragment row, 16-byte k chunk
+  int voff_w[CT], voff_x[MT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) voff_w[c] = (c * 16 + r16) * K + kq * 16;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) voff_x[t] = (t * 16 + r16) * K + kq * 16;
+
+  v4i acc[CT][MT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[c][t] = v4i{0, 0, 0, 0};
+  for (int s0 = st0 + wave; s0 < st1; s0 += NW * U) {
+    v4i w[U][CT], x[U][MT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int st = s0 + u * NW;
+      const int k0 = st * 64;
+      const bool out_k = st >= st1 || k0 + kq * 16 >= K;
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+        w[u][c] = __builtin_amdgcn_raw_buffer_load_b128(rw, out_k ? kOob : voff_w[c], k0, 0);
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        x[u][t] = __builtin_amdgcn_raw_buffer_load_b128(rx, out_k ? kOob : voff_x[t], k0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+          acc[c][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[u][c], x[u][t], acc[c][t], 0, 0, 0);
+  }
+
+  // exact sum of the waves' partials; fragment f is finished by wave f % NW
+  __shared__ v4i red[NW][CT * MT][64];
+#pragma unroll
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) red[wave][c * MT + t][lane] = acc[c][t];
+  __syncthreads();
+  for (int f = wave; f < CT * MT; f += NW) {
+    v4i cs = red[0][f][lane];
+#pragma unroll
+    for (int w2 = 1; w2 < NW; ++w2) cs += red[w2][f][lane];
+    // lane holds channels n .. n+3 of token m
+    const int m = (f % MT) * 16 + (lane & 15);
+    const int n = n0 + (f / MT) * 16 + 4 * (lane >> 4);
+    if (m >= M || n >= N) continue;
+    if (OUT == 0) {
+      *(v4i*)((int32_t*)out + ((int64_t)split * M + m) * N + n) = cs;
+    } else {
+      const float am = sa[m];
+      const float4 bn = *(const float4*)(sb + n);
+      const float wv[4] = {bn.x, bn.y, bn.z, bn.w};
+      unsigned short h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float y = (float)cs[e];
+        y = y * am;
+        y = y * wv[e];
+        h[e] = OUT == 1 ? f32_to_f16_rne(y) : f32_to_bf16_rne(y);
+      }
+      uint2 o;
+      o.x = (unsigned)h[0] | ((unsigned)h[1] << 16);
+      o.y = (unsigned)h[2] | ((unsigned)h[3] << 16);
+      *(uint2*)((unsigned short*)out + (int64_t)m * N + n) = o;
+    }
+  }
+}
+
+// Exact int32 sum of the S partial slices (S x M x N), then the dequant
+// epilogue; one thread per 4 consecutive channels of one token.
+template <int OUT>
+__global__ __launch_bounds__(256) void k_splitk_reduce(const int32_t* __restrict__ part, int S,
+                                                       int M, int N, const float* __restrict__ sa,
+                                                       const float* __restrict__ sb,
+                                                       void* __restrict__ y) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (m, n / 4)
+  const int n4 = N / 4;
+  if (i >= (int64_t)M * n4) return;
+  const int m = (int)(i / n4), n = (int)(i % n4) * 4;
+  v4i c = *(const v4i*)(part + (int64_t)m * N + n);
+  for (int s = 1; s < S; ++s) c += *(const v4i*)(part + ((int64_t)s * M + m) * N + n);
+  const float am = sa[m];
+  const float4 bn = *(const float4*)(sb + n);
+  const float wv[4] = {bn.x, bn.y, bn.z, bn.w};
+  unsigned short h[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float v = (float)c[e];
+    v = v * am;
+    v = v * wv[e];
+    h[e] = OUT == 1 ? f32_to_f16_rne(v) : f32_to_bf16_rne(v);
+  }
+  uint2 o;
+  o.x = (unsigned)h[0] | ((unsigned)h[1] << 16);
+  o.y = (unsigned)h[2] | ((unsigned)h[3] << 16);
+  *(uint2*)((unsigned short*)y + (int64_t)m * N + n) = o;
+}
+
+template <int MT, int OUT>
+void launch_splitk_kernel(const int8_t* qa, const int8_t* qb, int M, int N, int K, int s, int spp,
+                          const float* sa, const float* sb, void* out, hipStream_t st) {
+  constexpr int CT = kSplitkCT, U = 3;
+  const dim3 grid((unsigned)((N + 16 * CT - 1) / (16 * CT)), (unsigned)s), block(512);
+  hipLaunchKernelGGL((k_gemm_splitk<MT, CT, U, OUT>), grid, block, 0, st, qa, qb, M, N, K, spp, sa,
+                     sb, out);
+}
+
 template <int BM, int BN, int BK, int NST, int WGM, int WGN>
 hipError_t launch_tile(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N, int64_t K,
                        const float* sa, const float* sb, void* out, int mode, hipStream_t st) {
@@ -576,5 +718,43 @@ hipError_t launch_gemm(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N,
     default: return launch_tile<128, 128, GEMM_W128>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
   }
 }
+
+
+SplitkPlan splitk_plan(int64_t M, int64_t N, int64_t K) {
+  SplitkPlan p{1, 0};
+  if (M < 17 || M > 32 || N < 1 || K < 1) return p;
+  const int64_t tiles = (N + 16 * kSplitkCT - 1) / (16 * kSplitkCT);
+  const int64_t nsteps = (K + 63) / 64;
+  // about one block per CU, and at least 32 k steps (2 KiB of each weight row) per split
+  int64_t s = (256 + tiles - 1) / tiles;
+  s = std::min<int64_t>(s, std::max<int64_t>(1, nsteps / 32));
+  s = std::min<int64_t>(s, 16);
+  p.splits = (int)s;
+  p.steps_per_split = (int)((nsteps + s - 1) / s);
+  return p;
+}
+
+hipError_t launch_gemm_splitk(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N, int64_t K,
+                              const float* sa, const float* sb, void* y, bool bf16,
+                              int32_t* partials, hipStream_t st) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const SplitkPlan p = splitk_plan(M, N, K);
+  if (p.steps_per_split == 0) return hipErrorInvalidValue;
+  const int m = (int)M, n = (int)N, k = (int)K;
+  if (p.splits == 1) {
+    if (bf16) launch_splitk_kernel<2, 2>(qa, qb, m, n, k, 1, p.steps_per_split, sa, sb, y, st);
+    else launch_splitk_kernel<2, 1>(qa, qb, m, n, k, 1, p.steps_per_split, sa, sb, y, st);
+    return hipGetLastError();
+  }
+  launch_splitk_kernel<2, 0>(qa, qb, m, n, k, p.splits, p.steps_per_split, sa, sb, partials, st);
+  const int64_t threads = M * (N / 4);
+  const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  if (bf16)
+    hipLaunchKernelGGL(k_splitk_reduce<2>, grid, block, 0, st, partials, p.splits, m, n, sa, sb, y);
+  else
+    hipLaunchKernelGGL(k_splitk_reduce<1>, grid, block, 0, st, partials, p.splits, m, n, sa, sb, y);
+  return hipGetLastError();
+}
+
 
 }  // namespace w8a8
