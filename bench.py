@@ -138,38 +138,63 @@ class Layer:
             ev[1].record()
 
 
-def kernel_breakdown(layers, reps):
-    """Per-kernel mean durations (HIP events), each kernel type timed alone."""
+def graph_time(fn, n):
+    """Mean seconds per call of fn(i), i < n, from one replay of a HIP graph
+    that holds the n calls (after one eager call and one warm-up replay), so
+    that the host's launch cost, larger than the small kernels here, does not
+    enter."""
     import torch
 
-    def timed(fn, n):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        fn(0)
-        torch.cuda.synchronize()
-        a.record()
+    fn(0)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
         for i in range(n):
             fn(i)
-        b.record()
-        b.synchronize()
-        return a.elapsed_time(b) / n * 1e-3  # seconds
+    graph.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    graph.replay()
+    b.record()
+    b.synchronize()
+    return a.elapsed_time(b) / n * 1e-3
+
+
+def rotation(t, min_total=512 << 20, cap=32):
+    """t and copies of it, together at least min_total bytes: a kernel timed
+    over them in turn reads HBM, not the 256 MB last-level cache."""
+    n = max(1, min(cap, -(-min_total // (t.numel() * t.element_size()))))
+    return [t] + [t.clone() for _ in range(n - 1)]
+
+
+def kernel_breakdown(layers, reps):
+    """Per-kernel mean durations, each kernel type timed alone (graph_time).
+    The bandwidth-bound kernels rotate over copies of their input (rotation)."""
+    import torch
+
+    timed = graph_time
+
+    def hbm(t, by):
+        return dict(us=t * 1e6, GBs=by / t / 1e9, frac_hbm=by / t / 1e9 / PEAK_HBM_GBS)
 
     w8 = layers[0].w8
     out = {}
     for L in layers:
         d = {}
-        nb = len(L.cal)
-        t = timed(lambda i: w8.channel_amax(L.cal[i % nb], L.amax_x), reps)
-        by = L.cal[0].numel() * 2
-        d["channel_amax_calib"] = dict(us=t * 1e6, GBs=by / t / 1e9, frac_hbm=by / t / 1e9 / PEAK_HBM_GBS)
-        t = timed(lambda i: w8.channel_amax(L.w, L.amax_w), reps)
-        by = L.w.numel() * 2
-        d["channel_amax_weight"] = dict(us=t * 1e6, GBs=by / t / 1e9, frac_hbm=by / t / 1e9 / PEAK_HBM_GBS)
-        t = timed(lambda i: w8.scale_quant_rows(L.w, L.s, L.qw, L.sw), reps)
-        by = L.w.numel() * 3 + 4 * (L.N + L.K)
-        d["fold_quant_weight"] = dict(us=t * 1e6, GBs=by / t / 1e9, frac_hbm=by / t / 1e9 / PEAK_HBM_GBS)
-        t = timed(lambda i: w8.scale_quant_rows(L.x, L.inv_s, L.qx, L.sx), reps)
-        by = L.x.numel() * 3 + 4 * (L.M + L.K)
-        d["smooth_quant_act"] = dict(us=t * 1e6, GBs=by / t / 1e9, frac_hbm=by / t / 1e9 / PEAK_HBM_GBS)
+        cal = L.cal if sum(c.numel() * 2 for c in L.cal) >= (512 << 20) else rotation(L.cal[0])
+        nb = len(cal)
+        t = timed(lambda i: w8.channel_amax(cal[i % nb], L.amax_x), reps)
+        d["channel_amax_calib"] = hbm(t, cal[0].numel() * 2)
+        ws = rotation(L.w)
+        xs = rotation(L.x)
+        nw, nx = len(ws), len(xs)
+        t = timed(lambda i: w8.channel_amax(ws[i % nw], L.amax_w), reps)
+        d["channel_amax_weight"] = hbm(t, L.w.numel() * 2)
+        t = timed(lambda i: w8.scale_quant_rows(ws[i % nw], L.s, L.qw, L.sw), reps)
+        d["fold_quant_weight"] = hbm(t, L.w.numel() * 3 + 4 * (L.N + L.K))
+        t = timed(lambda i: w8.scale_quant_rows(xs[i % nx], L.inv_s, L.qx, L.sx), reps)
+        d["smooth_quant_act"] = hbm(t, L.x.numel() * 3 + 4 * (L.M + L.K))
         t = timed(lambda i: w8.gemm_dequant(L.qx, L.sx, L.qw, L.sw, L.x.dtype, L.y), reps)
         ops = L.gemm_ops()
         d["gemm_dequant"] = dict(us=t * 1e6, TOPS=ops / t / 1e12, frac_mfma=ops / t / 1e12 / PEAK_INT8_TOPS)
@@ -178,21 +203,17 @@ def kernel_breakdown(layers, reps):
                                  frac_mfma=ops / t16 / 1e12 / PEAK_DENSE16_TFLOPS)
         # the smoothing folded into the RMS norm in front of the layer (x taken as the norm's input)
         g = w8.fold_norm_weight(torch.ones(L.K, dtype=torch.float32, device=L.x.device), L.inv_s)
-        t = timed(lambda i: w8.rmsnorm_quant_rows(L.x, g, 1e-5, L.qx, L.sx), reps)
-        by = L.x.numel() * 3 + 4 * (L.M + L.K)
-        d["rmsnorm_smooth_quant_act"] = dict(us=t * 1e6, GBs=by / t / 1e9,
-                                             frac_hbm=by / t / 1e9 / PEAK_HBM_GBS)
+        t = timed(lambda i: w8.rmsnorm_quant_rows(xs[i % nx], g, 1e-5, L.qx, L.sx), reps)
+        d["rmsnorm_smooth_quant_act"] = hbm(t, L.x.numel() * 3 + 4 * (L.M + L.K))
         # FP8 (E4M3) form of the same layer: codes from the same smoothed tensors
         qw8, sw8 = w8.scale_quant_rows_e4m3(L.w, L.s)
         qx8, sx8 = w8.scale_quant_rows_e4m3(L.x, L.inv_s)
-        t = timed(lambda i: w8.scale_quant_rows_e4m3(L.x, L.inv_s, qx8, sx8), reps)
-        by = L.x.numel() * 3 + 4 * (L.M + L.K)
-        d["smooth_quant_act_e4m3"] = dict(us=t * 1e6, GBs=by / t / 1e9,
-                                          frac_hbm=by / t / 1e9 / PEAK_HBM_GBS)
+        t = timed(lambda i: w8.scale_quant_rows_e4m3(xs[i % nx], L.inv_s, qx8, sx8), reps)
+        d["smooth_quant_act_e4m3"] = hbm(t, L.x.numel() * 3 + 4 * (L.M + L.K))
         t8 = timed(lambda i: w8.gemm_dequant_e4m3(qx8, sx8, qw8, sw8, L.x.dtype, L.y), reps)
         d["gemm_dequant_e4m3"] = dict(us=t8 * 1e6, TFLOPS=ops / t8 / 1e12,
                                       frac_mfma=ops / t8 / 1e12 / PEAK_FP8_TFLOPS)
-        del qw8, sw8, qx8, sx8
+        del qw8, sw8, qx8, sx8, ws, xs
         out[f"{L.name}_{L.K}x{L.N}"] = {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in d.items()}
     # W8A8 vs the dense 16-bit product on the same shapes, summed over the layers
     t_w8 = sum(v["gemm_dequant"]["us"] for v in out.values())
@@ -229,23 +250,7 @@ def decode_sweep(wl, layers, reps):
             sx = ws[off:off + 4 * M].view(torch.float32)
             w8.linear(x, L.inv_s, L.qw, L.sw, y, ws)
 
-            def run(fn, n=reps):
-                # few-token kernels are shorter than a Python-side launch: time
-                # n calls captured in one HIP graph, replayed twice
-                fn(0)
-                torch.cuda.synchronize()
-                graph = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(graph):
-                    for i in range(n):
-                        fn(i)
-                graph.replay()
-                torch.cuda.synchronize()
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                graph.replay()
-                b.record()
-                b.synchronize()
-                return a.elapsed_time(b) / n * 1e-3
+            run = lambda fn: graph_time(fn, reps)  # noqa: E731
 
             t_lin = run(lambda i: w8.linear(x, L.inv_s, qws[i % copies], L.sw, y, ws))
             t_q = run(lambda i: w8.scale_quant_rows(x, L.inv_s, qx, sx))
