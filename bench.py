@@ -66,10 +66,10 @@ def gemm_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def pmc_traffic(workload: str):
+def pmc_traffic(workload: str, kernel: str = "gemm_i8"):
     """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
     or None when there is none or the GEMM source changed since it was taken."""
-    path = os.path.join(PROFILES, f"gemm_i8_{workload}_pmc.txt")
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_pmc.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -403,7 +403,7 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(bytes_per_launch / gemm_launch_avg / 1e9 / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": pmc_traffic(wl.name, "gemm_skinny"),
             "bytes_per_launch": bytes_per_launch,
             "avg_launch_us": round(gemm_launch_avg * 1e6, 3),
         },
