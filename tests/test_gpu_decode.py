@@ -56,7 +56,8 @@ def test_linear_decode_split_k(dtype, N, K, M):
     x = torch.randn((M, K), generator=g)
     x[:, :3] *= 50.0
     x = x.to(dtype).to(DEV)
-    ws = torch.zeros(w8.linear_workspace_bytes(M, N, K), dtype=torch.uint8, device=DEV)
+    # the workspace needs no initialisation: fill it with garbage
+    ws = torch.full((w8.linear_workspace_bytes(M, N, K),), 0x5A, dtype=torch.uint8, device=DEV)
     y = w8.linear(x, p["inv_s"], p["qw"], p["sw"], workspace=ws)
     qx = ws[:M * K].view(torch.int8).view(M, K)
     off = (M * K + 255) // 256 * 256
