@@ -225,14 +225,18 @@ def test_gemm_dequant_e4m3_exact_integers(out, M, N, K):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("li", [1, 3])
-def test_fp8_layer_llama2_7b(li):
-    """The FP8 form of a Llama-2-7B prefill layer (2048 tokens): weight and
-    activation codes and scales bit-exact on sampled rows, Y on sampled
-    (token, channel) blocks within the fp32 accumulation bound."""
-    wl = synth.WORKLOADS["llama2_7b_prefill"]
+@pytest.mark.parametrize("name,li", [("llama2_7b_prefill", 1), ("llama2_7b_prefill", 3),
+                                     ("llama2_70b_prefill", 0)])
+def test_fp8_layer(name, li):
+    """The FP8 form of a full-size prefill layer (Llama-2-7B fp16 at 2048
+    tokens, Llama-2-70B bf16 at 8192): weight and activation codes and scales
+    bit-exact on sampled rows, Y on sampled (token, channel) blocks within the
+    FP8 accumulation bound."""
+    wl = synth.WORKLOADS[name]
     L = wl.layers[li]
     M = wl.M[0]
+    dn = wl.dtype
+    out = torch.float16 if dn == "f16" else torch.bfloat16
     xc = synth.calibration(wl, li, wl.cal_batch, device=DEV)
     w = synth.weights(wl, li, device=DEV)
     x = synth.activations(wl, li, M, device=DEV)
@@ -241,15 +245,15 @@ def test_fp8_layer_llama2_7b(li):
     s, inv_s = w8.smooth_factors(amax_x, amax_w, 0.5)
     qw, sw = w8.scale_quant_rows_e4m3(w, s)
     qx, sx = w8.scale_quant_rows_e4m3(x, inv_s)
-    y = w8.gemm_dequant_e4m3(qx, sx, qw, sw, torch.float16)
+    y = w8.gemm_dequant_e4m3(qx, sx, qw, sw, out)
     torch.cuda.synchronize()
 
     rows = sample(M, 24, li)
     cols = sample(L.N, 40, li + 100)
-    qx_or, sx_or = oracle.scale_quant_rows_e4m3(synth.to_numpy_bits(x)[rows], "f16", host(inv_s))
+    qx_or, sx_or = oracle.scale_quant_rows_e4m3(synth.to_numpy_bits(x)[rows], dn, host(inv_s))
     assert np.array_equal(host(qx)[rows], qx_or)
     assert np.array_equal(host(sx)[rows].view(np.uint32), sx_or.view(np.uint32))
-    qw_or, sw_or = oracle.scale_quant_rows_e4m3(synth.to_numpy_bits(w)[cols], "f16", host(s))
+    qw_or, sw_or = oracle.scale_quant_rows_e4m3(synth.to_numpy_bits(w)[cols], dn, host(s))
     assert np.array_equal(host(qw)[cols], qw_or)
     assert np.array_equal(host(sw)[cols].view(np.uint32), sw_or.view(np.uint32))
-    check_fp8_y(y, qx, sx, qw, sw, "f16", rows=rows, cols=cols)
+    check_fp8_y(y, qx, sx, qw, sw, dn, rows=rows, cols=cols)
