@@ -255,6 +255,28 @@ def test_gpu_alignment_errors_with_real_buffers():
 # ---------------------------------------- the five workloads at full size
 
 
+def assert_freivalds(c, qx, qw, seed, vectors=4):
+    """The whole M x N accumulator matrix against the oracle's codes without
+    forming their product: for random integer vectors r in [-256, 256]^N,
+    C r == qX (qW^T r) exactly.  Every partial sum is an integer below 2^53
+    (|qW^T r| <= 127 * 256 * N, |qX (qW^T r)| and |C r| <= 127^2 * 256 * K * N
+    < 2^53 at every workload size), so fp64 products are exact.  A wrong C
+    passes one vector with probability at most 1/513."""
+    rng = np.random.default_rng(seed)
+    N = qw.shape[0]
+    for _ in range(vectors):
+        r = rng.integers(-256, 257, N).astype(np.float64)
+        v = np.zeros(qw.shape[1], dtype=np.float64)
+        for n0 in range(0, N, 4096):  # qW^T r, in row blocks to bound host memory
+            v += r[n0:n0 + 4096] @ qw[n0:n0 + 4096].astype(np.float64)
+        lhs = np.zeros(c.shape[0], dtype=np.float64)
+        rhs = np.zeros(c.shape[0], dtype=np.float64)
+        for m0 in range(0, c.shape[0], 512):
+            lhs[m0:m0 + 512] = c[m0:m0 + 512].astype(np.float64) @ r
+            rhs[m0:m0 + 512] = qx[m0:m0 + 512].astype(np.float64) @ v
+        assert np.array_equal(lhs, rhs)
+
+
 def _sample_rows(M, n=48, seed=0):
     rng = np.random.default_rng(seed)
     rows = set([0, M - 1]) | set(rng.integers(0, M, n).tolist())
@@ -319,6 +341,7 @@ def test_workload_layer(name, li, alpha):
         assert_y_close(y_np[rows], y_or, dname)
         c = host(w8.gemm_i32(qx, p["qw"]))
         assert np.array_equal(c[rows], c_or)
+        assert_freivalds(c, qx_or, qw_or, seed=M + 7 * li)
         ys[M] = y_np
     # decode shapes: the first rows do not depend on how many rows follow
     ms = sorted(wl.M)
