@@ -172,7 +172,7 @@ def check_fp8_y(y, qa, sa, qb, sb, name, rows=None, cols=None):
 @pytest.mark.parametrize("out", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("M,N,K", [(37, 136, 80), (300, 520, 1040), (2048, 4096, 256),
                                    (1, 8, 16), (5, 16, 0), (0, 8, 32), (8, 0, 32),
-                                   (513, 264, 4112), (16, 520, 1040)])
+                                   (513, 264, 4112), (16, 520, 1040), (3000, 6000, 272)])
 def test_gemm_dequant_e4m3_bound(out, M, N, K):
     qa = rand_e4m3_codes(M, K, M + K)
     qb = rand_e4m3_codes(N, K, N + 2 * K + 1, max_code=0x60)

@@ -160,14 +160,14 @@ def rand_codes(rows, cols, seed):
     return torch.randint(-127, 128, (rows, cols), generator=g, dtype=torch.int8).to(DEV)
 
 
-# shapes cover the three tile configurations (128x128, 256x128, 256x256), the
+# shapes cover the four tile configurations (128x128, 256x128, 256x192, 256x256), the
 # skinny few-token kernel (M <= 16 and M <= 32), ragged M, N and K tails, K = 0
 # and empty outputs
 GEMM_SHAPES = [(1, 8, 16), (37, 136, 80), (300, 520, 1040), (64, 512, 512),
                (2048, 4096, 256), (4000, 8184, 272), (4096, 8192, 144), (513, 264, 4112),
                (5, 16, 0), (0, 8, 32), (8, 0, 32),
                (1, 4096, 16384), (3, 8, 64), (16, 520, 1040), (17, 136, 80), (32, 264, 4112),
-               (33, 136, 80), (32, 16384, 272)]
+               (33, 136, 80), (32, 16384, 272), (3000, 6000, 272), (2048, 12288, 144)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
@@ -187,7 +187,8 @@ def test_gemm_i32_extremes():
 
 @pytest.mark.parametrize("out", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("M,N,K", [(37, 136, 80), (300, 520, 1040), (2048, 4096, 256),
-                                   (4000, 8184, 272), (5, 16, 0), (1, 4104, 4112), (32, 264, 1040)])
+                                   (4000, 8184, 272), (5, 16, 0), (1, 4104, 4112), (32, 264, 1040),
+                                   (3000, 6000, 272)])
 def test_gemm_dequant(out, M, N, K):
     qa, qb = rand_codes(M, K, M + K), rand_codes(N, K, N + 2 * K + 1)
     g = torch.Generator(device="cpu").manual_seed(M * N)
@@ -355,7 +356,7 @@ def test_workload_layer(name, li, alpha):
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("M,N,K", [(37, 136, 80), (300, 520, 1040), (2048, 4096, 256),
                                    (4000, 8184, 272), (5, 16, 0), (1, 264, 4104),
-                                   (2048, 12288, 4096)])
+                                   (2048, 12288, 4096), (3000, 6000, 272)])
 def test_gemm_float(dtype, M, N, K):
     """fp32-accumulated dense product: within K 2^-24 sum|a b| of the exact
     value before the final rounding, plus one unit of the output format."""

@@ -695,10 +695,12 @@ hipError_t launch_gemm(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N,
   // Pick the tile whose last wave of blocks over 256 CUs is fullest, with a
   // small preference for the larger tile (more MACs per byte of LDS traffic).
   struct Cand { int bm, bn; double eff; };
-  const Cand cands[] = {{256, 256, 1.0}, {256, 128, 0.92}, {128, 128, 0.8}};
+  // eff: operand bytes per MFMA, which the load-return path into LDS limits,
+  // fall with the tile's BM * BN / (BM + BN)
+  const Cand cands[] = {{256, 256, 1.0}, {256, 128, 0.92}, {128, 128, 0.8}, {256, 192, 0.96}};
   int best = 0;
   double best_score = -1.0;
-  for (int i = 0; i < 3; ++i) {
+  for (int i = 0; i < 4; ++i) {
     const int64_t tiles = ((M + cands[i].bm - 1) / cands[i].bm) * ((N + cands[i].bn - 1) / cands[i].bn);
     const int64_t waves = (tiles + 255) / 256;
     const double fill = (double)tiles / (double)(waves * 256);
@@ -709,12 +711,14 @@ hipError_t launch_gemm(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N,
   }
 #ifndef GEMM_W256
 #define GEMM_W256 128, 2, 2, 4
+#define GEMM_W256x192 128, 2, 4, 2
 #define GEMM_W256x128 128, 3, 4, 2
 #define GEMM_W128 128, 4, 2, 2
 #endif
   switch (best) {
     case 0: return launch_tile<256, 256, GEMM_W256>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
     case 1: return launch_tile<256, 128, GEMM_W256x128>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
+    case 3: return launch_tile<256, 192, GEMM_W256x192>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
     default: return launch_tile<128, 128, GEMM_W128>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
   }
 }
