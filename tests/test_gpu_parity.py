@@ -177,12 +177,17 @@ def test_gemm_i32(M, N, K):
     assert np.array_equal(c, oracle.gemm_i32(host(qa), host(qb)))
 
 
-def test_gemm_i32_extremes():
-    K = 28672
-    qa = torch.full((33, K), 127, dtype=torch.int8, device=DEV)
+@pytest.mark.parametrize("M,K", [(33, 28672), (300, 131072), (8, 131072)])
+def test_gemm_i32_extremes(M, K):
+    """All +127 against all -127 up to the largest K the int32 accumulator
+    allows (W8A8_MAX_K): -16129 K = -2114060288 at K = 131072, inside int32."""
+    qa = torch.full((M, K), 127, dtype=torch.int8, device=DEV)
     qb = torch.full((16, K), -127, dtype=torch.int8, device=DEV)
     c = host(w8.gemm_i32(qa, qb))
     assert (c == -16129 * K).all()
+    qb[3] = 127  # and the largest positive sum
+    c = host(w8.gemm_i32(qa, qb))
+    assert (c[:, 3] == 16129 * K).all() and (c[:, 4] == -16129 * K).all()
 
 
 @pytest.mark.parametrize("out", [torch.float16, torch.bfloat16])
