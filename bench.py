@@ -59,10 +59,15 @@ def parse():
 
 
 def gemm_source_hash() -> str:
+    """Hash of the GEMM sources' code (comments and blank lines dropped), which
+    ties a committed counter summary to the kernels it was taken from."""
     h = hashlib.sha256()
     for f in ("gemm.hip", "common.h"):
-        with open(os.path.join(ROOT, "w8a8_int8_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "w8a8_int8_amd", "csrc", f)) as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

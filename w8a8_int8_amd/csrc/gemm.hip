@@ -16,37 +16,49 @@
 // one token: the epilogue writes 4 fp16 / bf16 (8 B) or 4 int32 (16 B) per
 // lane per register group.  Integer accumulation is exact and order free.
 //
-// Block: 256 threads (4 waves, one per SIMD) own a BM x BN output tile
-// (tokens x channels); the waves form a 2 x 2 grid, each holding a
-// (BM/2) x (BN/2) register tile of 32 x 32 MFMA blocks in the accumulation
-// registers.
+// Block: WGM x WGN waves (8 for the 256-row tiles, 4 for 128 x 128) own a
+// BM x BN output tile (tokens x channels); wave (wm, wn) holds a
+// (BM / WGM) x (BN / WGN) register tile of 32 x 32 MFMA blocks.  Tiles:
+// 256 x 256, 256 x 192, 256 x 128 and 128 x 128; launch_gemm picks the one
+// whose last wave of blocks over the 256 CUs is fullest, preferring fewer
+// operand bytes per MFMA (the return path of the operand loads is the
+// limiting resource).
 //
-// K pipeline: K advances 64 bytes per stage through NST = 4 LDS slots.
-// Operand rows go from global memory straight into LDS with buffer loads in
-// LDS mode (16 B per lane, each wave instruction fills 1 KiB of LDS); the
-// prologue fills all four slots and every stage barrier refills the slot just
-// consumed with the stage four ahead, so up to three stages are in flight
-// while one is computed and a wave never holds global data in registers.  Per stage
-// a wave reads its fragments for the two 32-deep k steps with 128-bit LDS
-// reads and issues 2 x (BN/64) x (BM/64) MFMAs.  The fragment reads are
-// software pipelined: the second k step's fragments are read while the first
-// step's MFMAs run, and the next stage's first fragments are read (after the
-// stage barrier) while the second step's MFMAs run.  One barrier per stage;
-// it is a plain s_barrier (no memory fence), with the needed waits explicit:
-// each wave waits for its own LDS-mode loads of the next stage (vmcnt) and
-// for its own LDS reads of the slot that is about to be refilled (lgkmcnt).
+// K pipeline: K advances BK = 128 bytes per stage (one full cache line per
+// operand row) through NST LDS slots (2 to 4, as many as 160 KB of LDS holds
+// for the tile).  Operand rows go from global memory straight into LDS with
+// buffer loads in LDS mode (16 B per lane, each wave instruction fills 1 KiB
+// of LDS); the prologue fills all NST slots and every stage barrier refills
+// the slot just consumed with the stage NST ahead, so up to NST - 1 stages are
+// in flight while one is computed and a wave never holds global data in
+// registers.  Stages past the end are issued with out-of-range offsets (no
+// memory traffic) so the per-stage load count, and with it every vmcnt wait,
+// is constant.  Per stage a wave runs BK / 32 k steps (BK / 64 for FP8, whose
+// MFMA takes 64 bytes of K) of (BM / WGM / 32) x (BN / WGN / 32) MFMAs.  The
+// fragment reads are software pipelined: the next k step's fragments are read
+// while the current step's MFMAs run, and the next stage's first fragments
+// are read (after the stage barrier) while the last step's MFMAs run.  One
+// barrier per stage; it is a plain s_barrier (no memory fence), with the
+// needed waits explicit: each wave waits for its own LDS-mode loads of the
+// next stage (vmcnt) and for its own LDS reads of the slot that is about to
+// be refilled (lgkmcnt).
 //
-// LDS layout: a tile row is 64 B = 4 chunks of 16 B; four rows share one
-// 256-byte bank window.  Chunk c of row r sits at chunk slot c ^ ((r >> 2) & 3)
-// of that row, so the 16 lanes of a quarter wave reading one k chunk down 16
-// consecutive rows hit 16 distinct 16-byte bank groups.  The loads realize
-// the swizzle by choosing, per lane, which global chunk lands in its slot.
+// LDS layout: a tile row is BK bytes = CPR chunks of 16 B; RPW = 16 / CPR
+// rows share one 256-byte bank window.  Chunk c of row r sits at chunk slot
+// c ^ ((r / RPW) % CPR) of that row, so the lanes of a quarter wave reading
+// one k chunk down consecutive rows hit distinct 16-byte bank groups.  The
+// loads realize the swizzle by choosing, per lane, which global chunk lands in
+// its slot.
 //
 // Edges: the buffer resource of each operand tile ends at its last valid row,
 // so rows past M or N load as zero; chunks past K use an out-of-range offset
 // and load as zero too.  Blocks are dispatched round-robin over the 8 XCDs;
 // tile indices are remapped so each XCD (own L2) gets a contiguous run of
 // tiles, ordered token-tile fastest in groups of 8 token tiles.
+//
+// The same pipeline serves the dense fp16 / bf16 product (the comparison
+// baseline) and the FP8 E4M3 variant; few-token shapes go to k_gemm_skinny
+// and, in the runtime forward, to the split-K k_gemm_splitk (below).
 #include <algorithm>
 
 #include "common.h"
