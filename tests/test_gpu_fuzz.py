@@ -1,8 +1,9 @@
 """Seeded random shapes through every entry point, against the CPU oracle.
 
 Shapes are drawn small (the oracle finishes each in well under a second) but
-cover empty inputs, ragged tails of every tile size, the few-token GEMM path,
-zero rows, dead channels and both 16-bit input types.
+cover empty inputs, ragged tails of every tile size, the few-token GEMM paths
+(skinny and split-K), zero rows, dead channels, both 16-bit input types, the
+FP8 quantizer, the RMS-norm fold and the dense 16-bit product.
 """
 from __future__ import annotations
 
@@ -118,3 +119,75 @@ def test_repeat_runs_are_bitwise_identical():
     for o in outs[1:]:
         for a, b in zip(outs[0], o):
             assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_fuzz_e4m3_quant(case):
+    rng = np.random.default_rng(4000 + case)
+    dtype = torch.float16 if case % 2 == 0 else torch.bfloat16
+    rows = int(rng.choice([0, 1, int(rng.integers(2, 40))]))
+    cols = 16 * int(rng.integers(0 if case % 5 else 1, 120))
+    x = rand_x(rng, rows, cols, dtype)
+    c = torch.from_numpy(np.exp(rng.uniform(-6, 6, cols)).astype(np.float32)).to(DEV)
+    q, d = w8.scale_quant_rows_e4m3(x, c)
+    q_or, d_or = oracle.scale_quant_rows_e4m3(bits(x), dt(x), host(c))
+    assert np.array_equal(host(q), q_or)
+    assert np.array_equal(host(d).view(np.uint32), d_or.view(np.uint32))
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_fuzz_rmsnorm_quant(case):
+    rng = np.random.default_rng(5000 + case)
+    dtype = torch.float16 if case % 2 == 0 else torch.bfloat16
+    rows = int(rng.choice([1, int(rng.integers(2, 300))]))
+    cols = 16 * int(rng.integers(1, 300))
+    h = rand_x(rng, rows, cols, dtype)
+    gamma = torch.from_numpy(rng.uniform(0.1, 3.0, cols).astype(np.float32)).to(DEV)
+    inv_s = torch.from_numpy(np.exp(rng.uniform(-5, 3, cols)).astype(np.float32)).to(DEV)
+    eps = float(rng.choice([0.0, 1e-6, 1e-5, 0.1]))
+    g = w8.fold_norm_weight(gamma, inv_s)
+    q, d = w8.rmsnorm_quant_rows(h, g, eps)
+    g_or = oracle.fold_norm_weight(host(gamma), host(inv_s))
+    assert np.array_equal(host(g).view(np.uint32), g_or.view(np.uint32))
+    q_or, d_or = oracle.rmsnorm_smooth_quant_rows(bits(h), dt(h), g_or, eps)
+    assert np.array_equal(host(q), q_or)
+    dh = host(d).astype(np.float64)
+    assert (np.abs(dh - d_or) <= d_or * (cols / 2 + 6) * 2.0 ** -24).all()
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_fuzz_gemm_float(case):
+    """Dense 16-bit product: within K 2^-24 sum|a b| of the exact value, plus
+    one unit of the output format."""
+    rng = np.random.default_rng(6000 + case)
+    dtype = torch.float16 if case % 2 == 0 else torch.bfloat16
+    M = int(rng.choice([0, 1, int(rng.integers(2, 40)), int(rng.integers(40, 600))]))
+    N = 8 * int(rng.integers(1, 90))
+    K = 8 * int(rng.integers(0, 200))
+    a = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to(dtype).to(DEV)
+    b = torch.from_numpy((rng.standard_normal((N, K)) * 0.05).astype(np.float32)).to(dtype).to(DEV)
+    y = w8.gemm_float(a, b)
+    y64, bound = oracle.gemm_float(bits(a), bits(b), dt(a))
+    yb = bits(y)
+    got = yb.astype(np.float64) if dtype == torch.float16 else oracle.widen(yb, "bf16").astype(np.float64)
+    e = np.floor(np.log2(np.maximum(np.abs(y64), 2.0 ** -14 if dtype == torch.float16 else 2.0 ** -126)))
+    ulp = 2.0 ** (e - (10 if dtype == torch.float16 else 7))
+    assert (np.abs(got - y64) <= K * 2.0 ** -24 * bound + ulp).all()
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_fuzz_linear_split_k(case):
+    """17-32 tokens with K long enough that the runtime forward splits it."""
+    rng = np.random.default_rng(7000 + case)
+    dtype = torch.float16 if case % 2 == 0 else torch.bfloat16
+    M = int(rng.integers(17, 33))
+    K = 16 * int(rng.integers(256, 1024))
+    N = 8 * int(rng.integers(1, 160))
+    w = torch.from_numpy((rng.standard_normal((N, K)) * 0.02).astype(np.float32)).to(dtype).to(DEV)
+    xc = rand_x(rng, 64, K, dtype)
+    x = rand_x(rng, M, K, dtype)
+    p = w8.prepare_weight(w, w8.channel_amax(xc), 0.5)
+    y = w8.linear(x, p["inv_s"], p["qw"], p["sw"])
+    qx_or, sx_or = oracle.scale_quant_rows(bits(x), dt(x), host(p["inv_s"]))
+    y_or = oracle.dequant(oracle.gemm_i32(qx_or, host(p["qw"])), sx_or, host(p["sw"]), dt(x))
+    assert np.array_equal(bits(y).view(np.uint16), y_or.view(np.uint16))
