@@ -351,50 +351,90 @@ k_gemm_i8(const int8_t* __restrict__ qa, const int8_t* __restrict__ qb, int M, i
     wait_vmcnt<0>();  // no LDS-mode load may outlive the block's LDS
   }
 
-  // epilogue: lane holds, for register group g, channels n .. n+3 of token m
+  // Epilogue.  A lane holds, for register group g of fragment (a, b), output
+  // channels n .. n+3 of token m, with m = b * 32 + (lane & 31) and
+  // n = a * 32 + g * 8 + (lane >> 5) * 4 inside the wave tile.  Stored like
+  // that, a wave store would cover 32 rows with 16 bytes each, and the store
+  // path, which pays per request, would run at a quarter of its byte rate.
+  // So the results go through LDS, one 32-token slab of the wave tile at a
+  // time: each wave writes its slab into a private staging area and reads it
+  // back row-major, 16 contiguous bytes per lane, for full-line global stores.
+  // The staging row pitch is an odd number of 16-byte chunks, so the 32 rows
+  // of a slab write fall on distinct bank groups.
+  //
+  // The dequant scales are loaded before any store: the memory counter that
+  // their loads are waited on also counts stores, so a scale load issued after
+  // a store would make its use wait for that store to complete.  Indices are
+  // clamped so the loads stay in bounds; stores are guarded (N % 8 == 0, so a
+  // 16-byte chunk of a row is either inside N or wholly outside).
+  constexpr int ES = OUT == 0 ? 4 : 2;  // output element bytes
+  constexpr int CPO = WN * ES / 16;     // 16-byte output chunks per wave-tile row
+  constexpr int PITCH = WN * ES + 16;   // staging row pitch in bytes
+  static_assert((PITCH / 16) % 2 == 1 && NW * 32 * PITCH <= NST * SLOT && (32 * CPO) % 64 == 0,
+                "epilogue staging");
   const int hi = lane >> 5;
+  constexpr bool kDequant = OUT == 1 || OUT == 2 || OUT == 5 || OUT == 6;
+  float am[FM];
+  float4 bn[FN][4];
+  if constexpr (kDequant) {
+#pragma unroll
+    for (int b = 0; b < FM; ++b) am[b] = sa[min(m0 + wm * WM + b * 32 + (lane & 31), M - 1)];
+#pragma unroll
+    for (int a = 0; a < FN; ++a)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        bn[a][g] = *(const float4*)(sb + min(n0 + wn * WN + a * 32 + g * 8 + hi * 4, N - 4));
+  }
+  // every wave is past its last fragment read and its last LDS-mode load
+  wait_lgkmcnt0();
+  block_barrier();
+  int8_t* stage = lds + wave * 32 * PITCH;
 #pragma unroll
   for (int b = 0; b < FM; ++b) {
-    const int m = m0 + wm * WM + b * 32 + (lane & 31);
-    if (m >= M) continue;
-    float am = 0.0f;
-    if (OUT == 1 || OUT == 2 || OUT == 5 || OUT == 6) am = sa[m];
 #pragma unroll
     for (int a = 0; a < FN; ++a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * WN + a * 32 + g * 8 + hi * 4;
-        if (n >= N) continue;
         const acc_t& C = acc[a][b];
-        if (OUT == 0) {
-          v4i o = {(int)C[4 * g + 0], (int)C[4 * g + 1], (int)C[4 * g + 2], (int)C[4 * g + 3]};
-          *(v4i*)((int32_t*)out + (int64_t)m * N + n) = o;
-        } else if (OUT == 3 || OUT == 4) {
-          unsigned short h[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            h[e] = OUT == 3 ? f32_to_f16_rne((float)C[4 * g + e]) : f32_to_bf16_rne((float)C[4 * g + e]);
-          uint2 o;
-          o.x = (unsigned)h[0] | ((unsigned)h[1] << 16);
-          o.y = (unsigned)h[2] | ((unsigned)h[3] << 16);
-          *(uint2*)((unsigned short*)out + (int64_t)m * N + n) = o;
+        int8_t* dst = stage + (lane & 31) * PITCH + (a * 32 + g * 8 + hi * 4) * ES;
+        if constexpr (OUT == 0) {
+          *(v4i*)dst = v4i{(int)C[4 * g + 0], (int)C[4 * g + 1], (int)C[4 * g + 2], (int)C[4 * g + 3]};
         } else {
-          const float4 bn = *(const float4*)(sb + n);
-          const float w[4] = {bn.x, bn.y, bn.z, bn.w};
           unsigned short h[4];
+          if constexpr (OUT == 3 || OUT == 4) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float y = (float)C[4 * g + e];
-            y = y * am;
-            y = y * w[e];
-            h[e] = (OUT == 1 || OUT == 5) ? f32_to_f16_rne(y) : f32_to_bf16_rne(y);
+            for (int e = 0; e < 4; ++e)
+              h[e] = OUT == 3 ? f32_to_f16_rne((float)C[4 * g + e]) : f32_to_bf16_rne((float)C[4 * g + e]);
+          } else {
+            const float w[4] = {bn[a][g].x, bn[a][g].y, bn[a][g].z, bn[a][g].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float y = (float)C[4 * g + e];
+              y = y * am[b];
+              y = y * w[e];
+              h[e] = (OUT == 1 || OUT == 5) ? f32_to_f16_rne(y) : f32_to_bf16_rne(y);
+            }
           }
-          uint2 o;
-          o.x = (unsigned)h[0] | ((unsigned)h[1] << 16);
-          o.y = (unsigned)h[2] | ((unsigned)h[3] << 16);
-          *(uint2*)((unsigned short*)out + (int64_t)m * N + n) = o;
+          *(uint2*)dst = uint2{(unsigned)h[0] | ((unsigned)h[1] << 16),
+                               (unsigned)h[2] | ((unsigned)h[3] << 16)};
         }
       }
+    }
+    // read the slab back row-major (LDS operations of one wave complete in
+    // order, so the reads see the writes above and precede the next slab's)
+    constexpr int NR = 32 * CPO / 64;
+    v4i v[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int f = i * 64 + lane;
+      v[i] = *(const v4i*)(stage + (f / CPO) * PITCH + (f % CPO) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int f = i * 64 + lane;
+      const int m = m0 + wm * WM + b * 32 + f / CPO;
+      const int n = n0 + wn * WN + (f % CPO) * (16 / ES);
+      if (m < M && n < N) *(v4i*)((int8_t*)out + ((int64_t)m * N + n) * ES) = v[i];
     }
   }
 }
