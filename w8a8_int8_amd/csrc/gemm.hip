@@ -187,9 +187,11 @@ __device__ __forceinline__ void tile_of(int bid, int m_tiles, int n_tiles, int& 
 // front-loaded so their latency overlaps the remaining MFMAs.
 template <int I, int NMFMA, int NDS, int NVM>
 __device__ __forceinline__ void interleave() {
+  constexpr int VPM = (NVM + NMFMA - 1) / NMFMA;  // VMEMs per MFMA
   __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
   if constexpr (I < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-  if constexpr (I < NVM) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one VMEM
+  if constexpr (I * VPM < NVM)
+    __builtin_amdgcn_sched_group_barrier(0x010, NVM - I * VPM < VPM ? NVM - I * VPM : VPM, 0);
   if constexpr (I + 1 < NMFMA) interleave<I + 1, NMFMA, NDS, NVM>();
 }
 
@@ -215,7 +217,7 @@ k_gemm_i8(const int8_t* __restrict__ qa, const int8_t* __restrict__ qb, int M, i
   constexpr int SLOT = (BM + BN) * BK;          // bytes per LDS stage
   static_assert(LA >= 1 && LB >= 1 && LA * RPI * NW == BM && LB * RPI * NW == BN &&
                 FM >= 1 && FN >= 1 && KK % 2 == 0, "unsupported tile");
-  static_assert(NST >= 2 && (NST - 1) * L < 64, "unsupported pipeline depth");
+  static_assert(NST >= 2 && (NST - 1) * 2 * L < 64, "unsupported pipeline depth");  // vmcnt range
   __shared__ __attribute__((aligned(1024))) int8_t lds[NST * SLOT];
 
   const int tid = threadIdx.x;
@@ -247,24 +249,36 @@ k_gemm_i8(const int8_t* __restrict__ qa, const int8_t* __restrict__ qb, int M, i
 
   const int nk = (K + BK - 1) / BK;
 
-  // Issue this wave's LDS-mode loads of stage `st`.  A stage past the end
-  // (st >= nk) is issued with out-of-range offsets: it moves no data, keeps
-  // the per-stage load count constant (so one vmcnt value serves every
-  // iteration) and only touches a slot no later stage uses.
-  auto dma = [&](int st) {
+  // LDS-mode loads of stage `st`, numbered j = h * L + i: for h = 0 this
+  // wave's own loads (i < LA activations, then weights), for h = 1 those of
+  // wave + NW / 2, issued on its behalf (see the pipeline below).  Rows of
+  // wave + NW / 2 lie NW / 2 * RPI rows further down with the same chunk
+  // swizzle, so they differ only in the scalar offset.  Loads j0 <= j < j1
+  // are issued.  A stage past the end (st >= nk) is issued with out-of-range
+  // offsets: it moves no data, keeps every wave's per-stage load count
+  // constant (so fixed vmcnt values serve every iteration) and only touches
+  // the slot that the stage would have used, which no live stage occupies.
+  auto dma = [&](int st, int j0, int j1) {
     const int k0 = st * BK;
     int8_t* slot = lds + (st % NST) * SLOT;
 #pragma unroll
-    for (int i = 0; i < LA; ++i) {
-      const int vo = (k0 + kc_a[i] >= K) ? kOob : voff_a[i];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (lds_void_t*)(slot + (i * NW + wave) * 1024), 16, vo, k0, 0, 0);
-    }
+    for (int h = 0; h < 2; ++h) {
+      const int so = k0 + h * (NW / 2) * RPI * K;
+      const int w = wave + h * (NW / 2);
 #pragma unroll
-    for (int i = 0; i < LB; ++i) {
-      const int vo = (k0 + kc_b[i] >= K) ? kOob : voff_b[i];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rb, (lds_void_t*)(slot + BM * BK + (i * NW + wave) * 1024), 16, vo, k0, 0, 0);
+      for (int i = 0; i < LA; ++i) {
+        if (h * L + i < j0 || h * L + i >= j1) continue;
+        const int vo = (k0 + kc_a[i] >= K) ? kOob : voff_a[i];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, (lds_void_t*)(slot + (i * NW + w) * 1024), 16, vo, so, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < LB; ++i) {
+        if (h * L + LA + i < j0 || h * L + LA + i >= j1) continue;
+        const int vo = (k0 + kc_b[i] >= K) ? kOob : voff_b[i];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, (lds_void_t*)(slot + BM * BK + (i * NW + w) * 1024), 16, vo, so, 0, 0);
+      }
     }
   };
 
@@ -304,47 +318,82 @@ k_gemm_i8(const int8_t* __restrict__ qa, const int8_t* __restrict__ qb, int M, i
   };
 
   // Pipeline (stage s lives in slot s % NST).  Iteration kt computes stage kt
-  // as KK steps of 32-deep k; the fragments of step kk+1 are read while the
-  // MFMAs of step kk run.  Before the last step the stage barrier is taken:
-  // each wave first waits for its own loads of stage kt+1 (stages kt+2 ..
-  // kt+NST-1 may stay in flight) and for its own reads of slot kt, so after
-  // the barrier stage kt+1 is visible and slot kt is free; the loads of stage
-  // kt+NST go into it while the last step's MFMAs run and the next stage's
-  // first fragments are read.
+  // as KK steps of 32-deep k (64-deep for FP8); the fragments of step kk+1 are
+  // read while the MFMAs of step kk run.  Before the last step the stage
+  // barrier is taken: each wave first waits for its own loads of stage kt+1
+  // and for its own reads of slot kt, so after the barrier stage kt+1 is
+  // visible to every wave and slot kt is free.
+  //
+  // Where the loads go matters because a SIMD whose two waves both have
+  // loads waiting to issue leaves its matrix pipe idle (measured: the MFMA
+  // rate with a stage of loads in flight is that of MFMAs alone only when one
+  // of the two waves per SIMD issues all of them).  So:
+  //  - NST >= 3: the loads of stage kt+NST-1 go into the slot freed at the
+  //    previous barrier, spread over the first KK-1 steps of iteration kt,
+  //    PER per step, each wave its own; NST-2 stages stay in flight.
+  //  - NST == 2 with 8 waves: the loads of stage kt+2 go into slot kt right
+  //    after the barrier, all issued by waves 0..3 (one per SIMD), each its
+  //    own and those of wave + 4, while waves 4..7 only compute.
+  //  - NST == 2 with 4 waves: each wave issues its own after the barrier.
+  constexpr bool kSpread = NST >= 3;
+  constexpr bool kHalf = !kSpread && NW == 8;
+  constexpr int LW = kHalf ? 2 * L : L;              // loads per stage of a loading wave
+  constexpr int PER = (LW + KK - 2) / (KK - 1);      // loads per step when spread
+  static_assert(KK >= 2, "unsupported stage depth");
+  static_assert(!kHalf || ((NW / 2) * RPI / RPW) % CPR == 0, "half-wave load swizzle");
+  const bool loader = !kHalf || wave < NW / 2;
+  auto step_ptrs = [&](int kk, v4i*& cb, v4i*& ca, v4i*& nb, v4i*& na) {
+    cb = (kk & 1) ? fb1 : fb0;
+    ca = (kk & 1) ? fa1 : fa0;
+    nb = (kk & 1) ? fb0 : fb1;
+    na = (kk & 1) ? fa0 : fa1;
+  };
   if (nk > 0) {
+    // prologue: the stages in flight before iteration 0
+    constexpr int PRE = kSpread ? NST - 1 : NST;
+    if (loader) {
 #pragma unroll
-    for (int st = 0; st < NST; ++st) dma(st);
-    wait_vmcnt<(NST - 1) * L>();  // stage 0 landed
+      for (int st = 0; st < PRE; ++st) dma(st, 0, LW);
+    }
+    wait_vmcnt<(PRE - 1) * LW>();  // stage 0 landed
     block_barrier();
     read_frags(0, 0, fb0, fa0);
     for (int kt = 0; kt < nk - 1; ++kt) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        v4i* cb = (kk & 1) ? fb1 : fb0;
-        v4i* ca = (kk & 1) ? fa1 : fa0;
-        v4i* nb = (kk & 1) ? fb0 : fb1;
-        v4i* na = (kk & 1) ? fa0 : fa1;
+        v4i *cb, *ca, *nb, *na;
+        step_ptrs(kk, cb, ca, nb, na);
         if (kk + 1 < KK) {
           read_frags(kt, kk + 1, nb, na);
-          mfmas(cb, ca);
-          interleave<0, FN * FM, FR * (FN + FM), 0>();
+          if constexpr (kSpread) {
+            dma(kt + NST - 1, kk * PER, min((kk + 1) * PER, LW));
+            mfmas(cb, ca);
+            interleave<0, FN * FM, FR * (FN + FM), PER>();
+          } else {
+            mfmas(cb, ca);
+            interleave<0, FN * FM, FR * (FN + FM), 0>();
+          }
         } else {
-          wait_vmcnt<(NST - 2) * L>();  // stage kt+1 landed
-          wait_lgkmcnt0();              // this wave's reads of slot kt are done
-          block_barrier();              // every wave: stage kt+1 landed, slot kt free
-          dma(kt + NST);
-          read_frags(kt + 1, 0, nb, na);
-          mfmas(cb, ca);
-          interleave<0, FN * FM, FR * (FN + FM), L>();
+          wait_vmcnt<(NST - 2) * LW>();  // this wave's loads of stage kt+1 landed
+          wait_lgkmcnt0();               // this wave's reads of slot kt are done
+          block_barrier();               // every wave: stage kt+1 landed, slot kt free
+          if (!kSpread && loader) {
+            dma(kt + NST, 0, LW);
+            read_frags(kt + 1, 0, nb, na);
+            mfmas(cb, ca);
+            interleave<0, FN * FM, FR * (FN + FM), LW>();
+          } else {
+            read_frags(kt + 1, 0, nb, na);
+            mfmas(cb, ca);
+            interleave<0, FN * FM, FR * (FN + FM), 0>();
+          }
         }
       }
     }
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      v4i* cb = (kk & 1) ? fb1 : fb0;
-      v4i* ca = (kk & 1) ? fa1 : fa0;
-      v4i* nb = (kk & 1) ? fb0 : fb1;
-      v4i* na = (kk & 1) ? fa0 : fa1;
+      v4i *cb, *ca, *nb, *na;
+      step_ptrs(kk, cb, ca, nb, na);
       if (kk + 1 < KK) read_frags(nk - 1, kk + 1, nb, na);
       mfmas(cb, ca);
     }
