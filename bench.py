@@ -16,7 +16,9 @@ dense fp16 product of each layer (same tiling on the 16-bit matrix cores) to
 state the W8A8-vs-FP16 speedup at kernel level.  The roofline object reports the GEMM
 kernel (the dominant kernel) against the dense INT8 MFMA peak, with its
 average launch duration taken from HIP events recorded around every GEMM
-launch inside the timed region.  cpu_baseline times the CPU oracle on the
+launch of every fourth timed step (--event-every), created without the
+system-scope fence; each event pair still idles the GPU for a few
+microseconds, so the other timed steps carry none.  cpu_baseline times the CPU oracle on the
 host cores over one step of the same workload.
 
 python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
@@ -50,6 +52,9 @@ def parse():
     ap.add_argument("--workload", default="llama2_7b_prefill")
     ap.add_argument("--alpha", type=float, default=0.5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--event-every", type=int, default=4,
+                    help="record the GEMM timing events on every N-th timed step (each event pair "
+                         "costs the step a few microseconds of idle GPU)")
     ap.add_argument("--kernel-reps", type=int, default=20,
                     help="repetitions per kernel in the per-kernel breakdown pass")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -88,6 +93,66 @@ def pmc_traffic(workload: str, kernel: str = "gemm_i8"):
         return float(vals["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+class TimingEvents:
+    """HIP events for timing kernels on torch's current stream, created with
+    hipEventDisableSystemFence.  A default event's record carries a
+    system-scope release: cache write-back and invalidation at every record,
+    which on this GPU holds back the next kernel by about 6 us.  These events
+    only time (no host code reads memory through them), so they drop it."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+
+        import torch
+
+        torch.cuda.init()
+        path = None
+        with open("/proc/self/maps") as f:  # the HIP runtime torch already uses
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("HIP runtime not loaded")
+        self.hip = ctypes.CDLL(path)
+        self.ct = ctypes
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.torch = torch
+
+    def create(self):
+        ev = self.ct.c_void_p()
+        rc = self.hip.hipEventCreateWithFlags(self.ct.byref(ev), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags: {rc}")
+        return _Event(self, ev)
+
+
+class _Event:
+    def __init__(self, owner, handle):
+        self.o, self.h = owner, handle
+
+    def record(self):
+        rc = self.o.hip.hipEventRecord(self.h, self.o.torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord: {rc}")
+
+    def elapsed_time(self, end):
+        ms = self.o.ct.c_float()
+        rc = self.o.hip.hipEventElapsedTime(self.o.ct.byref(ms), self.h, end.h)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime: {rc}")
+        return ms.value
+
+    def destroy(self):
+        self.o.hip.hipEventDestroy(self.h)
 
 
 class Layer:
@@ -129,9 +194,10 @@ class Layer:
         return float(M * self.K + self.N * self.K + 2 * M * self.N + 4 * (M + self.N))
 
     def step(self, i, ev=None):
+        """One pass of the path for this layer; amax_w must be zero on entry
+        (run_step zeroes every layer's at once)."""
         w8 = self.w8
         w8.channel_amax(self.cal[i % len(self.cal)], self.amax_x)
-        self.amax_w.zero_()
         w8.channel_amax(self.w, self.amax_w)
         w8.smooth_factors(self.amax_x, self.amax_w, self.alpha, self.s, self.inv_s)
         w8.scale_quant_rows(self.w, self.s, self.qw, self.sw)
@@ -329,24 +395,36 @@ def main():
         torch.cuda.synchronize()
         del src
     layers = [Layer(wl, li, n_batches, args.alpha, dev) for li in range(len(wl.layers))]
+    # every layer's weight amax in one buffer, zeroed once per step
+    amax_w_all = torch.zeros(sum(L.K for L in layers), dtype=torch.float32, device=dev)
+    off = 0
+    for L in layers:
+        L.amax_w = amax_w_all[off:off + L.K]
+        off += L.K
+
+    def run_step(i, evs_row=None):
+        amax_w_all.zero_()
+        for li, L in enumerate(layers):
+            L.step(i, None if evs_row is None else evs_row[li])
+
     torch.cuda.synchronize()
     print(f"[bench] {wl.name}: {len(layers)} layers, M={wl.M[0]}, buffers ready", file=sys.stderr,
           flush=True)
 
     step_i = 0
     for _ in range(args.warmup):
-        for L in layers:
-            L.step(step_i)
+        run_step(step_i)
         step_i += 1
     torch.cuda.synchronize()
 
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in layers] for _ in range(args.steps)]
+    te = TimingEvents()
+    every = max(1, args.event_every)
+    ev_steps = [k for k in range(args.steps) if k % every == 0]
+    evs = {k: [(te.create(), te.create()) for _ in layers] for k in ev_steps}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        for L, ev in zip(layers, evs[k]):
-            L.step(step_i, ev)
+        run_step(step_i, evs.get(k))
         step_i += 1
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -355,7 +433,11 @@ def main():
     ops_per_step = sum(L.gemm_ops() for L in layers)
     value = ops_per_step / (elapsed / args.steps) / 1e12
 
-    gemm_s = [sum(a.elapsed_time(b) for a, b in row) * 1e-3 for row in evs]
+    gemm_s = [sum(a.elapsed_time(b) for a, b in row) * 1e-3 for row in evs.values()]
+    for row in evs.values():
+        for a, b in row:
+            a.destroy()
+            b.destroy()
     gemm_launch_avg = sum(gemm_s) / (len(gemm_s) * len(layers))
     ops_per_launch = ops_per_step / len(layers)
     achieved = ops_per_launch / gemm_launch_avg / 1e12
@@ -401,6 +483,7 @@ def main():
             "traffic": traffic,
             "ops_per_launch": ops_per_launch,
             "avg_launch_us": round(gemm_launch_avg * 1e6, 3),
+            "event_steps": len(ev_steps),
         } if not decode else {
             "kernel": "gemm_dequant (k_gemm_skinny)",
             "bound": "hbm",
@@ -411,6 +494,7 @@ def main():
             "traffic": pmc_traffic(wl.name, "gemm_skinny"),
             "bytes_per_launch": bytes_per_launch,
             "avg_launch_us": round(gemm_launch_avg * 1e6, 3),
+            "event_steps": len(ev_steps),
         },
         "kernels": kernels,
     }
