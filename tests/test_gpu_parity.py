@@ -205,6 +205,45 @@ def test_gemm_dequant(out, M, N, K):
     assert_y_close(np_bits(y), y_or, name)
 
 
+def _tile_of_shape(M, N):
+    """The tiled kernel's tile choice for an M x N output (restated from the
+    launcher: fullest last wave of blocks over 256 CUs, times the useful
+    fraction of padded token rows, times a per-tile preference)."""
+    best, best_score = None, -1.0
+    for bm, bn, eff in ((256, 256, 1.0), (256, 128, 0.92), (128, 128, 0.8), (256, 192, 0.96)):
+        tiles = -(-M // bm) * -(-N // bn)
+        fill = tiles / (-(-tiles // 256) * 256)
+        score = fill * (M / (-(-M // bm) * bm)) * eff
+        if score > best_score + 1e-9:
+            best, best_score = (bm, bn), score
+    return best
+
+
+@pytest.mark.parametrize("M,N,K,tile", [(2000, 22000, 272, (256, 256)), (2000, 12280, 272, (256, 192)),
+                                        (2000, 4088, 1040, (256, 128)), (130, 1000, 1040, (128, 128))])
+def test_gemm_tiles_ragged(M, N, K, tile):
+    """Each tile of the tiled kernel with a partial last tile in M and in N and
+    a K that ends inside a 128-byte stage.  With the 256-row tiles, waves 0-3
+    load the rows of waves 4-7 as well, so the rows checked include both
+    halves of the first tile and the ragged last tile rows.  C is checked in
+    full (Freivalds) and exactly on those rows; Y on the same rows."""
+    assert _tile_of_shape(M, N) == tile
+    qa, qb = rand_codes(M, K, M + 3 * K), rand_codes(N, K, N + K + 7)
+    c = host(w8.gemm_i32(qa, qb))
+    qa_h, qb_h = host(qa), host(qb)
+    assert_freivalds(c, qa_h, qb_h, seed=M + N)
+    rows = np.array(sorted(set(range(0, 64)) | set(range(M - 40, M)) | set(_sample_rows(M, 16).tolist())))
+    c_or = oracle.gemm_i32(qa_h[rows], qb_h)
+    assert np.array_equal(c[rows], c_or)
+    g = torch.Generator(device="cpu").manual_seed(M + K)
+    sa = (torch.rand(M, generator=g) * 0.05 + 1e-3).to(DEV)
+    sb = (torch.rand(N, generator=g) * 2e-4 + 1e-5).to(DEV)
+    for out, name in ((torch.float16, "f16"), (torch.bfloat16, "bf16")):
+        y = np_bits(w8.gemm_dequant(qa, sa, qb, sb, out))
+        y_or = oracle.dequant(c_or, host(sa)[rows], host(sb), name)
+        assert_y_close(y[rows], y_or, name)
+
+
 # ------------------------------------------------------ end to end, tiny
 
 
