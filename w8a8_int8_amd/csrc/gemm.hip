@@ -13,8 +13,9 @@
 // as its first operand (32 output channels x 32 k) and the activation
 // fragment as its second (32 k x 32 tokens), so that each lane's four
 // consecutive accumulator registers hold four consecutive output channels of
-// one token: the epilogue writes 4 fp16 / bf16 (8 B) or 4 int32 (16 B) per
-// lane per register group.  Integer accumulation is exact and order free.
+// one token.  Integer accumulation is exact and order free.  The epilogue
+// dequantizes in registers and restages each wave's results through LDS so
+// that every global store writes whole rows of 16 bytes per lane.
 //
 // Block: WGM x WGN waves (8 for the 256-row tiles, 4 for 128 x 128) own a
 // BM x BN output tile (tokens x channels); wave (wm, wn) holds a
@@ -28,12 +29,15 @@
 // operand row) through NST LDS slots (2 to 4, as many as 160 KB of LDS holds
 // for the tile).  Operand rows go from global memory straight into LDS with
 // buffer loads in LDS mode (16 B per lane, each wave instruction fills 1 KiB
-// of LDS); the prologue fills all NST slots and every stage barrier refills
-// the slot just consumed with the stage NST ahead, so up to NST - 1 stages are
-// in flight while one is computed and a wave never holds global data in
-// registers.  Stages past the end are issued with out-of-range offsets (no
-// memory traffic) so the per-stage load count, and with it every vmcnt wait,
-// is constant.  Per stage a wave runs BK / 32 k steps (BK / 64 for FP8, whose
+// of LDS), NST - 1 or NST - 2 stages in flight while one is computed, and a
+// wave never holds global data in registers.  Which waves issue a stage's
+// loads, and when, is set by the slot count (see the pipeline in the kernel):
+// a SIMD stalls its matrix pipe while both of its waves have loads waiting to
+// issue, so with two slots one wave per SIMD issues them all.  Stages past the
+// end are issued with out-of-range offsets (no memory traffic) so the
+// per-stage load count, and with it every vmcnt wait, is constant.
+//
+// Per stage a wave runs BK / 32 k steps (BK / 64 for FP8, whose
 // MFMA takes 64 bytes of K) of (BM / WGM / 32) x (BN / WGN / 32) MFMAs.  The
 // fragment reads are software pipelined: the next k step's fragments are read
 // while the current step's MFMAs run, and the next stage's first fragments
