@@ -814,17 +814,12 @@ hipError_t launch_gemm(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N,
     const double score = fill * mfill * cands[i].eff;
     if (score > best_score + 1e-9) { best_score = score; best = i; }
   }
-#ifndef GEMM_W256
-#define GEMM_W256 128, 2, 2, 4
-#define GEMM_W256x192 128, 2, 4, 2
-#define GEMM_W256x128 128, 3, 4, 2
-#define GEMM_W128 128, 4, 2, 2
-#endif
+  // template arguments after the tile: stage bytes BK, LDS slots NST, waves WGM x WGN
   switch (best) {
-    case 0: return launch_tile<256, 256, GEMM_W256>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
-    case 1: return launch_tile<256, 128, GEMM_W256x128>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
-    case 3: return launch_tile<256, 192, GEMM_W256x192>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
-    default: return launch_tile<128, 128, GEMM_W128>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
+    case 0: return launch_tile<256, 256, 128, 2, 2, 4>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
+    case 1: return launch_tile<256, 128, 128, 3, 4, 2>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
+    case 3: return launch_tile<256, 192, 128, 2, 4, 2>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
+    default: return launch_tile<128, 128, 128, 4, 2, 2>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
   }
 }
 
