@@ -11,3 +11,4 @@ from .smoothquant import (QMAX, apply_col_scale, channel_amax, dequant, gemm_flo
 from .smoothquant import (E4M3_MAX, e4m3_to_float, e4m3_value, gemm_e4m3,
                           quantize_rows_e4m3, round_to_e4m3, scale_quant_rows_e4m3)
 from .smoothquant import fold_norm_weight, rms_inv, rmsnorm_fp64, rmsnorm_smooth_quant_rows
+from .smoothquant import layernorm_fp64, layernorm_smooth_quant_rows, layernorm_stats

@@ -403,6 +403,78 @@ def rmsnorm_smooth_quant_rows(x, dtype: str, g, eps: float):
     return q, delta
 
 
+# --------------------------------- smoothing folded into a LayerNorm
+#
+# The same fold for the LayerNorm in front of the projections of OPT-family
+# decoders: y = (x - mean) / sqrt(var + eps) * gamma + beta, so
+# y * inv_s = (x - mean) r * RN32(gamma * inv_s) + RN32(beta * inv_s).  The
+# additive term keeps the row statistics inside every element, so here they
+# enter the codes.  Reading taken (the page gives no normalisation at all):
+# the statistics are the exact mean and population variance of the fp16 row,
+# each rounded once per the steps below, so that they do not depend on a
+# summation order; the rest is one IEEE fp32 operation per step.  fp16 input
+# only: every fp16 value is an integer multiple of 2^-24, so the row sums are
+# exact integers.
+
+
+def layernorm_stats(x, eps: float):
+    """Row statistics of the LayerNorm fold: (mean float32[rows], r float32[rows]).
+
+    With X_j = x_j * 2^24 (an integer for every finite fp16 value), K = cols,
+    S1 = sum X_j and S2 = sum X_j^2 (exact integers):
+      mean = f32(f64(f64(S1) / (K * 2^24)))
+      var  = f32(f64(f64(K * S2 - S1^2) / (K^2 * 2^48)))      (population variance)
+      t    = RN32(var + eps);  r = RN32(1 / RN32(sqrt(t))), or r = 0 when t = 0
+    where f64() is the correctly rounded conversion to double and f32() to
+    float (each to nearest even).  Rows must have K >= 1.
+    Pinned by test_layernorm_stats_* (exact rationals, closed forms).
+    """
+    assert x.dtype == np.float16 and x.ndim == 2 and x.shape[1] >= 1
+    rows, K = x.shape
+    X = (x.astype(np.float64) * float(1 << 24)).astype(np.int64)  # exact: |X| < 2^41
+    eps32 = np.float32(eps)
+    mean = np.zeros(rows, dtype=np.float32)
+    r = np.zeros(rows, dtype=np.float32)
+    for t in range(rows):
+        xt = [int(v) for v in X[t]]
+        s1 = sum(xt)
+        s2 = sum(v * v for v in xt)
+        mean[t] = np.float32(float(s1) / float(K << 24))
+        var = np.float32(float(K * s2 - s1 * s1) / float((K * K) << 48))
+        tt = np.float32(var + eps32)
+        if tt > 0:
+            r[t] = np.float32(1.0) / np.sqrt(tt)
+    return mean, r
+
+
+def layernorm_smooth_quant_rows(x, g, b, eps: float):
+    """Per-token INT8 of LayerNorm(x; gamma, beta) * inv_s, given the folded
+    g = RN32(gamma * inv_s) and b = RN32(beta * inv_s) (fold_norm_weight of
+    each).  Per element v_j = RN32(RN32(RN32(RN32(x_j - mean) * r) * g_j) + b_j),
+    left to right, no fused multiply-add; then quantize_rows(v).
+    Returns (q int8[rows, cols], delta float32[rows]).
+    Pinned by test_layernorm_quant_* (shift, scale and sign invariances,
+    closed forms, the plain fp64 definition within the quantization bound).
+    """
+    mean, r = layernorm_stats(x, eps)
+    x32 = x.astype(np.float32)
+    d = (x32 - mean[:, None]).astype(np.float32)
+    v = (d * r[:, None]).astype(np.float32)
+    v = (v * np.asarray(g, np.float32)[None, :]).astype(np.float32)
+    v = (v + np.asarray(b, np.float32)[None, :]).astype(np.float32)
+    return quantize_rows(v)
+
+
+def layernorm_fp64(x, gamma, beta, eps: float) -> np.ndarray:
+    """The plain LayerNorm (x - mean) / sqrt(var + eps) * gamma + beta in fp64,
+    with numpy's mean and population variance."""
+    x64 = x.astype(np.float64)
+    mu = x64.mean(axis=1, keepdims=True)
+    var = ((x64 - mu) ** 2).mean(axis=1, keepdims=True)
+    return (x64 - mu) / np.sqrt(var + eps) * np.asarray(gamma, np.float64)[None, :] + \
+        np.asarray(beta, np.float64)[None, :]
+
+
 # ------------------------------------------------------ composed flows
 
 

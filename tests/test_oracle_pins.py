@@ -542,3 +542,110 @@ def test_rmsnorm_quant_scale_invariance_and_zero_row():
     # the codes are those of the smoothing quantizer with the folded weight
     qs, ds = oracle.scale_quant_rows(x, "f16", (gamma * inv_s).astype(np.float32))
     assert np.array_equal(q1, qs)
+
+
+# -------------------------------------------- smoothing folded into a LayerNorm
+
+
+def _ln_rows(rows, cols, seed, shift=0.0):
+    g = np.random.default_rng(seed)
+    x = g.standard_normal((rows, cols)) * np.exp(g.uniform(-4, 4, (rows, 1))) + shift
+    x[:, g.choice(cols, 2, replace=False)] *= 40.0  # outlier channels
+    return np.clip(x, -60000, 60000).astype(np.float16)
+
+
+def test_layernorm_stats_exact_rationals():
+    """Mean and population variance against exact rationals from the textbook
+    two-pass form (sum of (x - mean)^2), a different route from the oracle's
+    K S2 - S1^2.  Where the integer sums stay below 2^53 the oracle's steps
+    round exactly once to fp64, so the fp32 results are those of the exact
+    values rounded to fp64 then to fp32."""
+    x = _ln_rows(12, 48, 3, shift=5.0)
+    x[0, :4] = np.float16(6e-8)  # subnormals
+    x[1] = np.float16(65504.0) * np.array([1, -1] * 24, np.float16)
+    mean, r = oracle.layernorm_stats(x, 0.0)
+    for t in range(x.shape[0]):
+        xs = [F(float(v)) for v in x[t]]
+        mu = sum(xs) / 48
+        var = sum((v - mu) ** 2 for v in xs) / 48
+        assert mean[t] == np.float32(float(mu)), t
+        var32 = np.float32(float(var))
+        want_r = np.float32(0.0) if var32 == 0 else np.float32(1.0) / np.sqrt(var32)
+        assert r[t] == want_r, t
+
+
+def test_layernorm_stats_closed_forms():
+    x = np.array([[2.0, -2.0] * 8, [3.0, 5.0] * 8, [7.0] * 16, [0.0] * 16,
+                  [-1.5, -0.5] * 8], np.float16)
+    mean, r = oracle.layernorm_stats(x, 0.0)
+    assert list(mean) == [0.0, 4.0, 7.0, 0.0, -1.0]
+    assert list(r) == [0.5, 1.0, 0.0, 0.0, 2.0]
+    mean, r = oracle.layernorm_stats(x, 0.25)
+    assert r[2] == 2.0 and r[3] == 2.0 and r[1] == np.float32(1.0) / np.sqrt(np.float32(1.25))
+
+
+def _ln_fold(cols, seed):
+    g = np.random.default_rng(seed)
+    gamma = g.uniform(0.2, 2.0, cols).astype(np.float32)
+    beta = g.uniform(-0.5, 0.5, cols).astype(np.float32)
+    inv_s = np.exp(g.uniform(-4, 2, cols)).astype(np.float32)
+    return gamma, beta, inv_s
+
+
+def test_layernorm_quant_matches_plain_definition():
+    """Dequantized codes against the plain fp64 LayerNorm(x; gamma, beta) *
+    inv_s: within half a quantization step plus the fp32 roundings of the
+    statistics and of each elementwise step."""
+    x = _ln_rows(20, 96, 11, shift=2.0)
+    gamma, beta, inv_s = _ln_fold(96, 12)
+    g, b = oracle.fold_norm_weight(gamma, inv_s), oracle.fold_norm_weight(beta, inv_s)
+    for eps in (0.0, 1e-5, 2.0):
+        q, delta = oracle.layernorm_smooth_quant_rows(x, g, b, eps)
+        plain = oracle.layernorm_fp64(x, gamma, beta, eps) * inv_s.astype(np.float64)[None, :]
+        deq = q.astype(np.float64) * delta.astype(np.float64)[:, None]
+        x64 = x.astype(np.float64)
+        mu = np.abs(x64.mean(axis=1, keepdims=True))
+        rg = np.abs(plain - beta.astype(np.float64)[None, :] * inv_s[None, :]) / np.maximum(
+            np.abs(x64 - x64.mean(axis=1, keepdims=True)), 1e-300)
+        tol = (delta.astype(np.float64)[:, None] / 2 * (1 + 2.0 ** -13)
+               + ((np.abs(x64) + mu) * rg + np.abs(b)[None, :]) * 2.0 ** -20)
+        assert (np.abs(deq - plain) <= tol).all(), eps
+        assert (np.abs(q).max(axis=1) == 127).all()
+
+
+def test_layernorm_quant_shift_scale_sign_invariance():
+    """LayerNorm ignores a shift of the row and, with eps = 0, a positive
+    scale; a sign flip negates (x - mean).  Shifts by an integer of rows whose
+    mean is an integer, and scales by 4, are exact in fp16 and in the
+    statistics, so the codes and the row scales must not change at all."""
+    g0 = np.random.default_rng(21)
+    half = g0.integers(-40, 41, (8, 32)).astype(np.float64)
+    x = np.concatenate([half, -half], axis=1) + g0.integers(-20, 21, (8, 1))  # integer means
+    x = x.astype(np.float16)
+    gamma, beta, inv_s = _ln_fold(64, 22)
+    g, b = oracle.fold_norm_weight(gamma, inv_s), oracle.fold_norm_weight(beta, inv_s)
+    q0, d0 = oracle.layernorm_smooth_quant_rows(x, g, b, 1e-3)
+    q1, d1 = oracle.layernorm_smooth_quant_rows((x.astype(np.float32) + 13).astype(np.float16), g, b, 1e-3)
+    assert np.array_equal(q0, q1) and np.array_equal(d0, d1)
+    y = _ln_rows(8, 64, 23)
+    q2, d2 = oracle.layernorm_smooth_quant_rows(y, g, b, 0.0)
+    q3, d3 = oracle.layernorm_smooth_quant_rows((y.astype(np.float32) * 4).astype(np.float16), g, b, 0.0)
+    assert np.array_equal(q2, q3) and np.array_equal(d2, d3)
+    zero = np.zeros(64, np.float32)
+    q4, d4 = oracle.layernorm_smooth_quant_rows(y, g, zero, 0.5)
+    q5, d5 = oracle.layernorm_smooth_quant_rows(-y, g, zero, 0.5)
+    assert np.array_equal(q4, -q5) and np.array_equal(d4, d5)
+
+
+def test_layernorm_quant_constant_row_is_the_bias():
+    """A constant row has x - mean = 0, so v = b and the codes are those of
+    the folded bias alone (zero codes when b = 0)."""
+    x = np.full((3, 32), 3.25, np.float16)
+    gamma, beta, inv_s = _ln_fold(32, 31)
+    g, b = oracle.fold_norm_weight(gamma, inv_s), oracle.fold_norm_weight(beta, inv_s)
+    for eps in (0.0, 1e-5):
+        q, d = oracle.layernorm_smooth_quant_rows(x, g, b, eps)
+        qb, db = oracle.quantize_rows(np.tile(b, (3, 1)))
+        assert np.array_equal(q, qb) and np.array_equal(d, db)
+        q, d = oracle.layernorm_smooth_quant_rows(x, g, np.zeros(32, np.float32), eps)
+        assert not q.any() and not d.any()
