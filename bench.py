@@ -276,6 +276,11 @@ def kernel_breakdown(layers, reps):
         g = w8.fold_norm_weight(torch.ones(L.K, dtype=torch.float32, device=L.x.device), L.inv_s)
         t = timed(lambda i: w8.rmsnorm_quant_rows(xs[i % nx], g, 1e-5, L.qx, L.sx), reps)
         d["rmsnorm_smooth_quant_act"] = hbm(t, L.x.numel() * 3 + 4 * (L.M + L.K))
+        if L.x.dtype == torch.float16:
+            # the same fold into a LayerNorm (OPT-family decoders), fp16 only
+            b = w8.fold_norm_weight(torch.zeros(L.K, dtype=torch.float32, device=L.x.device), L.inv_s)
+            t = timed(lambda i: w8.layernorm_quant_rows(xs[i % nx], g, b, 1e-5, L.qx, L.sx), reps)
+            d["layernorm_smooth_quant_act"] = hbm(t, L.x.numel() * 3 + 4 * (L.M + 2 * L.K))
         # FP8 (E4M3) form of the same layer: codes from the same smoothed tensors
         qw8, sw8 = w8.scale_quant_rows_e4m3(L.w, L.s)
         qx8, sx8 = w8.scale_quant_rows_e4m3(L.x, L.inv_s)

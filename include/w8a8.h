@@ -14,6 +14,7 @@
  *   3. X diag(s)^-1 and per-token INT8 quantization    w8a8_scale_quant_rows
  *      ... folded into the RMS norm that produces X     w8a8_fold_norm_weight (offline)
  *                                                       + w8a8_rmsnorm_quant_rows
+ *      ... or into a LayerNorm (fp16)                   w8a8_layernorm_quant_rows
  *   4. INT8 x INT8 -> INT32 product                    w8a8_gemm_i32 (diagnostic)
  *   5. dequantize with per-token x per-channel scales  w8a8_gemm_dequant (fuses 4+5)
  *   runtime forward = 3 + 4 + 5                         w8a8_linear
@@ -53,7 +54,7 @@
 extern "C" {
 #endif
 
-#define W8A8_ABI_VERSION 2
+#define W8A8_ABI_VERSION 3
 
 /* Largest K for which 127 * 127 * K fits int32, so that every accumulator
  * (and every partial sum) of the INT8 product is exact in int32. */
@@ -177,6 +178,37 @@ w8a8_status_t w8a8_fold_norm_weight(const float* gamma, const float* inv_s, int6
 w8a8_status_t w8a8_rmsnorm_quant_rows(const void* h, int dtype, int64_t rows, int64_t cols,
                                       const float* g, float eps, int8_t* q, float* row_scale,
                                       hipStream_t stream);
+
+/*
+ * The same fold for a LayerNorm (the norm in front of the projections of
+ * OPT-family decoders), y = (x - mean) / sqrt(var + eps) * gamma + beta:
+ * y * inv_s = (x - mean) r g + b with g = RN32(gamma * inv_s) and
+ * b = RN32(beta * inv_s), both from w8a8_fold_norm_weight.  The pages give no
+ * normalisation; the fold extends their X diag(s)^-1 (section
+ * "平滑化変換の数学").  The additive b keeps the row statistics in every
+ * element, so they are defined without a summation order: every fp16 value
+ * is an integer multiple of 2^-24, and with X = x * 2^24, K = cols,
+ * S1 = sum X and S2 = sum X^2 (exact integers),
+ *   mean = f32(f64(f64(S1) / (K * 2^24)))
+ *   var  = f32(f64(f64(K * S2 - S1^2) / (K^2 * 2^48)))   (population variance)
+ *   r    = 1 / sqrt(var + eps) in fp32 (each step one rounding), 0 when var + eps == 0
+ *   v_j  = ((x[t, j] - mean) * r) * g[j] + b[j]           (fp32, left to right)
+ * where f64() / f32() round to nearest even.  Then the per-row quantizer of
+ * w8a8_scale_quant_rows on v: codes and row_scale = m / 127.  Results are
+ * bit-reproducible.  One pass over x; y is never written.
+ *
+ *   x          [rows x cols] fp16 (dtype must be W8A8_F16; bf16's exponent
+ *              range does not allow exact integer sums), 16-byte aligned.
+ *   g, b       [cols] fp32 folded weight and bias, 16-byte aligned.
+ *   eps        finite, >= 0.
+ *   q, row_scale  outputs as in w8a8_scale_quant_rows.
+ *   rows >= 0, cols % 16 == 0, cols <= 65536, cols >= 16 when rows > 0.
+ * Errors: NULL, SHAPE, ALIGN, DTYPE (bf16 or unknown), ARG (eps negative, NaN or
+ * infinite), HIP.
+ */
+w8a8_status_t w8a8_layernorm_quant_rows(const void* x, int dtype, int64_t rows, int64_t cols,
+                                        const float* g, const float* b, float eps, int8_t* q,
+                                        float* row_scale, hipStream_t stream);
 
 /*
  * Step 4 alone (a diagnostic / test entry point): C = qa qb^T in exact int32.

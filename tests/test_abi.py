@@ -36,11 +36,11 @@ def declared_symbols():
 def test_library_loads_and_exports_header_symbols():
     lib = _lib.load()
     syms = declared_symbols()
-    assert len(syms) == 14
+    assert len(syms) == 15
     for s in syms:
         assert hasattr(lib, s), s
         assert s in _lib.PROTOTYPES, s
-    assert lib.w8a8_abi_version() == 2
+    assert lib.w8a8_abi_version() == 3
 
 
 def test_status_strings():
@@ -194,3 +194,20 @@ def test_rmsnorm_quant_rows_rejects():
     assert fold(P, P, -1, P, 0) == ESHAPE
     assert fold(P, P, 8, P + 2, 0) == EALIGN
     assert fold(0, 0, 0, 0, 0) == OK
+
+
+@cpu_only
+def test_layernorm_quant_rows_rejects():
+    lib = _lib.load()
+    f = lib.w8a8_layernorm_quant_rows
+    assert f(P, 0, 4, 16, P, 0, 1e-5, P, P, 0) == ENULL  # b
+    assert f(P, 0, 4, 16, 0, P, 1e-5, P, P, 0) == ENULL  # g
+    assert f(P, 1, 4, 16, P, P, 1e-5, P, P, 0) == EDTYPE  # bf16: no exact row sums
+    assert f(P, 3, 4, 16, P, P, 1e-5, P, P, 0) == EDTYPE
+    assert f(P, 0, 4, 24, P, P, 1e-5, P, P, 0) == ESHAPE
+    assert f(P, 0, 4, 0, P, P, 1e-5, P, P, 0) == ESHAPE  # empty rows have no mean
+    assert f(P, 0, 4, 65552, P, P, 1e-5, P, P, 0) == ESHAPE
+    assert f(P, 0, 4, 16, P, PODD, 1e-5, P, P, 0) == EALIGN
+    assert f(P, 0, 4, 16, P, P, -1e-5, P, P, 0) == EARG
+    assert f(P, 0, 4, 16, P, P, float("nan"), P, P, 0) == EARG
+    assert f(0, 0, 0, 16, P, P, 1e-5, 0, 0, 0) == OK  # no rows: no launch

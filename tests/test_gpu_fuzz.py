@@ -156,6 +156,28 @@ def test_fuzz_rmsnorm_quant(case):
 
 
 @pytest.mark.parametrize("case", range(12))
+def test_fuzz_layernorm_quant(case):
+    """LayerNorm fold: codes and row scales bit for bit, random shapes, row
+    offsets up to 10^3 and eps."""
+    rng = np.random.default_rng(5500 + case)
+    rows = int(rng.choice([1, int(rng.integers(2, 120))]))
+    cols = 16 * int(rng.integers(1, 300))
+    x = rand_x(rng, rows, cols, torch.float16)
+    x = (x.float() + torch.from_numpy(rng.uniform(-1e3, 1e3, (rows, 1)).astype(np.float32)).to(DEV)).half()
+    gamma = torch.from_numpy(rng.uniform(0.1, 3.0, cols).astype(np.float32)).to(DEV)
+    beta = torch.from_numpy(rng.uniform(-1.0, 1.0, cols).astype(np.float32)).to(DEV)
+    inv_s = torch.from_numpy(np.exp(rng.uniform(-5, 3, cols)).astype(np.float32)).to(DEV)
+    eps = float(rng.choice([0.0, 1e-6, 1e-5, 0.1]))
+    g, b = w8.fold_layernorm(gamma, beta, inv_s)
+    q, d = w8.layernorm_quant_rows(x, g, b, eps)
+    g_or = oracle.fold_norm_weight(host(gamma), host(inv_s))
+    b_or = oracle.fold_norm_weight(host(beta), host(inv_s))
+    q_or, d_or = oracle.layernorm_smooth_quant_rows(host(x), g_or, b_or, eps)
+    assert np.array_equal(host(q), q_or)
+    assert np.array_equal(host(d).view(np.uint32), d_or.view(np.uint32))
+
+
+@pytest.mark.parametrize("case", range(12))
 def test_fuzz_gemm_float(case):
     """Dense 16-bit product: within K 2^-24 sum|a b| of the exact value, plus
     one unit of the output format."""

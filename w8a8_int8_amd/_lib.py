@@ -22,6 +22,8 @@ PROTOTYPES = {
     "w8a8_fold_norm_weight": (c_int, [c_vp, c_vp, c_i64, c_vp, c_vp]),
     "w8a8_rmsnorm_quant_rows": (c_int, [c_vp, c_int, c_i64, c_i64, c_vp, ctypes.c_float, c_vp, c_vp,
                                         c_vp]),
+    "w8a8_layernorm_quant_rows": (c_int, [c_vp, c_int, c_i64, c_i64, c_vp, c_vp, ctypes.c_float,
+                                          c_vp, c_vp, c_vp]),
     "w8a8_gemm_i32": (c_int, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_vp]),
     "w8a8_gemm_dequant": (c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_vp]),
     "w8a8_scale_quant_rows_e4m3": (c_int, [c_vp, c_int, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp]),
@@ -33,7 +35,7 @@ PROTOTYPES = {
                             c_vp]),
 }
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 W8A8_F16, W8A8_BF16 = 0, 1
 
 _lib = None

@@ -143,6 +143,38 @@ def rmsnorm_quant_rows(h: torch.Tensor, g: torch.Tensor, eps: float,
     return q, row_scale
 
 
+def fold_layernorm(gamma: torch.Tensor, beta: torch.Tensor, inv_s: torch.Tensor):
+    """(g, b) = (gamma * inv_s, beta * inv_s) in fp32: the smoothing folded into
+    a LayerNorm's affine pair (two calls of w8a8_fold_norm_weight)."""
+    return fold_norm_weight(gamma, inv_s), fold_norm_weight(beta, inv_s)
+
+
+def layernorm_quant_rows(x: torch.Tensor, g: torch.Tensor, b: torch.Tensor, eps: float,
+                         q: Optional[torch.Tensor] = None,
+                         row_scale: Optional[torch.Tensor] = None):
+    """Per-token INT8 of LayerNorm(x; gamma, beta) * inv_s for fp16 x, given
+    the folded g = gamma * inv_s and b = beta * inv_s (fold_layernorm).
+
+    Returns (q int8 rows x cols, row_scale fp32[rows]); q * row_scale[:, None]
+    approximates LayerNorm(x) * inv_s.
+    """
+    _dev(x, g, b)
+    rows, cols = x.shape
+    _need(g, torch.float32, (cols,))
+    _need(b, torch.float32, (cols,))
+    q = torch.empty((rows, cols), dtype=torch.int8, device=x.device) if q is None else q
+    row_scale = (torch.empty(rows, dtype=torch.float32, device=x.device)
+                 if row_scale is None else row_scale)
+    _dev(q, row_scale)
+    _need(q, torch.int8, (rows, cols))
+    _need(row_scale, torch.float32, (rows,))
+    lib = _lib.load()
+    _lib.check("w8a8_layernorm_quant_rows", lib.w8a8_layernorm_quant_rows(
+        _ptr(x), _dtype_code(x), rows, cols, _ptr(g), _ptr(b), float(eps), _ptr(q),
+        _ptr(row_scale), _stream()))
+    return q, row_scale
+
+
 def gemm_i32(qa: torch.Tensor, qb: torch.Tensor, c: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Exact int32 C = qa @ qb.T for qa (M x K) and qb (N x K) int8."""
     _dev(qa, qb)

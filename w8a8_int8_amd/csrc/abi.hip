@@ -123,6 +123,20 @@ w8a8_status_t w8a8_rmsnorm_quant_rows(const void* h, int dtype, int64_t rows, in
                                                   q, row_scale, 0, stream));
 }
 
+w8a8_status_t w8a8_layernorm_quant_rows(const void* x, int dtype, int64_t rows, int64_t cols,
+                                        const float* g, const float* b, float eps, int8_t* q,
+                                        float* row_scale, hipStream_t stream) {
+  const w8a8_status_t st = check_quant(x, dtype, rows, cols, g, q, row_scale);
+  if (st != W8A8_OK) return st;
+  if (dtype != W8A8_F16) return W8A8_ERR_DTYPE;  // exact row sums need fp16's range
+  if (!b && cols) return W8A8_ERR_NULL;
+  if (!aligned(b, 16)) return W8A8_ERR_ALIGN;
+  if (!(eps >= 0.0f && eps <= 3.0e38f)) return W8A8_ERR_ARG;  // also rejects NaN and +inf
+  if (cols == 0 && rows) return W8A8_ERR_SHAPE;                // the mean of an empty row
+  return hip_status(w8a8::launch_layernorm_quant_rows(x, rows, cols, g, b, eps, q, row_scale,
+                                                      stream));
+}
+
 w8a8_status_t w8a8_gemm_i32(const int8_t* qa, const int8_t* qb, int32_t* c, int64_t M, int64_t N,
                             int64_t K, hipStream_t stream) {
   const w8a8_status_t st = check_gemm(qa, qb, c, M, N, K);

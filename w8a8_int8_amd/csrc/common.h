@@ -25,6 +25,11 @@ hipError_t launch_scale_quant_rows(const void* x, bool bf16, int64_t rows, int64
                                    const float* col_scale, bool norm, float eps, void* q,
                                    float* row_scale, int fmt, hipStream_t st);
 hipError_t launch_fold(const float* a, const float* b, int64_t n, float* out, hipStream_t st);
+// LayerNorm fold (fp16 rows): per-token INT8 of LayerNorm(x; gamma, beta) * inv_s
+// given g = RN32(gamma * inv_s) and b = RN32(beta * inv_s).
+hipError_t launch_layernorm_quant_rows(const void* x, int64_t rows, int64_t cols, const float* g,
+                                       const float* b, float eps, void* q, float* row_scale,
+                                       hipStream_t st);
 // Split-K few-token GEMM with the dequant epilogue (17 <= M <= 32): S int32
 // partial slices of M x N in `partials` (S from splitk_plan), summed exactly
 // by a second kernel.  With S == 1 there is one launch and `partials` is unused.

@@ -278,4 +278,197 @@ hipError_t launch_scale_quant_rows(const void* x, bool bf16, int64_t rows, int64
   }
 }
 
+// LayerNorm fold (fp16 rows), one row per block.  The smoothing's inv_s is
+// folded into the LayerNorm's affine pair, g = RN32(gamma * inv_s) and
+// b = RN32(beta * inv_s), and the additive b keeps the row statistics in
+// every element, so they decide codes; they are therefore computed without
+// any dependence on a summation order.  Every finite fp16 value is an integer
+// multiple of 2^-24, so with X = x * 2^24 (|X| < 2^41) the sums S1 = sum X and
+// S2 = sum X^2 are exact integers: S1 in int64, and S2 from the split
+// |X| = hi * 2^20 + lo as sum hi^2 * 2^40 + 2 sum hi lo * 2^20 + sum lo^2, three
+// int64 sums (each below 2^58 for rows of at most 65536).  Integer sums are
+// order free, so the wave and block reductions are exact.  Then, once per row:
+//   mean = f32(f64(f64(S1) / (K 2^24)))
+//   var  = f32(f64(f64(K S2 - S1^2) / (K^2 2^48)))     (population variance)
+//   r    = RN32(1 / RN32(sqrt(RN32(var + eps)))), or 0 when var + eps == 0
+// and per element v = RN32(RN32(RN32(RN32(x - mean) * r) * g) + b), one IEEE
+// fp32 operation per step, followed by the per-row quantizer.
+namespace {
+
+// Correctly rounded (to nearest even) conversion of a nonnegative 128-bit
+// integer to double: normalize the top 64 bits and fold every bit below them
+// into the lowest one, a sticky bit under the rounding position.
+__device__ __forceinline__ double u128_to_f64(unsigned __int128 v) {
+  const unsigned long long hi = (unsigned long long)(v >> 64), lo = (unsigned long long)v;
+  if (hi == 0) return (double)lo;
+  const int lz = __builtin_clzll(hi);
+  unsigned long long top = lz ? (hi << lz) | (lo >> (64 - lz)) : hi;
+  const unsigned long long rest = lz ? (lo << lz) : lo;
+  top |= (rest != 0) ? 1ull : 0ull;
+  return __builtin_ldexp((double)top, 64 - lz);
+}
+
+// Sums of the LayerNorm statistics carried through the reductions.
+struct LnSums {
+  long long s1;                     // sum X
+  unsigned long long hh, hl, ll;    // sum hi^2, sum hi lo, sum lo^2
+};
+
+__device__ __forceinline__ LnSums ln_add(LnSums a, const LnSums& b) {
+  a.s1 += b.s1;
+  a.hh += b.hh;
+  a.hl += b.hl;
+  a.ll += b.ll;
+  return a;
+}
+
+template <int CPT>
+__global__ __launch_bounds__(1024) void k_layernorm_quant_rows(const v4u* __restrict__ x,
+                                                               int cols8,
+                                                               const float4* __restrict__ gv,
+                                                               const float4* __restrict__ bv,
+                                                               float eps, uint2* __restrict__ q,
+                                                               float* __restrict__ row_scale) {
+  const int tid = threadIdx.x;
+  const int G = blockDim.x;
+  const int lane = tid % kWave, wave = tid / kWave, nwaves = G / kWave;
+  const int64_t row = blockIdx.x;
+
+  v4u xv[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = i * G + tid;
+    xv[i] = c < cols8 ? __builtin_nontemporal_load(x + row * cols8 + c) : v4u{0u, 0u, 0u, 0u};
+  }
+
+  // pass 1: exact integer sums (chunks past the row hold zeros and add nothing)
+  LnSums acc = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const unsigned h = (e & 1) ? (xv[i][e / 2] >> 16) : (xv[i][e / 2] & 0xffffu);
+      const unsigned ex = (h >> 10) & 0x1f, mant = h & 0x3ff;
+      const unsigned long long mag =
+          ex ? ((unsigned long long)(1024u + mant) << (ex - 1)) : (unsigned long long)mant;
+      acc.s1 += (h & 0x8000u) ? -(long long)mag : (long long)mag;
+      const unsigned hi = (unsigned)(mag >> 20), lo = (unsigned)(mag & 0xfffffu);
+      acc.hh += (unsigned long long)hi * hi;
+      acc.hl += (unsigned long long)hi * lo;
+      acc.ll += (unsigned long long)lo * lo;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    LnSums o;
+    o.s1 = __shfl_xor(acc.s1, off, kWave);
+    o.hh = __shfl_xor(acc.hh, off, kWave);
+    o.hl = __shfl_xor(acc.hl, off, kWave);
+    o.ll = __shfl_xor(acc.ll, off, kWave);
+    acc = ln_add(acc, o);
+  }
+  __shared__ LnSums red[16];
+  __shared__ float stat[2];
+  __shared__ float redm[16];
+  if (lane == 0) red[wave] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    LnSums t = red[0];
+    for (int w = 1; w < nwaves; ++w) t = ln_add(t, red[w]);
+    const long long K = (long long)cols8 * 8;
+    const __int128 s2 = ((__int128)t.hh << 40) + ((__int128)t.hl << 21) + (__int128)t.ll;
+    const __int128 v = (__int128)K * s2 - (__int128)t.s1 * (__int128)t.s1;  // >= 0
+    const double kd = (double)K;
+    const float mean = (float)((double)t.s1 / (kd * 16777216.0));
+    const float var = (float)(u128_to_f64((unsigned __int128)v) / (kd * kd * 281474976710656.0));
+    const float tv = var + eps;
+    stat[0] = mean;
+    stat[1] = tv > 0.0f ? 1.0f / sqrtf(tv) : 0.0f;
+  }
+  __syncthreads();
+  const float mean = stat[0], r = stat[1];
+
+  // pass 2: v in registers and the row max of |v|
+  float v[CPT][8];
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = i * G + tid;
+    if (c < cols8) {
+      const float4 g0 = gv[2 * c], g1 = gv[2 * c + 1], b0 = bv[2 * c], b1 = bv[2 * c + 1];
+      const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float t = elem<false>(xv[i], e) - mean;
+        t = t * r;
+        t = t * gg[e];
+        t = t + bb[e];
+        v[i][e] = t;
+        m = fmaxf(m, fabsf(t));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[i][e] = 0.0f;
+    }
+  }
+  m = wave_max(m);
+  if (lane == 0) redm[wave] = m;
+  __syncthreads();
+  m = redm[0];
+  for (int w = 1; w < nwaves; ++w) m = fmaxf(m, redm[w]);
+
+  // the per-row quantizer, as in k_scale_quant_rows
+  const float rcp = m > 0.0f ? 127.0f / m : 0.0f;
+  if (tid == 0) row_scale[row] = m > 0.0f ? m / 127.0f : 0.0f;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = i * G + tid;
+    if (c >= cols8) continue;
+    float t[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      t[e] = v[i][e] * rcp;
+      t[e] = t[e] + kRoundMagic;
+    }
+    uint2 o;
+    o.x = pack_codes(t[0], t[1], t[2], t[3]);
+    o.y = pack_codes(t[4], t[5], t[6], t[7]);
+    q[row * cols8 + c] = o;
+  }
+}
+
+template <int CPT>
+void launch_ln(const void* x, int64_t rows, int cols8, int G, const float* g, const float* b,
+               float eps, void* q, float* row_scale, hipStream_t st) {
+  hipLaunchKernelGGL(k_layernorm_quant_rows<CPT>, dim3((unsigned)rows), dim3(G), 0, st,
+                     (const v4u*)x, cols8, (const float4*)g, (const float4*)b, eps, (uint2*)q,
+                     row_scale);
+}
+
+}  // namespace
+
+hipError_t launch_layernorm_quant_rows(const void* x, int64_t rows, int64_t cols, const float* g,
+                                       const float* b, float eps, void* q, float* row_scale,
+                                       hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  const int cols8 = (int)(cols / 8);
+  int G = (cols8 + 1) / 2;  // two 16-byte chunks per thread, whole waves, at most 1024
+  G = ((G + kWave - 1) / kWave) * kWave;
+  if (G < kWave) G = kWave;
+  if (G > 1024) G = 1024;
+  switch ((cols8 + G - 1) / G) {
+    case 1: launch_ln<1>(x, rows, cols8, G, g, b, eps, q, row_scale, st); break;
+    case 2: launch_ln<2>(x, rows, cols8, G, g, b, eps, q, row_scale, st); break;
+    case 3: launch_ln<3>(x, rows, cols8, G, g, b, eps, q, row_scale, st); break;
+    case 4: launch_ln<4>(x, rows, cols8, G, g, b, eps, q, row_scale, st); break;
+    case 5: launch_ln<5>(x, rows, cols8, G, g, b, eps, q, row_scale, st); break;
+    case 6: launch_ln<6>(x, rows, cols8, G, g, b, eps, q, row_scale, st); break;
+    case 7: launch_ln<7>(x, rows, cols8, G, g, b, eps, q, row_scale, st); break;
+    case 8: launch_ln<8>(x, rows, cols8, G, g, b, eps, q, row_scale, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace w8a8
