@@ -25,6 +25,9 @@
 // The FP8 variant (same smoothing, FP8 E4M3 grid as the page's remark on
 // low-bit float formats allows) differs only in the grid maximum (448) and in
 // the rounding: the hardware conversion to E4M3, round to nearest even.
+//
+// The RMS-norm fold (NORM) reuses this kernel; the LayerNorm fold, whose
+// row statistics enter every element, is k_layernorm_quant_rows at the end.
 #include "common.h"
 
 namespace w8a8 {
