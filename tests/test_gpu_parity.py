@@ -161,13 +161,15 @@ def rand_codes(rows, cols, seed):
 
 
 # shapes cover the four tile configurations (128x128, 256x128, 256x192, 256x256), the
-# skinny few-token kernel (M <= 16 and M <= 32), ragged M, N and K tails, K = 0
+# few-token kernels (skinny: M <= 16 and M <= 32; 64-channel blocks over the whole
+# of K: 12 to 16 tokens on at least 12288 channels), ragged M, N and K tails, K = 0
 # and empty outputs
 GEMM_SHAPES = [(1, 8, 16), (37, 136, 80), (300, 520, 1040), (64, 512, 512),
                (2048, 4096, 256), (4000, 8184, 272), (4096, 8192, 144), (513, 264, 4112),
                (5, 16, 0), (0, 8, 32), (8, 0, 32),
                (1, 4096, 16384), (3, 8, 64), (16, 520, 1040), (17, 136, 80), (32, 264, 4112),
-               (33, 136, 80), (32, 16384, 272), (3000, 6000, 272), (2048, 12288, 144)]
+               (33, 136, 80), (32, 16384, 272), (3000, 6000, 272), (2048, 12288, 144),
+               (12, 12288, 1040), (16, 16392, 272), (13, 24576, 4112)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)

@@ -794,6 +794,19 @@ hipError_t launch_gemm(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N,
   // Few tokens: weight streaming, handled by the skinny kernel.  Between 17
   // and 32 tokens it reads two activation fragments per step, and the tiled
   // kernel is as fast once N alone gives it 128 or more blocks.
+  // 12 to 16 tokens over at least 192 blocks of 64 channels: the split-K
+  // kernel with a single K range per block.  Each of its activation fragments
+  // serves four weight fragments, where the skinny kernel re-reads the
+  // activations once per 16 channels (at 16 tokens that doubles the operand
+  // stream); below 12 tokens, or with fewer blocks, the skinny kernel is as
+  // fast or faster.
+  if (!tiled_only && M >= 12 && M <= 16 && N >= 192 * 16 * kSplitkCT) {
+    const int nst = (int)((K + 63) / 64);
+    if (out_mode == 0) launch_splitk_kernel<1, 0>(qa, qb, (int)M, (int)N, (int)K, 1, nst, sa, sb, out, st);
+    else if (out_mode == 1) launch_splitk_kernel<1, 1>(qa, qb, (int)M, (int)N, (int)K, 1, nst, sa, sb, out, st);
+    else launch_splitk_kernel<1, 2>(qa, qb, (int)M, (int)N, (int)K, 1, nst, sa, sb, out, st);
+    return hipGetLastError();
+  }
   if (!tiled_only && M <= 16) return launch_skinny<1>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
   if (!tiled_only && M <= 32 && N < 16384)
     return launch_skinny<2>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
