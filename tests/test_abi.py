@@ -61,6 +61,8 @@ def test_workspace_bytes():
     assert lib.w8a8_linear_workspace_bytes(32, 4096, 16384) == 32 * 16384 + 256 + 4 * 32 * 4096 * 4
     assert lib.w8a8_linear_workspace_bytes(32, 16384, 4096) == 32 * 4096 + 256  # 256 blocks: no split
     assert lib.w8a8_linear_workspace_bytes(16, 4096, 16384) == 16 * 16384 + 256  # unsplit kernel
+    assert lib.w8a8_linear_workspace_bytes(32, 12288, 4096) == 32 * 4096 + 256  # 192 tiles: one range
+    assert lib.w8a8_linear_workspace_bytes(32, 8192, 4096) == 32 * 4096 + 256 + 2 * 32 * 8192 * 4
 
 
 @cpu_only

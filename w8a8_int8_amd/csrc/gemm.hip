@@ -791,22 +791,29 @@ hipError_t launch_gemm(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N,
   // The skinny few-token kernel serves the INT8 modes only.
   const bool tiled_only = out_mode >= 3;
   if (out_mode == 3 || out_mode == 4) K *= 2;
-  // Few tokens: weight streaming, handled by the skinny kernel.  Between 17
-  // and 32 tokens it reads two activation fragments per step, and the tiled
-  // kernel is as fast once N alone gives it 128 or more blocks.
-  // 12 to 16 tokens over at least 192 blocks of 64 channels: the split-K
-  // kernel with a single K range per block.  Each of its activation fragments
+  // Few tokens: weight streaming.  12 to 32 tokens over at least 192 blocks
+  // of 64 channels: the split-K
+  // kernel with one K range per block.  Each of its activation fragments
   // serves four weight fragments, where the skinny kernel re-reads the
-  // activations once per 16 channels (at 16 tokens that doubles the operand
+  // activations once per 16 channels (at 16 tokens that doubles its operand
   // stream); below 12 tokens, or with fewer blocks, the skinny kernel is as
   // fast or faster.
-  if (!tiled_only && M >= 12 && M <= 16 && N >= 192 * 16 * kSplitkCT) {
+  if (!tiled_only && M >= 12 && M <= 32 && N >= 192 * 16 * kSplitkCT) {
     const int nst = (int)((K + 63) / 64);
-    if (out_mode == 0) launch_splitk_kernel<1, 0>(qa, qb, (int)M, (int)N, (int)K, 1, nst, sa, sb, out, st);
-    else if (out_mode == 1) launch_splitk_kernel<1, 1>(qa, qb, (int)M, (int)N, (int)K, 1, nst, sa, sb, out, st);
-    else launch_splitk_kernel<1, 2>(qa, qb, (int)M, (int)N, (int)K, 1, nst, sa, sb, out, st);
+    if (M <= 16) {
+      if (out_mode == 0) launch_splitk_kernel<1, 0>(qa, qb, (int)M, (int)N, (int)K, 1, nst, sa, sb, out, st);
+      else if (out_mode == 1) launch_splitk_kernel<1, 1>(qa, qb, (int)M, (int)N, (int)K, 1, nst, sa, sb, out, st);
+      else launch_splitk_kernel<1, 2>(qa, qb, (int)M, (int)N, (int)K, 1, nst, sa, sb, out, st);
+    } else {
+      if (out_mode == 0) launch_splitk_kernel<2, 0>(qa, qb, (int)M, (int)N, (int)K, 1, nst, sa, sb, out, st);
+      else if (out_mode == 1) launch_splitk_kernel<2, 1>(qa, qb, (int)M, (int)N, (int)K, 1, nst, sa, sb, out, st);
+      else launch_splitk_kernel<2, 2>(qa, qb, (int)M, (int)N, (int)K, 1, nst, sa, sb, out, st);
+    }
     return hipGetLastError();
   }
+  // Otherwise the skinny kernel; between 17 and 32 tokens it reads two
+  // activation fragments per step, and the tiled kernel is as fast once N
+  // alone gives it 128 or more blocks.
   if (!tiled_only && M <= 16) return launch_skinny<1>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
   if (!tiled_only && M <= 32 && N < 16384)
     return launch_skinny<2>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
@@ -842,8 +849,10 @@ SplitkPlan splitk_plan(int64_t M, int64_t N, int64_t K) {
   if (M < 17 || M > 32 || N < 1 || K < 1) return p;
   const int64_t tiles = (N + 16 * kSplitkCT - 1) / (16 * kSplitkCT);
   const int64_t nsteps = (K + 63) / 64;
-  // about one block per CU, and at least 32 k steps (2 KiB of each weight row) per split
-  int64_t s = (256 + tiles - 1) / tiles;
+  // about one block per CU, and at least 32 k steps (2 KiB of each weight row)
+  // per split; with 192 or more channel tiles one K range per block is faster
+  // than splitting (measured on a 4096 -> 12288 layer at 17-32 tokens)
+  int64_t s = tiles >= 192 ? 1 : (256 + tiles - 1) / tiles;
   s = std::min<int64_t>(s, std::max<int64_t>(1, nsteps / 32));
   s = std::min<int64_t>(s, 16);
   p.splits = (int)s;
