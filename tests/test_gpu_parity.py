@@ -82,7 +82,8 @@ def assert_s_parity(s_gpu, inv_gpu, amax_x, amax_w, alpha):
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("rows,cols", [(1, 8), (37, 136), (300, 1032), (2048, 4096),
-                                       (1000, 11008), (129, 28672)])
+                                       (1000, 11008), (129, 28672), (3001, 4104),
+                                       (22016, 4096)])
 def test_channel_amax(dtype, rows, cols):
     x = rand_act(rows, cols, dtype, seed=rows * 7 + cols)
     got = host(w8.channel_amax(x))

@@ -13,15 +13,16 @@
 // an unsigned atomic max on the fp32 bit pattern, which orders non-negative
 // floats the same way.
 //
-// Work split: a block owns a strip of 64 columns (128 bytes of every row) and
-// a tall range of rows.  One wave load covers 8 rows x 128 B (8 lanes per row,
-// full cache lines); the 4 waves take interleaved groups of 8 rows and each
-// lane keeps U loads in flight.  At the end the lanes that hold the same
-// columns are folded with cross-lane max, then the 4 waves through LDS, and
-// 64 lanes issue one coalesced atomic max each (one per column).  Row ranges
-// are sized so the grid has about 1024 blocks while each column receives at
-// most a few dozen atomics: the atomics, not the loads, are what a finer
-// split would pay for.
+// Work split: a block owns a strip of 256 columns (512 bytes of every row)
+// and a tall range of rows.  One wave load covers 2 rows x 512 B (32 lanes
+// per row); the 4 waves take interleaved pairs of rows and each lane keeps U
+// loads in flight.  At the end the two lanes that hold the same columns are
+// folded with a cross-lane max, then the 4 waves through LDS, and the block
+// issues one coalesced atomic max per column.  Row ranges are sized so the
+// grid has about 1024 blocks while each column receives at most 128 atomics.
+// Measured on fp16 weights of 4096 to 57344 rows: 512-byte row pieces stream
+// at 5.5-6.4 TB/s where 128-byte pieces (a strip of 64 columns) reached
+// 5.0-5.6 TB/s.
 #include "common.h"
 
 namespace w8a8 {
@@ -31,9 +32,13 @@ namespace {
 constexpr int kAmaxThreads = 256;
 constexpr int kAmaxWaves = kAmaxThreads / kWave;
 constexpr int kAmaxUnroll = 8;
-constexpr int kRowsPerLoad = 8;                                     // rows per wave load
-constexpr int kRowsPerGroup = kRowsPerLoad * kAmaxWaves;            // 32 rows per block step
-constexpr int kRowsPerBatch = kRowsPerGroup * kAmaxUnroll;          // 256 rows in flight
+constexpr int kLanesPerRow = 32;                                    // 16-byte chunks of a row piece
+constexpr int kStripCols = kLanesPerRow * 8;                        // 256 columns per block
+constexpr int kRowsPerLoad = kWave / kLanesPerRow;                  // 2 rows per wave load
+constexpr int kRowsPerGroup = kRowsPerLoad * kAmaxWaves;            // 8 rows per block step
+constexpr int kRowsPerBatch = kRowsPerGroup * kAmaxUnroll;          // 64 rows in flight
+constexpr int kMaxRowRanges = 128;                                  // atomics per column
+static_assert(kStripCols == kAmaxThreads, "one column per thread in the fold");
 
 __device__ __forceinline__ unsigned pmax16(unsigned a, unsigned b) {
   u16x2 x = __builtin_bit_cast(u16x2, a);
@@ -53,8 +58,8 @@ __global__ __launch_bounds__(kAmaxThreads) void k_channel_amax(const v4u* __rest
                                                                unsigned* __restrict__ amax_bits) {
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
-  const int sub = lane / 8;                                   // row within a wave load
-  const int64_t chunk = (int64_t)blockIdx.x * 8 + (lane % 8);  // 16-byte column chunk
+  const int sub = lane / kLanesPerRow;  // row within a wave load
+  const int64_t chunk = (int64_t)blockIdx.x * kLanesPerRow + (lane % kLanesPerRow);  // 16-byte chunk
   const int64_t r_begin = (int64_t)blockIdx.y * rows_per_block;
   const int64_t r_end = min(rows, r_begin + rows_per_block);
   const bool active = chunk < cols8;
@@ -85,17 +90,17 @@ __global__ __launch_bounds__(kAmaxThreads) void k_channel_amax(const v4u* __rest
       for (int u = 0; u < kAmaxUnroll; ++u) m = vmax(m, v[u]);
     }
   }
-  // fold the 8 row lanes that hold the same chunk (lanes l, l^8, l^16, l^32)
+  // fold the lanes that hold the same chunk (lanes l and l ^ 32)
 #pragma unroll
-  for (int off = 8; off < kWave; off <<= 1) {
+  for (int off = kLanesPerRow; off < kWave; off <<= 1) {
     m.x = pmax16(m.x, (unsigned)__shfl_xor((int)m.x, off, kWave));
     m.y = pmax16(m.y, (unsigned)__shfl_xor((int)m.y, off, kWave));
     m.z = pmax16(m.z, (unsigned)__shfl_xor((int)m.z, off, kWave));
     m.w = pmax16(m.w, (unsigned)__shfl_xor((int)m.w, off, kWave));
   }
-  // fold the waves through LDS: wave w's lanes 0..7 hold its 64 column maxima
-  __shared__ unsigned short part[kAmaxWaves][64];
-  if (lane < 8) {
+  // fold the waves through LDS: wave w's lanes 0..31 hold its 256 column maxima
+  __shared__ unsigned short part[kAmaxWaves][kStripCols];
+  if (lane < kLanesPerRow) {
     const unsigned w4[4] = {m.x, m.y, m.z, m.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -104,11 +109,12 @@ __global__ __launch_bounds__(kAmaxThreads) void k_channel_amax(const v4u* __rest
     }
   }
   __syncthreads();
-  if (wave != 0) return;
-  unsigned short b = part[0][lane];
+  // one column per thread (kStripCols == kAmaxThreads)
+  const int c = threadIdx.x;
+  unsigned short b = part[0][c];
 #pragma unroll
-  for (int w = 1; w < kAmaxWaves; ++w) b = max(b, part[w][lane]);
-  const int64_t col = (int64_t)blockIdx.x * 64 + lane;
+  for (int w = 1; w < kAmaxWaves; ++w) b = max(b, part[w][c]);
+  const int64_t col = (int64_t)blockIdx.x * kStripCols + c;
   if (col < cols8 * 8 && b != 0)  // +0 never raises a non-negative running max
     atomicMax(amax_bits + col, __float_as_uint(widen16(b, BF16)));
 }
@@ -119,10 +125,11 @@ hipError_t launch_channel_amax(const void* x, bool bf16, int64_t rows, int64_t c
                                hipStream_t st) {
   if (rows == 0) return hipSuccess;
   const int64_t cols8 = cols / 8;
-  const int64_t strips = (cols8 + 7) / 8;
-  // about 1024 blocks, at most 32 row ranges per strip, at least one 32-row step each
+  const int64_t strips = (cols8 + kLanesPerRow - 1) / kLanesPerRow;
+  // about 1024 blocks, at most kMaxRowRanges row ranges per strip, at least
+  // one block step of rows each
   int64_t row_blocks = (1024 + strips - 1) / strips;
-  if (row_blocks > 32) row_blocks = 32;
+  if (row_blocks > kMaxRowRanges) row_blocks = kMaxRowRanges;
   const int64_t max_rb = (rows + kRowsPerGroup - 1) / kRowsPerGroup;
   if (row_blocks > max_rb) row_blocks = max_rb;
   if (row_blocks < 1) row_blocks = 1;
