@@ -4,8 +4,9 @@ One step = one pass of the whole path over one batch, for every linear layer
 of the Llama-2-7B-shaped decoder block (prefill, M = 2048 tokens):
   1. channel amax: fold one fresh 2048-token calibration batch into the
      layer's running max|X_j| (streaming calibration; step i uses batch i)
-  2. max|W_j| over the weight, smoothing factors s and 1/s, fold s into W and
-     quantize it per output channel
+  2. max|W_j| over the weight, smoothing factors s and 1/s (1 and these in one
+     launch, w8a8_calibrate_smooth), fold s into W and quantize it per output
+     channel
   3. smooth X (X / s) and quantize it per token
   4.+5. INT8 GEMM with the fused dequant epilogue -> fp16 Y
 All inputs are resident in HBM before the timed region.
@@ -175,6 +176,7 @@ class Layer:
         f32 = dict(dtype=torch.float32, device=dev)
         self.amax_x = torch.zeros(self.K, **f32)
         self.amax_w = torch.zeros(self.K, **f32)
+        self.scratch = w8.calibrate_smooth_scratch(self.K, dev)
         self.s = torch.empty(self.K, **f32)
         self.inv_s = torch.empty(self.K, **f32)
         self.qw = torch.empty((self.N, self.K), dtype=torch.int8, device=dev)
@@ -194,12 +196,13 @@ class Layer:
         return float(M * self.K + self.N * self.K + 2 * M * self.N + 4 * (M + self.N))
 
     def step(self, i, ev=None):
-        """One pass of the path for this layer; amax_w must be zero on entry
-        (run_step zeroes every layer's at once)."""
+        """One pass of the path for this layer: calibration batch i folded into
+        the running max|X_j|, max|W_j| and the smoothing factors (one launch),
+        the weight folded and quantized, the activations smoothed and
+        quantized, and the INT8 GEMM with its dequant epilogue."""
         w8 = self.w8
-        w8.channel_amax(self.cal[i % len(self.cal)], self.amax_x)
-        w8.channel_amax(self.w, self.amax_w)
-        w8.smooth_factors(self.amax_x, self.amax_w, self.alpha, self.s, self.inv_s)
+        w8.calibrate_smooth(self.cal[i % len(self.cal)], self.w, self.alpha, self.amax_x,
+                            self.amax_w, self.s, self.inv_s, self.scratch)
         w8.scale_quant_rows(self.w, self.s, self.qw, self.sw)
         w8.scale_quant_rows(self.x, self.inv_s, self.qx, self.sx)
         if ev is not None:
@@ -262,6 +265,10 @@ def kernel_breakdown(layers, reps):
         nw, nx = len(ws), len(xs)
         t = timed(lambda i: w8.channel_amax(ws[i % nw], L.amax_w), reps)
         d["channel_amax_weight"] = hbm(t, L.w.numel() * 2)
+        # the step's form: one calibration batch, the weight maxima and s in one launch
+        t = timed(lambda i: w8.calibrate_smooth(cal[i % nb], ws[i % nw], L.alpha, L.amax_x,
+                                                L.amax_w, L.s, L.inv_s, L.scratch), reps)
+        d["calibrate_smooth"] = hbm(t, cal[0].numel() * 2 + L.w.numel() * 2)
         t = timed(lambda i: w8.scale_quant_rows(ws[i % nw], L.s, L.qw, L.sw), reps)
         d["fold_quant_weight"] = hbm(t, L.w.numel() * 3 + 4 * (L.N + L.K))
         t = timed(lambda i: w8.scale_quant_rows(xs[i % nx], L.inv_s, L.qx, L.sx), reps)
@@ -400,15 +407,8 @@ def main():
         torch.cuda.synchronize()
         del src
     layers = [Layer(wl, li, n_batches, args.alpha, dev) for li in range(len(wl.layers))]
-    # every layer's weight amax in one buffer, zeroed once per step
-    amax_w_all = torch.zeros(sum(L.K for L in layers), dtype=torch.float32, device=dev)
-    off = 0
-    for L in layers:
-        L.amax_w = amax_w_all[off:off + L.K]
-        off += L.K
 
     def run_step(i, evs_row=None):
-        amax_w_all.zero_()
         for li, L in enumerate(layers):
             L.step(i, None if evs_row is None else evs_row[li])
 

@@ -9,6 +9,7 @@
  * layer's weight with K input and N output channels):
  *   1. channel amax over calibration activations      w8a8_channel_amax
  *   2. smoothing factors s, their reciprocals          w8a8_smooth_factors
+ *      1 (one last batch) + weight maxima + 2 at once   w8a8_calibrate_smooth
  *      fold s into W and quantize W per output channel w8a8_channel_amax (on W)
  *                                                       + w8a8_scale_quant_rows
  *   3. X diag(s)^-1 and per-token INT8 quantization    w8a8_scale_quant_rows
@@ -54,7 +55,7 @@
 extern "C" {
 #endif
 
-#define W8A8_ABI_VERSION 3
+#define W8A8_ABI_VERSION 4
 
 /* Largest K for which 127 * 127 * K fits int32, so that every accumulator
  * (and every partial sum) of the INT8 product is exact in int32. */
@@ -114,6 +115,39 @@ w8a8_status_t w8a8_channel_amax(const void* x, int dtype, int64_t rows, int64_t 
  */
 w8a8_status_t w8a8_smooth_factors(const float* amax_x, const float* amax_w, int64_t K,
                                   double alpha, float* s, float* inv_s, hipStream_t stream);
+
+/*
+ * Steps 1 and 2 of one layer in one launch: fold one calibration batch into
+ * the running max|X_j|, take max|W_j| over the weight's output channels, and
+ * form s and inv_s from the two.  Page section "ハイパーパラメータ α", as
+ * w8a8_channel_amax (twice) followed by w8a8_smooth_factors, with the same
+ * results bit for bit; the usage example's `smooth_lm(model, act_scales,
+ * alpha)` is this call after the other calibration batches went through
+ * w8a8_channel_amax (or with cal_rows = 0).
+ *
+ *   x_cal    [cal_rows x K] fp16/bf16 (dtype) calibration batch, 16-byte
+ *            aligned; cal_rows may be 0 (then amax_x is only read).
+ *   w        [N x K] weight, same dtype, 16-byte aligned; N may be 0 (then
+ *            amax_w = 0 and s = 1).
+ *   amax_x   [K] fp32, in/out running maximum as in w8a8_channel_amax.
+ *   amax_w   [K] fp32 output, max_k |w[k, j]| (overwritten, not folded).
+ *   s, inv_s [K] fp32 outputs as in w8a8_smooth_factors (alpha in [0, 1]).
+ *   scratch  device memory of at least w8a8_calibrate_smooth_scratch_bytes(K)
+ *            bytes, 16-byte aligned, zero-filled by the caller before its
+ *            first use.  Every call leaves it zero again, so it is filled
+ *            once, not per call.  Calls that share a scratch must not run
+ *            concurrently (they would mix their weight maxima).
+ *   K >= 8, K % 8 == 0; cal_rows, N >= 0.
+ * The blocks meet through device-scope atomics only (no host round trip, no
+ * second launch): the last block over each 256 channels forms their s.
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, ARG (alpha outside [0, 1] or NaN,
+ * scratch_bytes too small), HIP.
+ */
+size_t w8a8_calibrate_smooth_scratch_bytes(int64_t K); /* 0 for an invalid K */
+w8a8_status_t w8a8_calibrate_smooth(const void* x_cal, int64_t cal_rows, const void* w, int64_t N,
+                                    int dtype, int64_t K, double alpha, float* amax_x,
+                                    float* amax_w, float* s, float* inv_s, void* scratch,
+                                    size_t scratch_bytes, hipStream_t stream);
 
 /*
  * Steps 2 (weights) and 3 (activations): scale every column, then quantize

@@ -36,11 +36,11 @@ def declared_symbols():
 def test_library_loads_and_exports_header_symbols():
     lib = _lib.load()
     syms = declared_symbols()
-    assert len(syms) == 15
+    assert len(syms) == 17
     for s in syms:
         assert hasattr(lib, s), s
         assert s in _lib.PROTOTYPES, s
-    assert lib.w8a8_abi_version() == 3
+    assert lib.w8a8_abi_version() == 4
 
 
 def test_status_strings():
@@ -126,6 +126,39 @@ def test_gemm_rejects():
     assert d(P, P, P, P, P, 3, 4, 8, 16, 0) == EDTYPE
     assert d(P, P, P, PODD, P, 0, 4, 8, 16, 0) == EALIGN
     assert d(P, P, P, P, P, 0, 4, 9, 16, 0) == ESHAPE
+
+
+def test_calibrate_smooth_scratch_bytes():
+    f = _lib.load().w8a8_calibrate_smooth_scratch_bytes
+    assert f(4096) == 4 * 4096 + 4 * 16
+    assert f(4104) == 4 * 4160 + 4 * 17  # 64-float padding, one counter per 256 channels
+    assert f(8) == 256 + 4
+    assert f(0) == 0 and f(12) == 0 and f(-8) == 0
+
+
+@cpu_only
+def test_calibrate_smooth_rejects():
+    lib = _lib.load()
+    f = lib.w8a8_calibrate_smooth
+    need = lib.w8a8_calibrate_smooth_scratch_bytes(64)
+    args = [P, 4, P, 8, 0, 64, 0.5, P, P, P, P, P, need, 0]
+
+    def call(**kw):
+        a = list(args)
+        names = ["x", "cal_rows", "w", "N", "dtype", "K", "alpha", "ax", "aw", "s", "inv_s",
+                 "scratch", "nbytes", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    assert call(dtype=2) == EDTYPE
+    assert call(K=12) == ESHAPE and call(K=0) == ESHAPE and call(N=-1) == ESHAPE
+    assert call(cal_rows=-1) == ESHAPE
+    assert call(x=0) == ENULL and call(w=0) == ENULL and call(scratch=0) == ENULL
+    assert call(ax=0) == ENULL and call(inv_s=0) == ENULL
+    assert call(alpha=1.5) == EARG and call(alpha=float("nan")) == EARG
+    assert call(nbytes=need - 1) == EARG
+    assert call(x=PODD) == EALIGN and call(scratch=P + 4) == EALIGN and call(s=P + 2) == EALIGN
 
 
 @cpu_only

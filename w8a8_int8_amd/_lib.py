@@ -18,6 +18,9 @@ PROTOTYPES = {
     "w8a8_status_str": (ctypes.c_char_p, [c_int]),
     "w8a8_channel_amax": (c_int, [c_vp, c_int, c_i64, c_i64, c_vp, c_vp]),
     "w8a8_smooth_factors": (c_int, [c_vp, c_vp, c_i64, ctypes.c_double, c_vp, c_vp, c_vp]),
+    "w8a8_calibrate_smooth_scratch_bytes": (c_size, [c_i64]),
+    "w8a8_calibrate_smooth": (c_int, [c_vp, c_i64, c_vp, c_i64, c_int, c_i64, ctypes.c_double,
+                                      c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
     "w8a8_scale_quant_rows": (c_int, [c_vp, c_int, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp]),
     "w8a8_fold_norm_weight": (c_int, [c_vp, c_vp, c_i64, c_vp, c_vp]),
     "w8a8_rmsnorm_quant_rows": (c_int, [c_vp, c_int, c_i64, c_i64, c_vp, ctypes.c_float, c_vp, c_vp,
@@ -35,7 +38,7 @@ PROTOTYPES = {
                             c_vp]),
 }
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 W8A8_F16, W8A8_BF16 = 0, 1
 
 _lib = None

@@ -84,6 +84,45 @@ def smooth_factors(amax_x: torch.Tensor, amax_w: torch.Tensor, alpha: float,
     return s, inv_s
 
 
+def calibrate_smooth_scratch(K: int, device) -> torch.Tensor:
+    """Zero-filled scratch for calibrate_smooth over K channels (reusable: every
+    call leaves it zero)."""
+    n = _lib.load().w8a8_calibrate_smooth_scratch_bytes(K)
+    if n == 0:
+        raise ValueError(f"no calibrate_smooth scratch for K = {K}")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def calibrate_smooth(x_cal: Optional[torch.Tensor], w: torch.Tensor, alpha: float,
+                     amax_x: torch.Tensor, amax_w: Optional[torch.Tensor] = None,
+                     s: Optional[torch.Tensor] = None, inv_s: Optional[torch.Tensor] = None,
+                     scratch: Optional[torch.Tensor] = None):
+    """One launch of: channel_amax(x_cal, amax_x) (skipped for None), amax_w =
+    channel max of the N x K weight ``w``, and smooth_factors.  Returns
+    (amax_w, s, inv_s)."""
+    _dev(w, amax_x)
+    N, K = w.shape
+    cal_rows = 0 if x_cal is None else x_cal.shape[0]
+    if x_cal is not None:
+        _dev(x_cal)
+        _need(x_cal, w.dtype, (cal_rows, K))
+    _need(amax_x, torch.float32, (K,))
+    f32 = dict(dtype=torch.float32, device=w.device)
+    amax_w = torch.empty(K, **f32) if amax_w is None else amax_w
+    s = torch.empty(K, **f32) if s is None else s
+    inv_s = torch.empty(K, **f32) if inv_s is None else inv_s
+    scratch = calibrate_smooth_scratch(K, w.device) if scratch is None else scratch
+    _dev(amax_w, s, inv_s, scratch)
+    for t in (amax_w, s, inv_s):
+        _need(t, torch.float32, (K,))
+    _need(scratch, torch.uint8, (scratch.numel(),))
+    lib = _lib.load()
+    _lib.check("w8a8_calibrate_smooth", lib.w8a8_calibrate_smooth(
+        _ptr(x_cal), cal_rows, _ptr(w), N, _dtype_code(w), K, float(alpha), _ptr(amax_x),
+        _ptr(amax_w), _ptr(s), _ptr(inv_s), _ptr(scratch), scratch.numel(), _stream()))
+    return amax_w, s, inv_s
+
+
 def scale_quant_rows(x: torch.Tensor, col_scale: torch.Tensor,
                      q: Optional[torch.Tensor] = None, row_scale: Optional[torch.Tensor] = None):
     """(q int8 rows x cols, row_scale fp32[rows]) of x * col_scale per row."""

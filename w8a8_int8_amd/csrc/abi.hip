@@ -86,6 +86,31 @@ w8a8_status_t w8a8_smooth_factors(const float* amax_x, const float* amax_w, int6
   return hip_status(w8a8::launch_smooth_factors(amax_x, amax_w, K, alpha, s, inv_s, stream));
 }
 
+size_t w8a8_calibrate_smooth_scratch_bytes(int64_t K) {
+  if (K < 1 || K % 8 != 0 || K >= kMaxRows) return 0;
+  return w8a8::calibrate_smooth_scratch_bytes(K);
+}
+
+w8a8_status_t w8a8_calibrate_smooth(const void* x_cal, int64_t cal_rows, const void* w, int64_t N,
+                                    int dtype, int64_t K, double alpha, float* amax_x,
+                                    float* amax_w, float* s, float* inv_s, void* scratch,
+                                    size_t scratch_bytes, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return W8A8_ERR_DTYPE;
+  if (cal_rows < 0 || N < 0 || cal_rows >= ((int64_t)1 << 40) || N >= ((int64_t)1 << 40) ||
+      K < 1 || K % 8 != 0 || K >= kMaxRows)
+    return W8A8_ERR_SHAPE;
+  if ((!x_cal && cal_rows) || (!w && N) || !amax_x || !amax_w || !s || !inv_s || !scratch)
+    return W8A8_ERR_NULL;
+  if (!(alpha >= 0.0 && alpha <= 1.0)) return W8A8_ERR_ARG;  // also rejects NaN
+  if (scratch_bytes < w8a8::calibrate_smooth_scratch_bytes(K)) return W8A8_ERR_ARG;
+  if (!aligned(x_cal, 16) || !aligned(w, 16) || !aligned(amax_x, 4) || !aligned(amax_w, 4) ||
+      !aligned(s, 4) || !aligned(inv_s, 4) || !aligned(scratch, 16))
+    return W8A8_ERR_ALIGN;
+  return hip_status(w8a8::launch_calibrate_smooth(x_cal, cal_rows, w, N, dtype == W8A8_BF16, K,
+                                                  alpha, amax_x, amax_w, s, inv_s, scratch,
+                                                  stream));
+}
+
 w8a8_status_t w8a8_scale_quant_rows(const void* x, int dtype, int64_t rows, int64_t cols,
                                     const float* col_scale, int8_t* q, float* row_scale,
                                     hipStream_t stream) {

@@ -24,6 +24,7 @@
 // at 5.5-6.4 TB/s where 128-byte pieces (a strip of 64 columns) reached
 // 5.0-5.6 TB/s.
 #include "common.h"
+#include "smooth_factor.h"
 
 namespace w8a8 {
 
@@ -51,17 +52,16 @@ __device__ __forceinline__ v4u vmax(v4u m, v4u v) {
              pmax16(m.z, v.z & 0x7fff7fffu), pmax16(m.w, v.w & 0x7fff7fffu)};
 }
 
+// The maximum of |x| over rows [r_begin, r_end) of the block's 256-column
+// strip, as a 16-bit magnitude pattern, for the column of this thread
+// (column blockIdx.x * 256 + threadIdx.x); 0 for columns past the end.
 template <bool BF16>
-__global__ __launch_bounds__(kAmaxThreads) void k_channel_amax(const v4u* __restrict__ x,
-                                                               int64_t rows, int64_t cols8,
-                                                               int64_t rows_per_block,
-                                                               unsigned* __restrict__ amax_bits) {
+__device__ __forceinline__ unsigned short strip_max(const v4u* __restrict__ x, int64_t cols8,
+                                                    int64_t r_begin, int64_t r_end) {
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
   const int sub = lane / kLanesPerRow;  // row within a wave load
   const int64_t chunk = (int64_t)blockIdx.x * kLanesPerRow + (lane % kLanesPerRow);  // 16-byte chunk
-  const int64_t r_begin = (int64_t)blockIdx.y * rows_per_block;
-  const int64_t r_end = min(rows, r_begin + rows_per_block);
   const bool active = chunk < cols8;
 
   v4u m = {0u, 0u, 0u, 0u};
@@ -114,9 +114,76 @@ __global__ __launch_bounds__(kAmaxThreads) void k_channel_amax(const v4u* __rest
   unsigned short b = part[0][c];
 #pragma unroll
   for (int w = 1; w < kAmaxWaves; ++w) b = max(b, part[w][c]);
-  const int64_t col = (int64_t)blockIdx.x * kStripCols + c;
+  return b;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kAmaxThreads) void k_channel_amax(const v4u* __restrict__ x,
+                                                               int64_t rows, int64_t cols8,
+                                                               int64_t rows_per_block,
+                                                               unsigned* __restrict__ amax_bits) {
+  const int64_t r_begin = (int64_t)blockIdx.y * rows_per_block;
+  const unsigned short b = strip_max<BF16>(x, cols8, r_begin, min(rows, r_begin + rows_per_block));
+  const int64_t col = (int64_t)blockIdx.x * kStripCols + threadIdx.x;
   if (col < cols8 * 8 && b != 0)  // +0 never raises a non-negative running max
     atomicMax(amax_bits + col, __float_as_uint(widen16(b, BF16)));
+}
+
+// One launch for a layer's calibration fold, weight maxima and smoothing
+// factors.  Row blocks y < rb_x take rows of the calibration batch xc and
+// fold into the running amax_x; the others take rows of the weight w and fold
+// into the accumulator acc_w (zero on entry).  Each strip counts its arriving
+// blocks; the last block of a strip forms s and inv_s of its 256 channels.
+//
+// Cross-block order without fences: every maximum and every count is a
+// device-scope atomic, performed at the one point of coherence that all eight
+// XCDs share (the same property the running max of k_channel_amax relies on).
+// A thread waits for its maximum's returned value before the block counts
+// itself, so when the count reaches the strip's total every maximum of the
+// strip has been performed; the last block then reads the maxima with atomic
+// read-modify-writes at that same point: amax_x by a compare-and-swap that
+// never matches, and acc_w by an exchange with 0, which also leaves the
+// accumulator zero for the next call.
+// It resets its counter the same way.  Its plain stores (amax_w, s, inv_s)
+// are for later kernels.
+template <bool BF16>
+__global__ __launch_bounds__(kAmaxThreads) void k_calibrate_smooth(
+    const v4u* __restrict__ xc, int64_t cal_rows, const v4u* __restrict__ w, int64_t w_rows,
+    int64_t cols8, int64_t rows_per_block, int64_t rb_x, double alpha,
+    unsigned* __restrict__ amax_x_bits, unsigned* __restrict__ acc_w_bits,
+    unsigned* __restrict__ arrivals, float* __restrict__ amax_w, float* __restrict__ s,
+    float* __restrict__ inv_s) {
+  const bool cal = (int64_t)blockIdx.y < rb_x;
+  const v4u* x = cal ? xc : w;
+  const int64_t rows = cal ? cal_rows : w_rows;
+  const int64_t r_begin = (cal ? (int64_t)blockIdx.y : (int64_t)blockIdx.y - rb_x) * rows_per_block;
+  const unsigned short b = strip_max<BF16>(x, cols8, r_begin, min(rows, r_begin + rows_per_block));
+  const int c = threadIdx.x;
+  const int64_t col = (int64_t)blockIdx.x * kStripCols + c;
+  const bool live = col < cols8 * 8;
+  unsigned seen = 0u;
+  if (live && b != 0)
+    seen = atomicMax((cal ? amax_x_bits : acc_w_bits) + col, __float_as_uint(widen16(b, BF16)));
+  // the returned value has arrived, so this thread's maximum has been
+  // performed, before the block is counted
+  asm volatile("s_waitcnt vmcnt(0)" : : "v"(seen) : "memory");
+  __shared__ unsigned last;
+  __syncthreads();
+  if (c == 0) last = atomicAdd(arrivals + blockIdx.x, 1u) == gridDim.y - 1 ? 1u : 0u;
+  __syncthreads();
+  if (!last) return;
+  if (live) {
+    // a compare-and-swap that never matches (the pattern is a NaN, never
+    // stored) reads the value as a read-modify-write, like the maxima
+    const float ax = __uint_as_float(atomicCAS(amax_x_bits + col, 0xffffffffu, 0xffffffffu));
+    const float aw = __uint_as_float(atomicExch(acc_w_bits + col, 0u));
+    amax_w[col] = aw;
+    float sj, ij;
+    smooth_factor(ax, aw, alpha, sj, ij);
+    s[col] = sj;
+    inv_s[col] = ij;
+  }
+  if (c == 0) atomicExch(arrivals + blockIdx.x, 0u);
 }
 
 }  // namespace
@@ -143,6 +210,43 @@ hipError_t launch_channel_amax(const void* x, bool bf16, int64_t rows, int64_t c
   else
     hipLaunchKernelGGL(k_channel_amax<false>, grid, dim3(kAmaxThreads), 0, st,
                        (const v4u*)x, rows, cols8, rpb, (unsigned*)amax);
+  return hipGetLastError();
+}
+
+size_t calibrate_smooth_scratch_bytes(int64_t K) {
+  if (K <= 0) return 0;
+  const int64_t strips = (K / 8 + kLanesPerRow - 1) / kLanesPerRow;
+  return (size_t)((4 * K + 255) / 256 * 256 + 4 * strips);
+}
+
+hipError_t launch_calibrate_smooth(const void* xc, int64_t cal_rows, const void* w,
+                                   int64_t w_rows, bool bf16, int64_t K, double alpha,
+                                   float* amax_x, float* amax_w, float* s, float* inv_s,
+                                   void* scratch, hipStream_t st) {
+  if (K == 0) return hipSuccess;
+  const int64_t cols8 = K / 8;
+  const int64_t strips = (cols8 + kLanesPerRow - 1) / kLanesPerRow;
+  // about 512 blocks over both matrices, the same rows per block for both
+  // (measured: 1024 blocks lose 1-6 us to the arrival protocol on 4096-channel
+  // layers, 256 blocks lose streaming rate on the larger weights)
+  const int64_t target = (512 + strips - 1) / strips;
+  int64_t rpb = (cal_rows + w_rows + target - 1) / target;
+  rpb = (rpb + kRowsPerGroup - 1) / kRowsPerGroup * kRowsPerGroup;
+  if (rpb < kRowsPerGroup) rpb = kRowsPerGroup;
+  const int64_t rb_x = (cal_rows + rpb - 1) / rpb;
+  int64_t rb_w = (w_rows + rpb - 1) / rpb;
+  if (rb_x + rb_w == 0) rb_w = 1;  // no rows at all: one empty block per strip still forms s
+  unsigned* acc_w = (unsigned*)scratch;
+  unsigned* arrivals = acc_w + (K + 63) / 64 * 64;
+  const dim3 grid((unsigned)strips, (unsigned)(rb_x + rb_w));
+  if (bf16)
+    hipLaunchKernelGGL(k_calibrate_smooth<true>, grid, dim3(kAmaxThreads), 0, st,
+                       (const v4u*)xc, cal_rows, (const v4u*)w, w_rows, cols8, rpb, rb_x, alpha,
+                       (unsigned*)amax_x, acc_w, arrivals, amax_w, s, inv_s);
+  else
+    hipLaunchKernelGGL(k_calibrate_smooth<false>, grid, dim3(kAmaxThreads), 0, st,
+                       (const v4u*)xc, cal_rows, (const v4u*)w, w_rows, cols8, rpb, rb_x, alpha,
+                       (unsigned*)amax_x, acc_w, arrivals, amax_w, s, inv_s);
   return hipGetLastError();
 }
 

@@ -18,6 +18,13 @@ hipError_t launch_channel_amax(const void* x, bool bf16, int64_t rows, int64_t c
                                hipStream_t st);
 hipError_t launch_smooth_factors(const float* ax, const float* aw, int64_t K, double alpha,
                                  float* s, float* inv_s, hipStream_t st);
+// Scratch of launch_calibrate_smooth: the weight maximum accumulator (K
+// floats, padded to 256 bytes) and one arrival counter per 256 channels.
+size_t calibrate_smooth_scratch_bytes(int64_t K);
+hipError_t launch_calibrate_smooth(const void* xc, int64_t cal_rows, const void* w,
+                                   int64_t w_rows, bool bf16, int64_t K, double alpha,
+                                   float* amax_x, float* amax_w, float* s, float* inv_s,
+                                   void* scratch, hipStream_t st);
 // fmt: 0 = symmetric INT8 codes, 1 = FP8 E4M3 codes.  norm (INT8 only): the
 // rows are RMS-norm inputs and col_scale the folded norm weight; the row scale
 // is divided by the row's rms (with eps).

@@ -1,14 +1,11 @@
-// Smoothing factors s_j = amax_x[j]^alpha / amax_w[j]^(1 - alpha) and inv_s_j = 1 / s_j.
+// Smoothing factors s_j = amax_x[j]^alpha / amax_w[j]^(1 - alpha) and inv_s_j = 1 / s_j
+// (the rounding is that of smooth_factor in smooth_factor.h).
 //
 // Method: jisaku.com glossary page "SmoothQuant", section "ハイパーパラメータ α".
-// The factor is formed in fp64 (device pow and one IEEE division) and rounded
-// once to fp32; the reciprocal is one IEEE fp32 division.  alpha = 1 and
-// alpha = 0 take the formula's exact values (s = amax_x, s = 1 / amax_w) so
-// those limits do not depend on the accuracy of pow.  A channel with a zero
-// maximum on either side is left unscaled (s = 1).
 //
 // K is at most a few tens of thousands: one thread per channel, launch bound.
 #include "common.h"
+#include "smooth_factor.h"
 
 namespace w8a8 {
 
@@ -20,19 +17,7 @@ __global__ __launch_bounds__(256) void k_smooth_factors(const float* __restrict_
                                                         float* __restrict__ inv_s) {
   const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= K) return;
-  const double a = ax[j], b = aw[j];
-  float sj;
-  if (a == 0.0 || b == 0.0) {
-    sj = 1.0f;
-  } else if (alpha == 1.0) {
-    sj = (float)a;
-  } else if (alpha == 0.0) {
-    sj = (float)(1.0 / b);
-  } else {
-    sj = (float)(pow(a, alpha) / pow(b, 1.0 - alpha));
-  }
-  s[j] = sj;
-  inv_s[j] = 1.0f / sj;
+  smooth_factor(ax[j], aw[j], alpha, s[j], inv_s[j]);
 }
 
 // out_j = a_j * b_j, one fp32 rounding: the folded weight of a per-channel
