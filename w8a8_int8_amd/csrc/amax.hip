@@ -23,6 +23,10 @@
 // Measured on fp16 weights of 4096 to 57344 rows: 512-byte row pieces stream
 // at 5.5-6.4 TB/s where 128-byte pieces (a strip of 64 columns) reached
 // 5.0-5.6 TB/s.
+//
+// k_calibrate_smooth runs the same strip code over a calibration batch and a
+// weight in one grid and forms the smoothing factors at the end of each strip
+// (its comment gives the cross-block protocol).
 #include "common.h"
 #include "smooth_factor.h"
 
