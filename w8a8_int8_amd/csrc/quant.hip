@@ -287,15 +287,26 @@ hipError_t launch_scale_quant_rows(const void* x, bool bf16, int64_t rows, int64
 // every element, so they decide codes; they are therefore computed without
 // any dependence on a summation order.  Every finite fp16 value is an integer
 // multiple of 2^-24, so with X = x * 2^24 (|X| < 2^41) the sums S1 = sum X and
-// S2 = sum X^2 are exact integers: S1 in int64, and S2 from the split
-// |X| = hi * 2^20 + lo as sum hi^2 * 2^40 + 2 sum hi lo * 2^20 + sum lo^2, three
-// int64 sums (each below 2^58 for rows of at most 65536).  Integer sums are
-// order free, so the wave and block reductions are exact.  Then, once per row:
+// S2 = sum X^2 are exact integers.  Then, once per row:
 //   mean = f32(f64(f64(S1) / (K 2^24)))
 //   var  = f32(f64(f64(K S2 - S1^2) / (K^2 2^48)))     (population variance)
 //   r    = RN32(1 / RN32(sqrt(RN32(var + eps)))), or 0 when var + eps == 0
 // and per element v = RN32(RN32(RN32(RN32(x - mean) * r) * g) + b), one IEEE
 // fp32 operation per step, followed by the per-row quantizer.
+//
+// The sums are taken in fp64 up to the wave level, where no addition rounds:
+// a wave covers at most 4096 elements (64 lanes, 8 chunks of 8 per lane).
+//   - sum x: every partial sum is a multiple of 2^-24 below 4096 * 65504 <
+//     2^28, so it needs at most 52 significant bits.
+//   - sum x^2: x^2 is exact in fp64 (11-bit significand squared) and t =
+//     x^2 * 2^8 is a multiple of 2^-40 below 2^40.  t splits exactly into
+//     its integer part (summed: below 2^52) and its fraction (summed: a
+//     multiple of 2^-40 below 2^12), each within 52 bits.
+// So the wave sums are the exact values, and each becomes an int64 in
+// fixed units (S1 in 2^-24, the integer part in 2^-8 of x^2, the fraction in
+// 2^-48) for the order-free integer sum across waves.  That keeps the VALU
+// cost near nine fp64 operations per element where 64-bit integer squares
+// took several times as many.
 namespace {
 
 // Correctly rounded (to nearest even) conversion of a nonnegative 128-bit
@@ -311,22 +322,26 @@ __device__ __forceinline__ double u128_to_f64(unsigned __int128 v) {
   return __builtin_ldexp((double)top, 64 - lz);
 }
 
-// Sums of the LayerNorm statistics carried through the reductions.
+// Per-wave sums of the LayerNorm statistics, as integers in fixed units.
 struct LnSums {
-  long long s1;                     // sum X
-  unsigned long long hh, hl, ll;    // sum hi^2, sum hi lo, sum lo^2
+  long long s1;  // sum x, units of 2^-24
+  long long ta;  // sum of the integer parts of x^2 * 2^8, units of 2^-8 of x^2
+  long long tb;  // sum of the fractions of x^2 * 2^8, units of 2^-48 of x^2
 };
 
 __device__ __forceinline__ LnSums ln_add(LnSums a, const LnSums& b) {
   a.s1 += b.s1;
-  a.hh += b.hh;
-  a.hl += b.hl;
-  a.ll += b.ll;
+  a.ta += b.ta;
+  a.tb += b.tb;
   return a;
 }
 
+// Up to four chunks per thread the registers are held to 64, so that two
+// blocks of 1024 threads fit on a CU (one block per CU measured 15% slower).
 template <int CPT>
-__global__ __launch_bounds__(1024) void k_layernorm_quant_rows(const v4u* __restrict__ x,
+__global__ __attribute__((amdgpu_flat_work_group_size(64, 1024),
+                          amdgpu_waves_per_eu(CPT <= 4 ? 8 : 4))) void
+k_layernorm_quant_rows(const v4u* __restrict__ x,
                                                                int cols8,
                                                                const float4* __restrict__ gv,
                                                                const float4* __restrict__ bv,
@@ -344,32 +359,29 @@ __global__ __launch_bounds__(1024) void k_layernorm_quant_rows(const v4u* __rest
     xv[i] = c < cols8 ? __builtin_nontemporal_load(x + row * cols8 + c) : v4u{0u, 0u, 0u, 0u};
   }
 
-  // pass 1: exact integer sums (chunks past the row hold zeros and add nothing)
-  LnSums acc = {0, 0, 0, 0};
+  // pass 1: exact fp64 sums within the wave (chunks past the row hold zeros
+  // and add nothing)
+  double s1 = 0.0, ta = 0.0, tb = 0.0;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const unsigned h = (e & 1) ? (xv[i][e / 2] >> 16) : (xv[i][e / 2] & 0xffffu);
-      const unsigned ex = (h >> 10) & 0x1f, mant = h & 0x3ff;
-      const unsigned long long mag =
-          ex ? ((unsigned long long)(1024u + mant) << (ex - 1)) : (unsigned long long)mant;
-      acc.s1 += (h & 0x8000u) ? -(long long)mag : (long long)mag;
-      const unsigned hi = (unsigned)(mag >> 20), lo = (unsigned)(mag & 0xfffffu);
-      acc.hh += (unsigned long long)hi * hi;
-      acc.hl += (unsigned long long)hi * lo;
-      acc.ll += (unsigned long long)lo * lo;
+      const double xd = (double)elem<false>(xv[i], e);
+      s1 += xd;
+      const double t = (xd * xd) * 256.0;
+      const double ti = __builtin_trunc(t);
+      ta += ti;
+      tb += t - ti;
     }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
-    LnSums o;
-    o.s1 = __shfl_xor(acc.s1, off, kWave);
-    o.hh = __shfl_xor(acc.hh, off, kWave);
-    o.hl = __shfl_xor(acc.hl, off, kWave);
-    o.ll = __shfl_xor(acc.ll, off, kWave);
-    acc = ln_add(acc, o);
+    s1 += __shfl_xor(s1, off, kWave);
+    ta += __shfl_xor(ta, off, kWave);
+    tb += __shfl_xor(tb, off, kWave);
   }
+  const LnSums acc = {(long long)(s1 * 16777216.0), (long long)ta,
+                      (long long)(tb * 1099511627776.0)};
   __shared__ LnSums red[16];
   __shared__ float stat[2];
   __shared__ float redm[16];
@@ -379,7 +391,8 @@ __global__ __launch_bounds__(1024) void k_layernorm_quant_rows(const v4u* __rest
     LnSums t = red[0];
     for (int w = 1; w < nwaves; ++w) t = ln_add(t, red[w]);
     const long long K = (long long)cols8 * 8;
-    const __int128 s2 = ((__int128)t.hh << 40) + ((__int128)t.hl << 21) + (__int128)t.ll;
+    // sum X^2 = sum x^2 * 2^48 = ta * 2^40 + tb
+    const __int128 s2 = ((__int128)t.ta << 40) + (__int128)t.tb;
     const __int128 v = (__int128)K * s2 - (__int128)t.s1 * (__int128)t.s1;  // >= 0
     const double kd = (double)K;
     const float mean = (float)((double)t.s1 / (kd * 16777216.0));
