@@ -66,7 +66,7 @@ def sample(n, k, seed):
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("rows,cols", [(1, 16), (3, 48), (64, 512), (257, 4096),
-                                       (5, 65536), (7, 0), (4100, 11008), (2050, 28672)])
+                                       (5, 65536), (7, 0), (4100, 11008), (1027, 9008), (2050, 28672)])
 def test_scale_quant_rows_e4m3(dtype, rows, cols):
     x = rand_act(rows, cols, dtype, seed=rows + 5 * cols)
     if rows > 2:

@@ -138,7 +138,7 @@ def test_smooth_factors(alpha):
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("rows,cols", [(1, 16), (3, 48), (64, 512), (1025, 4096),
-                                       (2050, 7168), (4100, 11008), (33, 28672),
+                                       (2050, 7168), (4100, 11008), (1027, 9008), (33, 28672),
                                        (5, 65536), (7, 0)])
 def test_scale_quant_rows(dtype, rows, cols):
     x = rand_act(rows, cols, dtype, seed=rows + 3 * cols)

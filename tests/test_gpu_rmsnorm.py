@@ -65,7 +65,7 @@ def check(h, gamma, inv_s, eps, rows_idx=None):
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("rows,cols", [(1, 16), (3, 48), (64, 512), (1025, 4096), (2050, 7168),
-                                       (33, 28672), (5, 65536)])
+                                       (33, 28672), (5, 65536), (1027, 9008)])
 def test_rmsnorm_quant_rows(dtype, rows, cols):
     h, gamma, inv_s = case(rows, cols, dtype, rows * 7 + cols)
     if rows > 2:

@@ -254,7 +254,9 @@ hipError_t launch_scale_quant_rows(const void* x, bool bf16, int64_t rows, int64
   // where the block size reaches 1024), a whole number of waves.  Rows per
   // block: two while a thread holds two chunks, one beyond, which keeps the
   // fp32 row slice a thread carries between the passes at 32 values or fewer
-  // (more would cost occupancy).
+  // (more would cost occupancy).  The exception is rows of 8200 to 12288
+  // values (blocks of 9 to 12 waves, two per CU): four rows per block there
+  // measured 4-8% faster at 11008 columns, and slower at 4096 and 16384.
   int G = (cols8 + 1) / 2;
   G = ((G + kWave - 1) / kWave) * kWave;
   if (G < kWave) G = kWave;
@@ -263,8 +265,11 @@ hipError_t launch_scale_quant_rows(const void* x, bool bf16, int64_t rows, int64
   switch (cpt <= 1 ? 1 : cpt) {
     case 1: return launch_cfg<1, 4>(x, bf16, fmt, rows, cols8, G, col_scale, norm, eps, q,
                                           row_scale, st);
-    case 2: return launch_cfg<2, 2>(x, bf16, fmt, rows, cols8, G, col_scale, norm, eps, q,
-                                          row_scale, st);
+    case 2:
+      if (cols8 > 1024 && cols8 <= 1536)
+        return launch_cfg<2, 4>(x, bf16, fmt, rows, cols8, G, col_scale, norm, eps, q, row_scale,
+                                st);
+      return launch_cfg<2, 2>(x, bf16, fmt, rows, cols8, G, col_scale, norm, eps, q, row_scale, st);
     case 3: return launch_cfg<3, 1>(x, bf16, fmt, rows, cols8, G, col_scale, norm, eps, q,
                                           row_scale, st);
     case 4: return launch_cfg<4, 1>(x, bf16, fmt, rows, cols8, G, col_scale, norm, eps, q,
