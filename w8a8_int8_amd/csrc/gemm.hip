@@ -496,9 +496,8 @@ k_gemm_i8(const int8_t* __restrict__ qa, const int8_t* __restrict__ qb, int M, i
 // streaming, so the tiling follows the weight.  A block owns 16 output
 // channels over all of K and all M tokens; its NW waves split K (below: by
 // interleaved 64-deep k steps, or by contiguous ranges when K is long).  Each
-// step is one
-// v_mfma_i32_16x16x64_i8 per 16 tokens with the weight fragment as the first
-// operand (16 channels x 64 k) and the activation fragment as the second
+// step is one v_mfma_i32_16x16x64_i8 per 16 tokens with the weight fragment
+// as the first operand (16 channels x 64 k) and the activation fragment as the second
 // (64 k x 16 tokens).  Operands load straight into registers with buffer
 // loads, U steps in flight per wave; token rows past M and channel rows past N
 // are outside their buffer resources and read as zero without touching
