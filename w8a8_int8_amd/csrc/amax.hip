@@ -36,12 +36,12 @@ namespace {
 
 constexpr int kAmaxThreads = 256;
 constexpr int kAmaxWaves = kAmaxThreads / kWave;
-constexpr int kAmaxUnroll = 8;
+constexpr int kAmaxUnroll = 8;                                      // loads in flight per lane
+constexpr int kFusedUnroll = 16;                                    // ... in k_calibrate_smooth
 constexpr int kLanesPerRow = 32;                                    // 16-byte chunks of a row piece
 constexpr int kStripCols = kLanesPerRow * 8;                        // 256 columns per block
 constexpr int kRowsPerLoad = kWave / kLanesPerRow;                  // 2 rows per wave load
 constexpr int kRowsPerGroup = kRowsPerLoad * kAmaxWaves;            // 8 rows per block step
-constexpr int kRowsPerBatch = kRowsPerGroup * kAmaxUnroll;          // 64 rows in flight
 constexpr int kMaxRowRanges = 128;                                  // atomics per column
 static_assert(kStripCols == kAmaxThreads, "one column per thread in the fold");
 
@@ -59,9 +59,11 @@ __device__ __forceinline__ v4u vmax(v4u m, v4u v) {
 // The maximum of |x| over rows [r_begin, r_end) of the block's 256-column
 // strip, as a 16-bit magnitude pattern, for the column of this thread
 // (column blockIdx.x * 256 + threadIdx.x); 0 for columns past the end.
-template <bool BF16>
+// U loads in flight per lane, U * kRowsPerGroup rows per batch.
+template <bool BF16, int U>
 __device__ __forceinline__ unsigned short strip_max(const v4u* __restrict__ x, int64_t cols8,
                                                     int64_t r_begin, int64_t r_end) {
+  constexpr int kRowsPerBatch = kRowsPerGroup * U;
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
   const int sub = lane / kLanesPerRow;  // row within a wave load
@@ -73,25 +75,25 @@ __device__ __forceinline__ unsigned short strip_max(const v4u* __restrict__ x, i
     const v4u* p = x + chunk;
     int64_t r = r_begin + wave * kRowsPerLoad + sub;
     // full batches: U loads per lane in flight, no per-load bounds test
-    for (; r + (int64_t)(kAmaxUnroll - 1) * kRowsPerGroup < r_end; r += kRowsPerBatch) {
-      v4u v[kAmaxUnroll];
+    for (; r + (int64_t)(U - 1) * kRowsPerGroup < r_end; r += kRowsPerBatch) {
+      v4u v[U];
 #pragma unroll
-      for (int u = 0; u < kAmaxUnroll; ++u)
+      for (int u = 0; u < U; ++u)
         v[u] = __builtin_nontemporal_load(p + (r + (int64_t)u * kRowsPerGroup) * cols8);
 #pragma unroll
-      for (int u = 0; u < kAmaxUnroll; ++u) m = vmax(m, v[u]);
+      for (int u = 0; u < U; ++u) m = vmax(m, v[u]);
     }
     // the last partial batch: all of its loads issued together as well (a
     // row-by-row tail would pay one memory round trip per row group)
     if (r < r_end) {
-      v4u v[kAmaxUnroll];
+      v4u v[U];
 #pragma unroll
-      for (int u = 0; u < kAmaxUnroll; ++u) {
+      for (int u = 0; u < U; ++u) {
         const int64_t ru = r + (int64_t)u * kRowsPerGroup;
         v[u] = ru < r_end ? __builtin_nontemporal_load(p + ru * cols8) : v4u{0u, 0u, 0u, 0u};
       }
 #pragma unroll
-      for (int u = 0; u < kAmaxUnroll; ++u) m = vmax(m, v[u]);
+      for (int u = 0; u < U; ++u) m = vmax(m, v[u]);
     }
   }
   // fold the lanes that hold the same chunk (lanes l and l ^ 32)
@@ -127,7 +129,8 @@ __global__ __launch_bounds__(kAmaxThreads) void k_channel_amax(const v4u* __rest
                                                                int64_t rows_per_block,
                                                                unsigned* __restrict__ amax_bits) {
   const int64_t r_begin = (int64_t)blockIdx.y * rows_per_block;
-  const unsigned short b = strip_max<BF16>(x, cols8, r_begin, min(rows, r_begin + rows_per_block));
+  const unsigned short b =
+      strip_max<BF16, kAmaxUnroll>(x, cols8, r_begin, min(rows, r_begin + rows_per_block));
   const int64_t col = (int64_t)blockIdx.x * kStripCols + threadIdx.x;
   if (col < cols8 * 8 && b != 0)  // +0 never raises a non-negative running max
     atomicMax(amax_bits + col, __float_as_uint(widen16(b, BF16)));
@@ -161,7 +164,8 @@ __global__ __launch_bounds__(kAmaxThreads) void k_calibrate_smooth(
   const v4u* x = cal ? xc : w;
   const int64_t rows = cal ? cal_rows : w_rows;
   const int64_t r_begin = (cal ? (int64_t)blockIdx.y : (int64_t)blockIdx.y - rb_x) * rows_per_block;
-  const unsigned short b = strip_max<BF16>(x, cols8, r_begin, min(rows, r_begin + rows_per_block));
+  const unsigned short b =
+      strip_max<BF16, kFusedUnroll>(x, cols8, r_begin, min(rows, r_begin + rows_per_block));
   const int c = threadIdx.x;
   const int64_t col = (int64_t)blockIdx.x * kStripCols + c;
   const bool live = col < cols8 * 8;
@@ -230,10 +234,12 @@ hipError_t launch_calibrate_smooth(const void* xc, int64_t cal_rows, const void*
   if (K == 0) return hipSuccess;
   const int64_t cols8 = K / 8;
   const int64_t strips = (cols8 + kLanesPerRow - 1) / kLanesPerRow;
-  // about 512 blocks over both matrices, the same rows per block for both
-  // (measured: 1024 blocks lose 1-6 us to the arrival protocol on 4096-channel
-  // layers, 256 blocks lose streaming rate on the larger weights)
-  const int64_t target = (512 + strips - 1) / strips;
+  // about 448 blocks over both matrices, the same rows per block for both,
+  // with 16 loads in flight per lane.  Measured on the Llama-2-7B layers:
+  // more blocks lose time to the arrival protocol (each strip's counter and
+  // each column's maximum take one atomic per row block, one after another),
+  // fewer lose streaming rate on the larger weights.
+  const int64_t target = (448 + strips - 1) / strips;
   int64_t rpb = (cal_rows + w_rows + target - 1) / target;
   rpb = (rpb + kRowsPerGroup - 1) / kRowsPerGroup * kRowsPerGroup;
   if (rpb < kRowsPerGroup) rpb = kRowsPerGroup;
