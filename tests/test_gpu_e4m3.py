@@ -203,7 +203,7 @@ def small_int_codes(rows, cols, seed):
 
 @pytest.mark.parametrize("out", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("M,N,K", [(37, 136, 80), (300, 520, 1040), (2048, 4096, 256),
-                                   (1, 8, 16), (32, 64, 65536)])
+                                   (1, 8, 16), (32, 64, 65536), (2000, 22000, 272)])
 def test_gemm_dequant_e4m3_exact_integers(out, M, N, K):
     """Products of integers |v| <= 16 and their partial sums (|.| <= 256 K
     < 2^24) are exact in fp32 in any order, so C is exact and y must equal the

@@ -219,17 +219,30 @@ def _tile_of_shape(M, N):
         score = fill * (M / (-(-M // bm) * bm)) * eff
         if score > best_score + 1e-9:
             best, best_score = (bm, bn), score
+    # two shapes in one grid: whole waves of 256 x 256 tiles, then 256 x 192
+    if best[0] == 256:
+        cyc = {256: 2339, 192: 1853, 128: 1404}
+        mt = -(-M // 256)
+        single = -(-(mt * -(-N // best[1])) // 256) * cyc[best[1]]
+        w = mt * -(-N // 256) // 256
+        if w >= 1 and (w * 256) % mt == 0 and w * 256 // mt * 256 < N:
+            nt2 = -(-(N - w * 256 // mt * 256) // 192)
+            if (w * cyc[256] + -(-(mt * nt2) // 256) * cyc[192]) * 100 <= single * 97:
+                return "two"
     return best
 
 
-@pytest.mark.parametrize("M,N,K,tile", [(2000, 22000, 272, (256, 256)), (2000, 12280, 272, (256, 192)),
-                                        (2000, 4088, 1040, (256, 128)), (130, 1000, 1040, (128, 128))])
+@pytest.mark.parametrize("M,N,K,tile", [(2000, 24560, 272, (256, 256)), (2000, 12280, 272, (256, 192)),
+                                        (2000, 4088, 1040, (256, 128)), (130, 1000, 1040, (128, 128)),
+                                        (2000, 22000, 272, "two"), (4000, 7160, 1040, "two")])
 def test_gemm_tiles_ragged(M, N, K, tile):
-    """Each tile of the tiled kernel with a partial last tile in M and in N and
-    a K that ends inside a 128-byte stage.  With the 256-row tiles, waves 0-3
-    load the rows of waves 4-7 as well, so the rows checked include both
-    halves of the first tile and the ragged last tile rows.  C is checked in
-    full (Freivalds) and exactly on those rows; Y on the same rows."""
+    """Each tile of the tiled kernel, and the grid of two tile shapes (whole
+    waves of 256 x 256 tiles, then 256 x 192 tiles over the last channels),
+    with a partial last tile in M and in N and a K that ends inside a
+    128-byte stage.  With the 256-row tiles, waves 0-3 load the rows of waves
+    4-7 as well, so the rows checked include both halves of the first tile and
+    the ragged last tile rows.  C is checked in full (Freivalds) and exactly
+    on those rows; Y on the same rows."""
     assert _tile_of_shape(M, N) == tile
     qa, qb = rand_codes(M, K, M + 3 * K), rand_codes(N, K, N + K + 7)
     c = host(w8.gemm_i32(qa, qb))
@@ -403,7 +416,7 @@ def test_workload_layer(name, li, alpha):
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("M,N,K", [(37, 136, 80), (300, 520, 1040), (2048, 4096, 256),
                                    (4000, 8184, 272), (5, 16, 0), (1, 264, 4104),
-                                   (2048, 12288, 4096), (3000, 6000, 272)])
+                                   (2048, 12288, 4096), (3000, 6000, 272), (2000, 22000, 272)])
 def test_gemm_float(dtype, M, N, K):
     """fp32-accumulated dense product: within K 2^-24 sum|a b| of the exact
     value before the final rounding, plus one unit of the output format."""
