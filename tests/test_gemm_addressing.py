@@ -1,0 +1,124 @@
+"""Operand addressing of the GEMM kernels, checked on the CPU.
+
+The kernels read their operands with raw buffer loads: the hardware compares
+a load's vector offset (plus its immediate offset) with the buffer
+resource's size and returns zero without touching memory when it is past
+the end; the scalar offset is added to the address but not compared.  This
+file models the offsets each kernel issues, lane by lane, and checks that
+every load the hardware would not mask reads 16 bytes inside a valid row of
+the operand: rows past M or N and chunks past K must be masked.  The model
+restates the kernels' index arithmetic (w8a8_int8_amd/csrc/gemm.hip), so a
+change there needs the same change here; the GPU parity tests cannot see an
+out-of-bounds read whose data only feeds discarded outputs.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+K_OOB = 0x40000000
+
+
+def tiled_loads(BM, BN, NST, WGM, WGN, M, N, K, tm, tn, row_offset_in_scalar=False):
+    """(operand, row_base, vector offset, scalar offset, num_records) of every
+    LDS-mode load one block of the tiled kernel issues (128-byte stages).
+    row_offset_in_scalar models the mistaken form in which the loads issued
+    for waves NW/2 .. NW-1 carry their row offset in the scalar offset."""
+    BK = 128
+    NW = WGM * WGN
+    CPR, RPI = BK // 16, 1024 // BK
+    RPW = 16 // CPR
+    LA, LB = BM // RPI // NW, BN // RPI // NW
+    spread = NST >= 3
+    half = (not spread) and NW == 8
+    nk = (K + BK - 1) // BK
+    # every stage the pipeline issues: 0 .. nk - 1 plus the zero-filled ones past the end
+    last = nk - 1 + (NST - 1 if spread else NST)
+    out = []
+    lane = np.arange(64)
+    lrow, lslot = lane // CPR, lane % CPR
+    for opnd, base, rows_tile, LX in (("a", tm * BM, BM, LA), ("b", tn * BN, BN, LB)):
+        size = M if opnd == "a" else N
+        recs = min(rows_tile, size - base) * K
+        for wave in range(NW // 2 if half else NW):
+            for h in range(2 if half else 1):
+                for i in range(LX):
+                    row = (i * NW + wave) * RPI + lrow
+                    kc = (lslot ^ ((row // RPW) % CPR)) << 4
+                    voff = row * K + kc
+                    ro = h * (NW // 2) * RPI * K
+                    for st in range(last + 1):
+                        k0 = st * BK
+                        if row_offset_in_scalar:
+                            out.append((opnd, base, np.where(k0 + kc >= K, K_OOB, voff), k0 + ro, recs))
+                        else:
+                            out.append((opnd, base, np.where(k0 + kc >= K, K_OOB, voff + ro), k0, recs))
+    return out
+
+
+def assert_in_bounds(loads, M, N, K):
+    for opnd, base, vo, so, recs in loads:
+        size = M if opnd == "a" else N
+        live = vo < recs  # what the hardware does not mask
+        off = vo[live].astype(np.int64) + so
+        row = base + off // K
+        col = off % K
+        assert (row < size).all() and (row >= 0).all(), (opnd, base)
+        assert (col + 16 <= K).all() and (col % 16 == 0).all(), (opnd, base)
+
+
+TILES = [  # BM, BN, NST, WGM, WGN: every tile the launcher can pick
+    (256, 256, 2, 2, 4),
+    (256, 192, 2, 4, 2),
+    (256, 128, 3, 4, 2),
+    (128, 128, 4, 2, 2),
+]
+
+
+@pytest.mark.parametrize("tile", TILES, ids=lambda t: f"{t[0]}x{t[1]}")
+@pytest.mark.parametrize("M,N,K", [(2000, 8192, 256), (37, 136, 1040), (300, 520, 272),
+                                   (2048, 4104, 144), (2, 8, 16), (259, 200, 400)])
+def test_tiled_kernel_loads_stay_in_bounds(tile, M, N, K):
+    BM, BN, NST, WGM, WGN = tile
+    mt, nt = -(-M // BM), -(-N // BN)
+    # the last tile in each direction is where the rows run out
+    for tm in sorted({0, mt - 1}):
+        for tn in sorted({0, nt - 1}):
+            assert_in_bounds(tiled_loads(BM, BN, NST, WGM, WGN, M, N, K, tm, tn), M, N, K)
+
+
+def test_the_scalar_offset_is_not_a_row_offset():
+    """The case that motivated this file: a 256 x 256 tile whose last token
+    tile ends inside a 64-row group (M = 2000).  Loads issued for waves 4-7
+    carry their 32-row offset in the vector offset.  The model with that
+    offset moved into the (unchecked) scalar offset must fail, reading rows
+    past M."""
+    M, N, K = 2000, 8192, 256
+    assert_in_bounds(tiled_loads(256, 256, 2, 2, 4, M, N, K, M // 256, 0), M, N, K)
+    with pytest.raises(AssertionError):
+        assert_in_bounds(tiled_loads(256, 256, 2, 2, 4, M, N, K, M // 256, 0,
+                                     row_offset_in_scalar=True), M, N, K)
+
+
+def skinny_loads(M, N, K, n0, MT, NW=8, U=8):
+    """Loads of one block of the few-token kernel: 16 weight rows, all of K."""
+    lane = np.arange(64)
+    r16, kq = lane % 16, lane // 16
+    nsteps = -(-K // 64)
+    out = []
+    recs_w = min(16, N - n0) * K
+    recs_x = M * K
+    for st in range(nsteps + NW * U):  # steps past the end are issued out of range
+        k0 = st * 64
+        out_k = (st >= nsteps) | (k0 + kq * 16 >= K)
+        out.append(("b", n0, np.where(out_k, K_OOB, r16 * K + kq * 16), k0, recs_w))
+        for t in range(MT):
+            out.append(("a", 0, np.where(out_k, K_OOB, (t * 16 + r16) * K + kq * 16), k0, recs_x))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16392, 4096), (13, 136, 1040), (31, 4104, 16384)])
+def test_few_token_kernel_loads_stay_in_bounds(M, N, K):
+    MT = -(-M // 16)
+    for n0 in sorted({0, (N - 1) // 16 * 16}):
+        assert_in_bounds(skinny_loads(M, N, K, n0, MT), M, N, K)

@@ -55,8 +55,9 @@
 // its slot.
 //
 // Edges: the buffer resource of each operand tile ends at its last valid row,
-// so rows past M or N load as zero; chunks past K use an out-of-range offset
-// and load as zero too.  Blocks are dispatched round-robin over the 8 XCDs;
+// and every row offset is part of the range-checked vector offset, so rows
+// past M or N load as zero without a memory access; chunks past K use an
+// out-of-range offset and load as zero too.  Blocks are dispatched round-robin over the 8 XCDs;
 // tile indices are remapped so each XCD (own L2) gets a contiguous run of
 // tiles, ordered token-tile fastest in groups of 8 token tiles.
 //
@@ -272,31 +273,34 @@ __device__ __forceinline__ void gemm_tile(const int8_t* __restrict__ qa,
   // wave's own loads (i < LA activations, then weights), for h = 1 those of
   // wave + NW / 2, issued on its behalf (see the pipeline below).  Rows of
   // wave + NW / 2 lie NW / 2 * RPI rows further down with the same chunk
-  // swizzle, so they differ only in the scalar offset.  Loads j0 <= j < j1
-  // are issued.  A stage past the end (st >= nk) is issued with out-of-range
-  // offsets: it moves no data, keeps every wave's per-stage load count
-  // constant (so fixed vmcnt values serve every iteration) and only touches
-  // the slot that the stage would have used, which no live stage occupies.
+  // swizzle.  That row offset goes into the vector offset, the one the
+  // hardware compares with the resource's size (the scalar offset, which
+  // carries k0, is not range checked), so a row past the tile's last valid
+  // one reads zero and touches no memory.  Loads j0 <= j < j1 are issued.
+  // A stage past the end (st >= nk) is issued with out-of-range offsets: it
+  // moves no data, keeps every wave's per-stage load count constant (so
+  // fixed vmcnt values serve every iteration) and only touches the slot that
+  // the stage would have used, which no live stage occupies.
   auto dma = [&](int st, int j0, int j1) {
     const int k0 = st * BK;
     int8_t* slot = lds + (st % NST) * SLOT;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int so = k0 + h * (NW / 2) * RPI * K;
+      const int ro = h * (NW / 2) * RPI * K;
       const int w = wave + h * (NW / 2);
 #pragma unroll
       for (int i = 0; i < LA; ++i) {
         if (h * L + i < j0 || h * L + i >= j1) continue;
-        const int vo = (k0 + kc_a[i] >= K) ? kOob : voff_a[i];
+        const int vo = (k0 + kc_a[i] >= K) ? kOob : voff_a[i] + ro;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ra, (lds_void_t*)(slot + (i * NW + w) * 1024), 16, vo, so, 0, 0);
+            ra, (lds_void_t*)(slot + (i * NW + w) * 1024), 16, vo, k0, 0, 0);
       }
 #pragma unroll
       for (int i = 0; i < LB; ++i) {
         if (h * L + LA + i < j0 || h * L + LA + i >= j1) continue;
-        const int vo = (k0 + kc_b[i] >= K) ? kOob : voff_b[i];
+        const int vo = (k0 + kc_b[i] >= K) ? kOob : voff_b[i] + ro;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rb, (lds_void_t*)(slot + BM * BK + (i * NW + w) * 1024), 16, vo, so, 0, 0);
+            rb, (lds_void_t*)(slot + BM * BK + (i * NW + w) * 1024), 16, vo, k0, 0, 0);
       }
     }
   };
