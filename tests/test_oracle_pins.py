@@ -232,6 +232,106 @@ def test_quantize_error_bound():
     assert (err <= d[:, None] / 2 * (1 + 2 ** -13)).all()
 
 
+def _fp32_neighbours(t: np.ndarray, spread: int = 6) -> np.ndarray:
+    """Each fp32 value of t and its `spread` neighbours on either side."""
+    t = np.ascontiguousarray(t, dtype=np.float32)
+    steps = np.arange(-spread, spread + 1, dtype=np.int64)
+    return (t.view(np.int32).astype(np.int64)[:, None] + steps[None, :]).astype(np.int32).view(
+        np.float32).ravel()
+
+
+def test_quantizer_reading_multiplies_by_the_rounded_reciprocal():
+    """Reading R9: code = RNE(RN32(v * RN32(127 / m))), not RNE(RN32(v / RN32(m / 127))).
+
+    The page fixes the INT8 range (section "Activation外れ値問題") but not how
+    a value is divided by the step.  The two readings differ only where
+    v * 127 / m lies within an fp32 ulp of a half-integer, so the cases are
+    crafted: for several row maxima m, the fp32 neighbours of the preimages
+    (k + 1/2) m / 127 of every midpoint, kept where numpy's fp32 arithmetic
+    says the readings part.  Each kept case is then decided with exact
+    rationals (tests/exact.py): the oracle must give the multiply reading's
+    code, which must differ from the divide reading's."""
+    f32 = np.float32
+    cases = []
+    for m in f32([3, 7, 11, 13, 0.3, 5e-3, 91.7, 1234.5, 3 * 2.0 ** -20]):
+        k = np.arange(0, 127, dtype=np.float64)
+        cand = _fp32_neighbours(((k + 0.5) * float(m) / 127).astype(f32))
+        cand = cand[np.abs(cand) < m]
+        a = np.rint((cand * (f32(127) / m)).astype(f32))
+        b = np.rint((cand / (m / f32(127))).astype(f32))
+        for j, c in enumerate(cand[a != b][:3]):
+            cases.append((m, c if j % 2 == 0 else -c))
+    assert len(cases) >= 20
+    rows = np.zeros((len(cases), 2), dtype=np.float32)
+    for t, (m, c) in enumerate(cases):
+        rows[t] = (m, c)
+    q, d = oracle.quantize_rows(rows)
+    for t, (m, c) in enumerate(cases):
+        r = rn32(Fraction(127) / F(m))
+        delta = rn32(F(m) / 127)
+        want = _nearest_code(F(rn32(F(c) * F(r))))
+        alt = _nearest_code(F(rn32(F(c) / F(delta))))
+        assert want != alt, (m, c)
+        assert int(q[t, 1]) == want and int(q[t, 0]) == 127 and F(d[t]) == F(delta), (m, c)
+
+
+def test_smoothing_reading_multiplies_by_the_stored_inverse():
+    """Reading R7: X~ = X s^-1 (section "平滑化変換の数学") is applied as
+    RN32(x * inv_s) with the stored inv_s, not as a division RN32(x / s) by
+    s = RN32(1 / inv_s).  Crafted rows [127, x] with inv_s = [1, c]: the row
+    maximum is 127, so r = 1 and the code of x is RNE(RN32(x * c)) itself.
+    c runs over the fp32 neighbours of (k + 1/2) / x, kept where numpy's fp32
+    arithmetic says the two readings part; exact rationals then decide each
+    case, and the oracle must follow the multiply reading."""
+    f32 = np.float32
+    xs = np.array([3, 5.5, 7.25, 11, 13.125, 17, 29.5, 0.75, 1.375], dtype=np.float16)
+    cases = []
+    for xc in xs:
+        k = np.arange(1, 126, dtype=np.float64)
+        cand = _fp32_neighbours(((k + 0.5) / float(xc)).astype(f32))
+        x32 = f32(xc)
+        a = np.rint((x32 * cand).astype(f32))
+        b = np.rint((x32 / (f32(1) / cand).astype(f32)).astype(f32))
+        for j, c in enumerate(cand[a != b][:3]):
+            cases.append((xc if j % 2 == 0 else -xc, c))
+    assert len(cases) >= 20
+    for xc, c in cases:
+        x = np.array([[127, xc]], dtype=np.float16)
+        inv_s = np.array([1.0, c], dtype=np.float32)
+        q, d = oracle.scale_quant_rows(x, "f16", inv_s)
+        want = _nearest_code(F(rn32(F(xc) * F(c))))
+        alt = _nearest_code(F(rn32(F(xc) / F(rn32(Fraction(1) / F(c))))))
+        assert want != alt, (xc, c)
+        assert int(q[0, 1]) == want and float(d[0]) == 1.0, (xc, c)
+
+
+def _wide_fp32(shape, seed):
+    g = np.random.default_rng(seed)
+    return (g.standard_normal(shape) * np.exp(g.uniform(-20, 20, shape))).astype(np.float32)
+
+
+def test_apply_col_scale_is_one_rounded_product():
+    """apply_col_scale(v, c)[t, j] == RN32(v[t, j] * c[j]) exactly (exact
+    rationals), on values spread over 2^-29 .. 2^29."""
+    v = _wide_fp32((6, 40), 31)
+    c = _wide_fp32((40,), 32)
+    got = oracle.apply_col_scale(v, c)
+    assert got.dtype == np.float32
+    for t in range(6):
+        for j in range(40):
+            assert F(got[t, j]) == F(rn32(F(v[t, j]) * F(c[j]))), (t, j)
+
+
+def test_fold_norm_weight_is_one_rounded_product():
+    """g_j = RN32(gamma_j * inv_s_j) exactly (exact rationals)."""
+    gamma = _wide_fp32((300,), 33)
+    inv_s = _wide_fp32((300,), 34)
+    g = oracle.fold_norm_weight(gamma, inv_s)
+    assert g.dtype == np.float32
+    for j in range(300):
+        assert F(g[j]) == F(rn32(F(gamma[j]) * F(inv_s[j]))), j
+
+
 def test_golden_page_outlier_example():
     """The page's ordinary / outlier channel values (tests/golden, cited there).
 
