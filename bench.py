@@ -350,6 +350,17 @@ def decode_sweep(wl, layers, reps):
     return out
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, layers, alpha, min_seconds=10.0):
     """The CPU oracle, as it stands, over one step of the same workload."""
     import oracle
@@ -376,6 +387,9 @@ def cpu_baseline(wl, layers, alpha, min_seconds=10.0):
         steps += 1
     dt = time.perf_counter() - t0
     return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": int(threads),
+            "affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+            "threads_note": "the exact integer product runs as an fp64 BLAS product on `cores` "
+                            "threads; the other oracle steps are numpy on one thread",
             "kind": "oracle", "seconds": round(dt, 3), "steps": steps,
             "sample": (f"{steps} full step(s) of {wl.name} on the host: for each of the "
                        f"{len(layers)} layers, amax over one {wl.cal_batch}-token calibration "

@@ -43,6 +43,45 @@ def test_library_loads_and_exports_header_symbols():
     assert lib.w8a8_abi_version() == 4
 
 
+def declared_prototypes():
+    """name -> list of parameter declarations, from the header's prototypes."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(w8a8_[a-z0-9_]+)\s*\(([^)]*)\)\s*;", text):
+        params = [p.strip() for p in m.group(2).split(",") if p.strip() and p.strip() != "void"]
+        out[m.group(1)] = params
+    return out
+
+
+def test_binding_prototypes_match_the_header():
+    """The binding's argument lists follow the header: same count, and the
+    pointer / integer / floating kind of every parameter."""
+    def kind_decl(p):
+        if "*" in p or "hipStream_t" in p:
+            return "ptr"
+        if p.startswith("double") or p.startswith("float"):
+            return "fp"
+        return "int"
+
+    def kind_ct(t):
+        if t is ctypes.c_void_p:
+            return "ptr"
+        if t in (ctypes.c_double, ctypes.c_float):
+            return "fp"
+        return "int"
+
+    decl = declared_prototypes()
+    assert sorted(decl) == sorted(_lib.PROTOTYPES)
+    for name, params in decl.items():
+        args = _lib.PROTOTYPES[name][1]
+        assert [kind_decl(p) for p in params] == [kind_ct(t) for t in args], name
+    # the two calls whose form departs from the first sketch of the boundary:
+    # device-side smoothing factors on a stream, and a workspace size that
+    # depends on N (the split-K partial sums are S x M x N)
+    assert decl["w8a8_smooth_factors"][-1].startswith("hipStream_t")
+    assert [p.split()[-1] for p in decl["w8a8_linear_workspace_bytes"]] == ["M", "N", "K"]
+
+
 def test_status_strings():
     lib = _lib.load()
     for code in range(0, 7):

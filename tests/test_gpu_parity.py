@@ -357,7 +357,9 @@ def _workload_cases():
 @pytest.mark.parametrize("name,li,alpha", _workload_cases())
 def test_workload_layer(name, li, alpha):
     """Full-size layer through the calls the benchmark times, against the oracle:
-    amax, s, inv_s, qW, sw, qX and sx in full; Y and C on sampled token rows."""
+    amax, s, inv_s, qW, sw, qX and sx in full; C of sampled token rows against
+    the oracle's product, all of C by the Freivalds check, then every element
+    of the runtime forward's Y against the oracle's dequant of that C."""
     wl = synth.WORKLOADS[name]
     L = wl.layers[li]
     dname = wl.dtype
@@ -403,6 +405,12 @@ def test_workload_layer(name, li, alpha):
         c = host(w8.gemm_i32(qx, p["qw"]))
         assert np.array_equal(c[rows], c_or)
         assert_freivalds(c, qx_or, qw_or, seed=M + 7 * li)
+        # C is now verified in full, so the oracle's dequant of it is the
+        # oracle's Y: every output of the product path, bit for bit
+        for m0 in range(0, M, 1024):
+            y_or_blk = oracle.dequant(c[m0:m0 + 1024], sx_or[m0:m0 + 1024], sw_or, dname)
+            assert_y_close(y_np[m0:m0 + 1024], y_or_blk, dname)
+        del c
         ys[M] = y_np
     # decode shapes: the first rows do not depend on how many rows follow
     ms = sorted(wl.M)
