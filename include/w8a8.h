@@ -28,8 +28,9 @@
  *     so the page's "W_j" (input channel j) is column j of that array.
  *   - Memory: pointers are DEVICE pointers on the current HIP device unless a
  *     comment says otherwise.  The caller allocates and owns every buffer; the
- *     library allocates nothing and keeps no mutable state, so concurrent calls
- *     on different streams are safe when their buffers do not overlap.
+ *     library allocates nothing and keeps no mutable state (the one exception
+ *     is the static scratch of w8a8_linear_noalloc, at the end), so concurrent
+ *     calls on different streams are safe when their buffers do not overlap.
  *   - Asynchrony: device work is enqueued on `stream` (0 = the null stream)
  *     and the call returns without synchronizing.
  *   - Errors: every check below runs on the host before any HIP call; a failed
@@ -55,7 +56,7 @@
 extern "C" {
 #endif
 
-#define W8A8_ABI_VERSION 4
+#define W8A8_ABI_VERSION 5
 
 /* Largest K for which 127 * 127 * K fits int32, so that every accumulator
  * (and every partial sum) of the INT8 product is exact in int32. */
@@ -69,6 +70,7 @@ typedef enum {
   W8A8_ERR_DTYPE = 4,     /* unknown dtype code */
   W8A8_ERR_ARG = 5,       /* another argument is out of range (alpha, workspace size) */
   W8A8_ERR_HIP = 6,       /* the HIP launch failed */
+  W8A8_ERR_TOO_LARGE = 7, /* w8a8_linear_noalloc: needs more than its static scratch */
 } w8a8_status_t;
 
 /* Storage type of activations, weights and outputs. */
@@ -361,6 +363,36 @@ size_t w8a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
 w8a8_status_t w8a8_linear(const void* x, int dtype, const float* inv_s, const int8_t* qw,
                           const float* sw, void* y, int64_t M, int64_t N, int64_t K,
                           void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * w8a8_linear without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation.  It computes exactly what w8a8_linear computes
+ * (the same kernels, bit-identical y) and takes its scratch (the INT8
+ * activations, their scales and the split-K partial sums) from a static
+ * device array of W8A8_NOALLOC_SCRATCH_BYTES inside the library.  It calls
+ * no allocating routine.  Every GPU the library runs on holds one such array
+ * until the process ends.
+ *
+ *   Arguments and shape rules as w8a8_linear, without workspace / ws_bytes.
+ *   Limit: w8a8_linear_workspace_bytes(M, N, K) <= W8A8_NOALLOC_SCRATCH_BYTES
+ *   (for example 2048 tokens at K = 28672, or 4096 tokens at K = 8192, and
+ *   every few-token call of up to 32 tokens at K <= 65536); larger calls return
+ *   W8A8_ERR_TOO_LARGE and enqueue nothing.
+ *   Sharing: all calls on one GPU share its array, which keeps the last
+ *   call's contents (nothing in it needs to start at zero).  Calls that
+ *   overlap on one GPU (concurrent streams, or host threads with the same
+ *   current device) race on it: the caller serialises them, for example by
+ *   issuing them on one stream.
+ *   The first call on each device looks up the array's device address
+ *   (hipGetSymbolAddress) and keeps it; make that first call outside graph
+ *   capture.
+ * Errors: those of w8a8_linear (ARG cannot occur), TOO_LARGE.
+ */
+#define W8A8_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+w8a8_status_t w8a8_linear_noalloc(const void* x, int dtype, const float* inv_s, const int8_t* qw,
+                                  const float* sw, void* y, int64_t M, int64_t N, int64_t K,
+                                  hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -36,11 +36,11 @@ def declared_symbols():
 def test_library_loads_and_exports_header_symbols():
     lib = _lib.load()
     syms = declared_symbols()
-    assert len(syms) == 17
+    assert len(syms) == 18
     for s in syms:
         assert hasattr(lib, s), s
         assert s in _lib.PROTOTYPES, s
-    assert lib.w8a8_abi_version() == 4
+    assert lib.w8a8_abi_version() == 5
 
 
 def declared_prototypes():
@@ -84,7 +84,7 @@ def test_binding_prototypes_match_the_header():
 
 def test_status_strings():
     lib = _lib.load()
-    for code in range(0, 7):
+    for code in range(0, 8):
         s = lib.w8a8_status_str(code)
         assert s and s.decode()
     assert lib.w8a8_status_str(99).decode() == "unknown status"
@@ -210,6 +210,18 @@ def test_linear_rejects():
     assert lin(P, 0, P, P, P, P, 4, 8, 16, P + 16, need, 0) == EALIGN  # workspace 256 B
     assert lin(P, 0, P, P, P, P, 4, 8, 24, P, 1 << 20, 0) == ESHAPE
     assert lin(P, 0, P, P, P, P, 4, 12, 16, P, need, 0) == ESHAPE
+
+
+@cpu_only
+def test_linear_noalloc_rejects():
+    f = _lib.load().w8a8_linear_noalloc
+    assert f(P, 0, P, P, P, P, 4096, 16, 16384, 0) == 7  # more than the static scratch
+    assert f(P, 0, P, P, P, P, -1, 8, 16, 0) == ESHAPE
+    assert f(P, 5, P, P, P, P, 4, 8, 16, 0) == EDTYPE
+    assert f(P, 0, P, P, 0, P, 4, 8, 16, 0) == ENULL
+    assert f(P, 0, P, P, P, P, 4, 8, 24, 0) == ESHAPE
+    assert f(PODD, 0, P, P, P, P, 4, 8, 16, 0) == EALIGN
+    assert f(P, 0, P, P, PODD, P, 4, 8, 16, 0) == EALIGN
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -332,6 +332,23 @@ def linear(x: torch.Tensor, inv_s: torch.Tensor, qw: torch.Tensor, sw: torch.Ten
     return y
 
 
+def linear_noalloc(x: torch.Tensor, inv_s: torch.Tensor, qw: torch.Tensor, sw: torch.Tensor,
+                   y: torch.Tensor) -> torch.Tensor:
+    """``linear`` with the library's static scratch instead of a workspace
+    (w8a8_linear_noalloc): ``y`` is required, so nothing is allocated."""
+    _dev(x, inv_s, qw, sw, y)
+    M, K = x.shape
+    N = qw.shape[0]
+    _need(inv_s, torch.float32, (K,))
+    _need(qw, torch.int8, (N, K))
+    _need(sw, torch.float32, (N,))
+    _need(y, x.dtype, (M, N))
+    lib = _lib.load()
+    _lib.check("w8a8_linear_noalloc", lib.w8a8_linear_noalloc(
+        _ptr(x), _dtype_code(x), _ptr(inv_s), _ptr(qw), _ptr(sw), _ptr(y), M, N, K, _stream()))
+    return y
+
+
 def prepare_weight(w: torch.Tensor, amax_x: torch.Tensor, alpha: float) -> dict:
     """Offline weight path of one layer: max|W_j|, (s, inv_s), folded INT8 weight.
 

@@ -7,7 +7,16 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "common.h"
+
+// The scratch of w8a8_linear_noalloc: one file-scope device array, which
+// every GPU the library runs on holds (at its own address) until the process
+// ends.  Host code never uses the name itself, which is only a host-side
+// stand-in: it takes the array's device address per device from
+// hipGetSymbolAddress and passes that to the kernels.
+static __device__ __align__(256) char scratch[W8A8_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -22,6 +31,25 @@ constexpr int64_t kMaxQuantCols = 65536;         // 1024 threads x 8 chunks x 8 
 constexpr size_t kWsAlign = 256;
 
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Device address of `scratch` on the current device, resolved once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+w8a8_status_t scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return W8A8_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return W8A8_ERR_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return W8A8_OK;
+}
 
 w8a8_status_t check_gemm(const void* qa, const void* qb, const void* out, int64_t M, int64_t N,
                          int64_t K) {
@@ -48,6 +76,16 @@ w8a8_status_t check_quant(const void* x, int dtype, int64_t rows, int64_t cols,
   return W8A8_OK;
 }
 
+// Argument checks of the runtime forward (workspace as w8a8_linear takes it).
+w8a8_status_t check_linear(const void* x, int dtype, const float* inv_s, const int8_t* qw,
+                           const float* sw, const void* y, int64_t M, int64_t N, int64_t K,
+                           const void* workspace, size_t ws_bytes);
+
+// Enqueue the runtime forward on checked arguments.
+w8a8_status_t launch_linear(const void* x, int dtype, const float* inv_s, const int8_t* qw,
+                            const float* sw, void* y, int64_t M, int64_t N, int64_t K,
+                            void* workspace, hipStream_t stream);
+
 }  // namespace
 
 extern "C" {
@@ -63,6 +101,9 @@ const char* w8a8_status_str(int status) {
     case W8A8_ERR_DTYPE: return "unknown dtype code";
     case W8A8_ERR_ARG: return "argument out of range";
     case W8A8_ERR_HIP: return "HIP launch failed";
+    case W8A8_ERR_TOO_LARGE:
+      return "the call needs more scratch than the library's static array holds "
+             "(W8A8_NOALLOC_SCRATCH_BYTES); use w8a8_linear with a workspace";
     default: return "unknown status";
   }
 }
@@ -224,28 +265,74 @@ size_t w8a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 w8a8_status_t w8a8_linear(const void* x, int dtype, const float* inv_s, const int8_t* qw,
                           const float* sw, void* y, int64_t M, int64_t N, int64_t K,
                           void* workspace, size_t ws_bytes, hipStream_t stream) {
+  const w8a8_status_t st = check_linear(x, dtype, inv_s, qw, sw, y, M, N, K, workspace, ws_bytes);
+  if (st != W8A8_OK) return st;
+  return launch_linear(x, dtype, inv_s, qw, sw, y, M, N, K, workspace, stream);
+}
+
+w8a8_status_t w8a8_linear_noalloc(const void* x, int dtype, const float* inv_s, const int8_t* qw,
+                                  const float* sw, void* y, int64_t M, int64_t N, int64_t K,
+                                  hipStream_t stream) {
+  if (M < 0 || N < 0 || K < 0) return W8A8_ERR_SHAPE;
+  if (w8a8_linear_workspace_bytes(M, N, K) > (size_t)W8A8_NOALLOC_SCRATCH_BYTES)
+    return W8A8_ERR_TOO_LARGE;
+  // every argument check first, with a stand-in for the scratch's address
+  // (any 256-byte aligned value), so a rejected call makes no HIP call at all
+  w8a8_status_t st = check_linear(x, dtype, inv_s, qw, sw, y, M, N, K, (void*)kWsAlign,
+                                  W8A8_NOALLOC_SCRATCH_BYTES);
+  if (st != W8A8_OK) return st;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != W8A8_OK) return st;
+  return launch_linear(x, dtype, inv_s, qw, sw, y, M, N, K, ws, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+struct LinearWs {
+  int8_t* qx;
+  float* sx;
+  int32_t* part;
+};
+
+LinearWs linear_ws(const void* workspace, int64_t M, int64_t K) {
+  char* base = (char*)workspace;
+  const size_t off_sx = round_up((size_t)M * (size_t)K, kWsAlign);
+  return LinearWs{(int8_t*)base, (float*)(base + off_sx),
+                  (int32_t*)(base + off_sx + round_up((size_t)M * 4, kWsAlign))};
+}
+
+w8a8_status_t check_linear(const void* x, int dtype, const float* inv_s, const int8_t* qw,
+                           const float* sw, const void* y, int64_t M, int64_t N, int64_t K,
+                           const void* workspace, size_t ws_bytes) {
   if (!valid_dtype(dtype)) return W8A8_ERR_DTYPE;
   if (M < 0 || N < 0 || K < 0) return W8A8_ERR_SHAPE;
   if (!workspace || (!sw && N)) return W8A8_ERR_NULL;
   if (!aligned(workspace, kWsAlign)) return W8A8_ERR_ALIGN;
   if (ws_bytes < w8a8_linear_workspace_bytes(M, N, K)) return W8A8_ERR_ARG;
-  int8_t* qx = (int8_t*)workspace;
-  const size_t off_sx = round_up((size_t)M * (size_t)K, kWsAlign);
-  float* sx = (float*)((char*)workspace + off_sx);
-  int32_t* part = (int32_t*)((char*)workspace + off_sx + round_up((size_t)M * 4, kWsAlign));
-  w8a8_status_t st = check_quant(x, dtype, M, K, inv_s, qx, sx);
+  const LinearWs ws = linear_ws(workspace, M, K);
+  w8a8_status_t st = check_quant(x, dtype, M, K, inv_s, ws.qx, ws.sx);
   if (st != W8A8_OK) return st;
-  st = check_gemm(qx, qw, y, M, N, K);
+  st = check_gemm(ws.qx, qw, y, M, N, K);
   if (st != W8A8_OK) return st;
   if (!aligned(sw, 16)) return W8A8_ERR_ALIGN;
-  hipError_t e = w8a8::launch_scale_quant_rows(x, dtype == W8A8_BF16, M, K, inv_s, false, 0.0f, qx,
-                                               sx, 0, stream);
-  if (e != hipSuccess) return W8A8_ERR_HIP;
-  if (linear_splitk(M, N, K))
-    return hip_status(w8a8::launch_gemm_splitk(qx, qw, M, N, K, sx, sw, y, dtype == W8A8_BF16, part,
-                                               stream));
-  return hip_status(w8a8::launch_gemm(qx, qw, M, N, K, sx, sw, y, dtype == W8A8_BF16 ? 2 : 1,
-                                      stream));
+  return W8A8_OK;
 }
 
-}  // extern "C"
+w8a8_status_t launch_linear(const void* x, int dtype, const float* inv_s, const int8_t* qw,
+                            const float* sw, void* y, int64_t M, int64_t N, int64_t K,
+                            void* workspace, hipStream_t stream) {
+  const LinearWs ws = linear_ws(workspace, M, K);
+  const bool bf16 = dtype == W8A8_BF16;
+  hipError_t e = w8a8::launch_scale_quant_rows(x, bf16, M, K, inv_s, false, 0.0f, ws.qx, ws.sx, 0,
+                                               stream);
+  if (e != hipSuccess) return W8A8_ERR_HIP;
+  if (linear_splitk(M, N, K))
+    return hip_status(w8a8::launch_gemm_splitk(ws.qx, qw, M, N, K, ws.sx, sw, y, bf16, ws.part,
+                                               stream));
+  return hip_status(w8a8::launch_gemm(ws.qx, qw, M, N, K, ws.sx, sw, y, bf16 ? 2 : 1, stream));
+}
+
+}  // namespace
