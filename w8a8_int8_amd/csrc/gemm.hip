@@ -9,17 +9,18 @@
 //   Y[t, k] = out(fp32(fp32(C[t, k]) * sa[t]) * sb[k])    (IEEE fp32, RNE)
 //
 // Operands: qa = activation codes, M x K; qb = weight codes, N x K; both K
-// contiguous.  Every MFMA is v_mfma_i32_32x32x32_i8 with the weight fragment
-// as its first operand (32 output channels x 32 k) and the activation
-// fragment as its second (32 k x 32 tokens), so that each lane's four
-// consecutive accumulator registers hold four consecutive output channels of
-// one token.  Integer accumulation is exact and order free.  The epilogue
+// contiguous.  Every INT8 MFMA is v_mfma_i32_16x16x64_i8 with the weight
+// fragment as its first operand (16 output channels x 64 k) and the
+// activation fragment as its second (64 k x 16 tokens), so that each lane's
+// four accumulator registers hold four consecutive output channels of one
+// token.  Integer accumulation is exact and order free.  The epilogue
 // dequantizes in registers and restages each wave's results through LDS so
 // that every global store writes whole rows of 16 bytes per lane.
 //
 // Block: WGM x WGN waves (8 for the 256-row tiles, 4 for 128 x 128) own a
 // BM x BN output tile (tokens x channels); wave (wm, wn) holds a
-// (BM / WGM) x (BN / WGN) register tile of 32 x 32 MFMA blocks.  Tiles:
+// (BM / WGM) x (BN / WGN) register tile of MFMA blocks (16 x 16 for INT8,
+// 32 x 32 for the 16-bit and FP8 forms, see MmaKind).  Tiles:
 // 256 x 256, 256 x 192, 256 x 128 and 128 x 128; launch_gemm picks the one
 // whose last wave of blocks over the 256 CUs is fullest, preferring fewer
 // operand bytes per MFMA (the return path of the operand loads is the
@@ -37,11 +38,12 @@
 // end are issued with out-of-range offsets (no memory traffic) so the
 // per-stage load count, and with it every vmcnt wait, is constant.
 //
-// Per stage a wave runs BK / 32 k steps (BK / 64 for FP8, whose
-// MFMA takes 64 bytes of K) of (BM / WGM / 32) x (BN / WGN / 32) MFMAs.  The
+// Per stage a wave runs BK / KSTEP k steps (KSTEP = 64 bytes for INT8 and
+// FP8, 32 for fp16 / bf16) of (BM / WGM / MB) x (BN / WGN / MB) MFMAs.  The
 // fragment reads are software pipelined: the next k step's fragments are read
-// while the current step's MFMAs run, and the next stage's first fragments
-// are read (after the stage barrier) while the last step's MFMAs run.  One
+// while the current step's MFMAs run (the larger operand in place, column by
+// column), and the next stage's first fragments are read (after the stage
+// barrier) while the last step's MFMAs run.  One
 // barrier per stage; it is a plain s_barrier (no memory fence), with the
 // needed waits explicit: each wave waits for its own LDS-mode loads of the
 // next stage (vmcnt) and for its own LDS reads of the slot that is about to
@@ -65,6 +67,7 @@
 // baseline) and the FP8 E4M3 variant; few-token shapes go to k_gemm_skinny
 // and, in the runtime forward, to the split-K k_gemm_splitk (below).
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -89,21 +92,35 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 //   4: bf16 operands, fp32 accumulators rounded to bf16 (the dense baseline)
 //   5: FP8 E4M3 operands, fp32 accumulators dequantized to fp16
 //   6: FP8 E4M3 operands, fp32 accumulators dequantized to bf16
-// A fragment is FR 16-byte chunks per lane: the 32 x 32 MFMAs for int8, fp16
-// and bf16 take 32 bytes of K per row (FR = 1), the FP8 one 64 bytes (FR = 2);
-// the byte-addressed LDS pipeline is the same for all of them.
+// Geometry of an MFMA: it multiplies an MB x KSTEP block of the weight by a
+// KSTEP x MB block of the activations (MB = 32 or 16 rows each).  A lane's
+// fragment of a block is FR 16-byte chunks of row lane % MB, k chunks
+// FR * (lane / MB) .. + FR - 1 of the k step, so KSTEP = 16 * FR * 64 / MB
+// bytes.  A lane's accumulators hold, for group g < NACC / 4, the four
+// consecutive output channels g * (256 / MB) + (lane / MB) * 4 .. + 3 of
+// token lane % MB.  The byte-addressed LDS pipeline is the same for all.
+//   int8:       16 x 16 x 64 (MB 16, FR 1).  Back-to-back INT8 MFMAs from
+//               registers run at 3.8-3.9 POPS with random operands in this
+//               shape (the shader clock holds about 1.95 GHz) against 3.3-3.4
+//               POPS in the 32 x 32 x 32 shape (about 1.65 GHz); a 16 x 16
+//               block also gives a wave four times the independent
+//               accumulators, which the matrix pipe needs to issue back to
+//               back.  In this kernel it is 2-7% faster on the 256 x 256 and
+//               256 x 192 tiles and equal on 256 x 128.
+//   fp16, bf16: 32 x 32 x 16 (MB 32, FR 1)
+//   FP8 E4M3:   32 x 32 x 64 (MB 32, FR 2)
 typedef int v8i __attribute__((ext_vector_type(8)));
 template <int OUT>
 struct MmaKind {
-  static constexpr int FR = 1;
-  typedef v16i acc_t;
+  static constexpr int MB = 16, FR = 1;
+  typedef v4i acc_t;
   __device__ static __forceinline__ acc_t mma(const v4i* a, const v4i* b, acc_t c) {
-    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a[0], b[0], c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a[0], b[0], c, 0, 0, 0);
   }
 };
 template <>
 struct MmaKind<3> {
-  static constexpr int FR = 1;
+  static constexpr int MB = 32, FR = 1;
   typedef v16f acc_t;
   __device__ static __forceinline__ acc_t mma(const v4i* a, const v4i* b, acc_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a[0]),
@@ -112,7 +129,7 @@ struct MmaKind<3> {
 };
 template <>
 struct MmaKind<4> {
-  static constexpr int FR = 1;
+  static constexpr int MB = 32, FR = 1;
   typedef v16f acc_t;
   __device__ static __forceinline__ acc_t mma(const v4i* a, const v4i* b, acc_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a[0]),
@@ -120,7 +137,7 @@ struct MmaKind<4> {
   }
 };
 struct MmaE4m3 {
-  static constexpr int FR = 2;
+  static constexpr int MB = 32, FR = 2;
   typedef v16f acc_t;
   // format selectors 0 / 0: both operands FP8 E4M3, no block scales
   __device__ static __forceinline__ acc_t mma(const v4i* a, const v4i* b, acc_t c) {
@@ -186,24 +203,21 @@ __device__ __forceinline__ void tile_of(int bid, int m_tiles, int n_tiles, int& 
   tn = in_g / gsize;
 }
 
-// Scheduling hint for the compiler: interleave each MFMA with up to DPM LDS
-// reads and a share of the global (LDS-mode) loads, so that no wave stalls on
-// a memory queue while its matrix pipe idles.  I counts MFMAs; memory
-// instructions are front-loaded so their latency overlaps the remaining
-// MFMAs.  The three- and four-slot tiles issue all of a k step's fragment
-// reads with its first MFMA (measured 2% faster on the 256 x 128 tile; on
-// the two-slot tiles, where the loads come in a burst after the barrier, one
-// read per MFMA is as fast or faster).
-template <int I, int NMFMA, int NDS, int NVM, int DPM = 1>
-__device__ __forceinline__ void interleave() {
-  constexpr int VPM = (NVM + NMFMA - 1) / NMFMA;  // VMEMs per MFMA
-  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-  if constexpr (I * DPM < NDS)
-    __builtin_amdgcn_sched_group_barrier(0x100, NDS - I * DPM < DPM ? NDS - I * DPM : DPM, 0);
-  if constexpr (I * VPM < NVM)
-    __builtin_amdgcn_sched_group_barrier(0x010, NVM - I * VPM < VPM ? NVM - I * VPM : VPM, 0);
-  if constexpr (I + 1 < NMFMA) interleave<I + 1, NMFMA, NDS, NVM, DPM>();
+// Scheduling hint for the compiler, for one k step of the tiled kernel (see
+// kstep there): column P of NP issues its NQ MFMAs, then its fragment read
+// for the next step (two while P < NQ, each FR chunks) and a share of the
+// NVM global (LDS-mode) loads, so that no wave stalls on a memory queue
+// while its matrix pipe idles.
+template <int P, int NP, int NQ, int FR, int NVM>
+__device__ __forceinline__ void interleave_cols() {
+  constexpr int VPC = (NVM + NP - 1) / NP;  // VMEMs per column
+  __builtin_amdgcn_sched_group_barrier(0x008, NQ, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, FR * (P < NQ ? 2 : 1), 0);
+  if constexpr (P * VPC < NVM)
+    __builtin_amdgcn_sched_group_barrier(0x010, NVM - P * VPC < VPC ? NVM - P * VPC : VPC, 0);
+  if constexpr (P + 1 < NP) interleave_cols<P + 1, NP, NQ, FR, NVM>();
 }
+
 
 // The tiled kernels' LDS, sized for the largest tile's stages (every tiled
 // kernel runs one block per CU).  It is one file-scope array rather than a
@@ -227,18 +241,21 @@ __device__ __forceinline__ void gemm_tile(const int8_t* __restrict__ qa,
                                           int ldc, int tm, int tn) {
   constexpr int NW = WGM * WGN;                 // waves per block
   constexpr int WM = BM / WGM, WN = BN / WGN;   // wave tile (tokens, channels)
-  constexpr int FM = WM / 32, FN = WN / 32;
+  constexpr int MB = MmaKind<OUT>::MB;          // rows of an MFMA block
+  constexpr int LPR = 64 / MB;                  // lane groups (k chunks) per fragment row
+  constexpr int FM = WM / MB, FN = WN / MB;
   constexpr int CPR = BK / 16;                  // 16-byte chunks per LDS row
   constexpr int RPW = 16 / CPR;                 // rows per 256-byte bank window
   constexpr int RPI = 1024 / BK;                // rows filled by one LDS-mode wave load
   constexpr int FR = MmaKind<OUT>::FR;          // 16-byte chunks per fragment
-  constexpr int KK = BK / (32 * FR);            // MFMA k steps per stage
+  constexpr int KK = BK / (16 * FR * LPR);      // MFMA k steps per stage
   constexpr int LA = BM / RPI / NW;             // LDS-mode loads per wave per stage, activations
   constexpr int LB = BN / RPI / NW;             // ... weights
   constexpr int L = LA + LB;
   constexpr int SLOT = (BM + BN) * BK;          // bytes per LDS stage
   static_assert(LA >= 1 && LB >= 1 && LA * RPI * NW == BM && LB * RPI * NW == BN &&
-                FM >= 1 && FN >= 1 && KK % 2 == 0, "unsupported tile");
+                FM >= 1 && FN >= 1 && FM * MB == WM && FN * MB == WN && KK % 2 == 0 &&
+                (MB / RPW) % CPR == 0, "unsupported tile");
   static_assert(NST >= 2 && (NST - 1) * 2 * L < 64, "unsupported pipeline depth");  // vmcnt range
   static_assert(NST * SLOT <= kTileLds, "LDS size");
 
@@ -305,9 +322,10 @@ __device__ __forceinline__ void gemm_tile(const int8_t* __restrict__ qa,
     }
   };
 
-  // fragment reads: lane reads row (base + (lane & 31)), k chunk 2 * kk + (lane >> 5);
-  // bases are multiples of 32 rows, so the swizzle depends on lane & 31 only
-  const int fr = lane & 31, fk = lane >> 5;
+  // fragment reads: lane reads row (base + lane % MB), k chunks
+  // FR * (LPR * kk + lane / MB) + f; bases are multiples of MB rows, a whole
+  // number of swizzle periods, so the swizzle depends on lane % MB only
+  const int fr = lane % MB, fk = lane / MB;
   const int fsw = (fr / RPW) % CPR;
   const int off_a = (wm * WM + fr) * BK;
   const int off_b = BM * BK + (wn * WN + fr) * BK;
@@ -319,30 +337,53 @@ __device__ __forceinline__ void gemm_tile(const int8_t* __restrict__ qa,
 #pragma unroll
     for (int b = 0; b < FM; ++b) acc[a][b] = acc_t{};
 
-  // fragment f of a lane is chunks FR * (2 * kk + fk) + f of its row (f < FR)
-  v4i fb0[FN * FR], fa0[FM * FR], fb1[FN * FR], fa1[FM * FR];
-  auto read_frags = [&](int st, int kk, v4i* fb, v4i* fa) {
+  // Fragments.  Fragment f of a lane is chunk FR * (LPR * kk + fk) + f of its
+  // row (f < FR).  Of the two operands, the one with more fragments per wave
+  // (P, NP of them) is read in place: fragment p of the next k step goes into
+  // the registers of fragment p as soon as the MFMAs of column p have been
+  // issued.  The other (Q, NQ <= NP) is double-buffered; its fragment q of
+  // the next step is read after column q.  So a wave holds NP + 2 NQ
+  // fragments instead of 2 (NP + NQ).
+  constexpr bool kAin = FM >= FN;  // the activation fragments are read in place
+  constexpr int NP = kAin ? FM : FN, NQ = kAin ? FN : FM;
+  v4i fp[NP * FR], fq0[NQ * FR], fq1[NQ * FR];
+  auto read_frag = [&](const int8_t* slot, int kk, bool act, int i, v4i* dst) {
+    const int base = act ? off_a + i * MB * BK : off_b + i * MB * BK;
+#pragma unroll
+    for (int f = 0; f < FR; ++f)
+      dst[f] = *(const v4i*)(slot + base + (((FR * (LPR * kk + fk) + f) ^ fsw) << 4));
+  };
+  auto read_all = [&](int st, int kk, v4i* fq) {
     const int8_t* slot = lds + (st % NST) * SLOT;
 #pragma unroll
-    for (int f = 0; f < FR; ++f) {
-      const int ch = ((FR * (2 * kk + fk) + f) ^ fsw) << 4;
+    for (int p = 0; p < NP; ++p) read_frag(slot, kk, kAin, p, fp + p * FR);
 #pragma unroll
-      for (int a = 0; a < FN; ++a) fb[a * FR + f] = *(const v4i*)(slot + off_b + a * 32 * BK + ch);
-#pragma unroll
-      for (int b = 0; b < FM; ++b) fa[b * FR + f] = *(const v4i*)(slot + off_a + b * 32 * BK + ch);
-    }
+    for (int q = 0; q < NQ; ++q) read_frag(slot, kk, !kAin, q, fq + q * FR);
   };
-  auto mfmas = [&](const v4i* fb, const v4i* fa) {
+
+  // One k step: column p issues its NQ MFMAs, then (when `rd`) the reads of
+  // fragment p (and fragment p of Q) of step rkk of stage rst.
+  auto kstep = [&](const v4i* cq, v4i* nq, bool rd, int rst, int rkk) {
+    const int8_t* slot = lds + (rst % NST) * SLOT;
 #pragma unroll
-    for (int a = 0; a < FN; ++a)
+    for (int p = 0; p < NP; ++p) {
 #pragma unroll
-      for (int b = 0; b < FM; ++b)
-        acc[a][b] = MmaKind<OUT>::mma(fb + a * FR, fa + b * FR, acc[a][b]);
+      for (int q = 0; q < NQ; ++q) {
+        if constexpr (kAin)
+          acc[q][p] = MmaKind<OUT>::mma(cq + q * FR, fp + p * FR, acc[q][p]);
+        else
+          acc[p][q] = MmaKind<OUT>::mma(fp + p * FR, cq + q * FR, acc[p][q]);
+      }
+      if (rd) {
+        read_frag(slot, rkk, kAin, p, fp + p * FR);
+        if (p < NQ) read_frag(slot, rkk, !kAin, p, nq + p * FR);
+      }
+    }
   };
 
   // Pipeline (stage s lives in slot s % NST).  Iteration kt computes stage kt
-  // as KK steps of 32-deep k (64-deep for FP8); the fragments of step kk+1 are
-  // read while the MFMAs of step kk run.  Before the last step the stage
+  // as KK k steps (64 bytes deep for INT8 and FP8, 32 for fp16 / bf16); the
+  // fragments of step kk+1 are read while the MFMAs of step kk run.  Before the last step the stage
   // barrier is taken: each wave first waits for its own loads of stage kt+1
   // and for its own reads of slot kt, so after the barrier stage kt+1 is
   // visible to every wave and slot kt is free.
@@ -364,111 +405,116 @@ __device__ __forceinline__ void gemm_tile(const int8_t* __restrict__ qa,
   constexpr int PER = (LW + KK - 2) / (KK - 1);      // loads per step when spread
   static_assert(KK >= 2, "unsupported stage depth");
   static_assert(!kHalf || ((NW / 2) * RPI / RPW) % CPR == 0, "half-wave load swizzle");
-  const bool loader = !kHalf || wave < NW / 2;
-  auto step_ptrs = [&](int kk, v4i*& cb, v4i*& ca, v4i*& nb, v4i*& na) {
-    cb = (kk & 1) ? fb1 : fb0;
-    ca = (kk & 1) ? fa1 : fa0;
-    nb = (kk & 1) ? fb0 : fb1;
-    na = (kk & 1) ? fa0 : fa1;
-  };
-  if (nk > 0) {
+  // The K loop, in one copy for waves that issue loads and one for waves that
+  // only compute: with a run-time branch on the role inside the loop, the
+  // accumulators would meet at every join, where the register allocator
+  // copies them.
+  auto kloop = [&](auto loads_tag) {
+    constexpr bool kLoads = decltype(loads_tag)::value;
     // prologue: the stages in flight before iteration 0
     constexpr int PRE = kSpread ? NST - 1 : NST;
-    if (loader) {
+    if constexpr (kLoads) {
 #pragma unroll
       for (int st = 0; st < PRE; ++st) dma(st, 0, LW);
     }
     wait_vmcnt<(PRE - 1) * LW>();  // stage 0 landed
     block_barrier();
-    read_frags(0, 0, fb0, fa0);
+    read_all(0, 0, fq0);
     for (int kt = 0; kt < nk - 1; ++kt) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        v4i *cb, *ca, *nb, *na;
-        step_ptrs(kk, cb, ca, nb, na);
+        v4i* cq = (kk & 1) ? fq1 : fq0;
+        v4i* nq = (kk & 1) ? fq0 : fq1;
         if (kk + 1 < KK) {
-          read_frags(kt, kk + 1, nb, na);
           if constexpr (kSpread) {
             dma(kt + NST - 1, kk * PER, min((kk + 1) * PER, LW));
-            mfmas(cb, ca);
-            interleave<0, FN * FM, FR * (FN + FM), PER, FR * (FN + FM)>();
+            kstep(cq, nq, true, kt, kk + 1);
+            interleave_cols<0, NP, NQ, FR, PER>();
           } else {
-            mfmas(cb, ca);
-            interleave<0, FN * FM, FR * (FN + FM), 0>();
+            kstep(cq, nq, true, kt, kk + 1);
+            interleave_cols<0, NP, NQ, FR, 0>();
           }
         } else {
           wait_vmcnt<(NST - 2) * LW>();  // this wave's loads of stage kt+1 landed
           wait_lgkmcnt0();               // this wave's reads of slot kt are done
           block_barrier();               // every wave: stage kt+1 landed, slot kt free
-          if (!kSpread && loader) {
+          if constexpr (!kSpread && kLoads) {
             dma(kt + NST, 0, LW);
-            read_frags(kt + 1, 0, nb, na);
-            mfmas(cb, ca);
-            interleave<0, FN * FM, FR * (FN + FM), LW>();
+            kstep(cq, nq, true, kt + 1, 0);
+            interleave_cols<0, NP, NQ, FR, LW>();
           } else {
-            read_frags(kt + 1, 0, nb, na);
-            mfmas(cb, ca);
-            interleave<0, FN * FM, FR * (FN + FM), 0>();
+            kstep(cq, nq, true, kt + 1, 0);
+            interleave_cols<0, NP, NQ, FR, 0>();
           }
         }
       }
     }
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      v4i *cb, *ca, *nb, *na;
-      step_ptrs(kk, cb, ca, nb, na);
-      if (kk + 1 < KK) read_frags(nk - 1, kk + 1, nb, na);
-      mfmas(cb, ca);
+      v4i* cq = (kk & 1) ? fq1 : fq0;
+      v4i* nq = (kk & 1) ? fq0 : fq1;
+      kstep(cq, nq, kk + 1 < KK, nk - 1, kk + 1);
     }
     wait_vmcnt<0>();  // no LDS-mode load may outlive the block's LDS
+  };
+  if (nk > 0) {
+    if constexpr (kHalf) {
+      if (wave < NW / 2)
+        kloop(std::true_type{});
+      else
+        kloop(std::false_type{});
+    } else {
+      kloop(std::true_type{});
+    }
   }
 
   // Epilogue.  A lane holds, for register group g of fragment (a, b), output
-  // channels n .. n+3 of token m, with m = b * 32 + (lane & 31) and
-  // n = a * 32 + g * 8 + (lane >> 5) * 4 inside the wave tile.  Stored like
-  // that, a wave store would cover 32 rows with 16 bytes each, and the store
-  // path, which pays per request, would run at a quarter of its byte rate.
-  // So the results go through LDS, one 32-token slab of the wave tile at a
-  // time: each wave writes its slab into a private staging area and reads it
-  // back row-major, 16 contiguous bytes per lane, for full-line global stores.
-  // The staging row pitch is an odd number of 16-byte chunks, so the 32 rows
-  // of a slab write fall on distinct bank groups.
+  // channels n .. n+3 of token m, with m = b * MB + lane % MB and
+  // n = a * MB + g * 4 * LPR + (lane / MB) * 4 inside the wave tile.  Stored
+  // like that, a wave store would cover MB rows with 64 / MB * 16 bytes each,
+  // and the store path, which pays per request, would run below its byte
+  // rate.  So the results go through LDS, one MB-token slab of the wave tile
+  // at a time: each wave writes its slab into a private staging area and
+  // reads it back row-major, 16 contiguous bytes per lane, for full-line
+  // global stores.  The staging row pitch is an odd number of 16-byte chunks,
+  // so the rows of a slab write fall on distinct bank groups.
   //
   // The dequant scales are loaded before any store: the memory counter that
   // their loads are waited on also counts stores, so a scale load issued after
   // a store would make its use wait for that store to complete.  Indices are
   // clamped so the loads stay in bounds; stores are guarded (N % 8 == 0, so a
   // 16-byte chunk of a row is either inside N or wholly outside).
-  constexpr int ES = OUT == 0 ? 4 : 2;  // output element bytes
-  constexpr int CPO = WN * ES / 16;     // 16-byte output chunks per wave-tile row
-  constexpr int PITCH = WN * ES + 16;   // staging row pitch in bytes
-  static_assert((PITCH / 16) % 2 == 1 && NW * 32 * PITCH <= NST * SLOT && (32 * CPO) % 64 == 0,
-                "epilogue staging");
-  const int hi = lane >> 5;
+  constexpr int NG = sizeof(acc_t) / 16;  // groups of 4 accumulators per lane
+  constexpr int ES = OUT == 0 ? 4 : 2;    // output element bytes
+  constexpr int CPO = WN * ES / 16;       // 16-byte output chunks per wave-tile row
+  constexpr int PITCH = WN * ES + 16;     // staging row pitch in bytes
+  static_assert((PITCH / 16) % 2 == 1 && NW * MB * PITCH <= NST * SLOT && (MB * CPO) % 64 == 0 &&
+                NG * 4 * LPR == MB, "epilogue staging");
+  const int hi = lane / MB;
   constexpr bool kDequant = OUT == 1 || OUT == 2 || OUT == 5 || OUT == 6;
   float am[FM];
-  float4 bn[FN][4];
+  float4 bn[FN][NG];
   if constexpr (kDequant) {
 #pragma unroll
-    for (int b = 0; b < FM; ++b) am[b] = sa[min(m0 + wm * WM + b * 32 + (lane & 31), M - 1)];
+    for (int b = 0; b < FM; ++b) am[b] = sa[min(m0 + wm * WM + b * MB + fr, M - 1)];
 #pragma unroll
     for (int a = 0; a < FN; ++a)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        bn[a][g] = *(const float4*)(sb + min(n0 + wn * WN + a * 32 + g * 8 + hi * 4, N - 4));
+      for (int g = 0; g < NG; ++g)
+        bn[a][g] = *(const float4*)(sb + min(n0 + wn * WN + a * MB + g * 4 * LPR + hi * 4, N - 4));
   }
   // every wave is past its last fragment read and its last LDS-mode load
   wait_lgkmcnt0();
   block_barrier();
-  int8_t* stage = lds + wave * 32 * PITCH;
+  int8_t* stage = lds + wave * MB * PITCH;
 #pragma unroll
   for (int b = 0; b < FM; ++b) {
 #pragma unroll
     for (int a = 0; a < FN; ++a) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < NG; ++g) {
         const acc_t& C = acc[a][b];
-        int8_t* dst = stage + (lane & 31) * PITCH + (a * 32 + g * 8 + hi * 4) * ES;
+        int8_t* dst = stage + fr * PITCH + (a * MB + g * 4 * LPR + hi * 4) * ES;
         if constexpr (OUT == 0) {
           *(v4i*)dst = v4i{(int)C[4 * g + 0], (int)C[4 * g + 1], (int)C[4 * g + 2], (int)C[4 * g + 3]};
         } else {
@@ -494,7 +540,7 @@ __device__ __forceinline__ void gemm_tile(const int8_t* __restrict__ qa,
     }
     // read the slab back row-major (LDS operations of one wave complete in
     // order, so the reads see the writes above and precede the next slab's)
-    constexpr int NR = 32 * CPO / 64;
+    constexpr int NR = MB * CPO / 64;
     v4i v[NR];
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
@@ -504,7 +550,7 @@ __device__ __forceinline__ void gemm_tile(const int8_t* __restrict__ qa,
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       const int f = i * 64 + lane;
-      const int m = m0 + wm * WM + b * 32 + f / CPO;
+      const int m = m0 + wm * WM + b * MB + f / CPO;
       const int n = n0 + wn * WN + (f % CPO) * (16 / ES);
       if (m < M && n < N) *(v4i*)((int8_t*)out + ((int64_t)m * ldc + n) * ES) = v[i];
     }
