@@ -23,6 +23,7 @@ microseconds, so the other timed steps carry none.  cpu_baseline times the CPU o
 host cores over one step of the same workload.
 
 python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                [--other-workloads A,B] [--ceilings]
 """
 from __future__ import annotations
 
@@ -58,6 +59,12 @@ def parse():
                          "costs the step a few microseconds of idle GPU)")
     ap.add_argument("--kernel-reps", type=int, default=20,
                     help="repetitions per kernel in the per-kernel breakdown pass")
+    ap.add_argument("--other-workloads", default="opt30b_prefill,llama2_70b_prefill,opt6.7b_decode",
+                    help="comma-separated workloads whose kernels are also timed (per-kernel pass "
+                         "only, into the `other_workloads` key); empty for none")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only run the hardware probes (read-only streaming, copy, INT8 MFMA from "
+                         "registers with the shader clock) and print their figures")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this size first (outside the timed "
                          "region): the reference for scaling hardware byte counters")
@@ -242,9 +249,11 @@ def rotation(t, min_total=512 << 20, cap=32):
     return [t] + [t.clone() for _ in range(n - 1)]
 
 
-def kernel_breakdown(layers, reps):
+def kernel_breakdown(layers, reps, lean=False):
     """Per-kernel mean durations, each kernel type timed alone (graph_time).
-    The bandwidth-bound kernels rotate over copies of their input (rotation)."""
+    The bandwidth-bound kernels rotate over copies of their input (rotation).
+    lean: only the path's own kernels and the dense 16-bit product (no norm
+    folds, no FP8 variant)."""
     import torch
 
     timed = graph_time
@@ -279,6 +288,11 @@ def kernel_breakdown(layers, reps):
         t16 = timed(lambda i: w8.gemm_float(L.x, L.w, L.y), reps)
         d["dense16_gemm"] = dict(us=t16 * 1e6, TFLOPS=ops / t16 / 1e12,
                                  frac_mfma=ops / t16 / 1e12 / PEAK_DENSE16_TFLOPS)
+        if lean:
+            del ws, xs
+            out[f"{L.name}_{L.K}x{L.N}"] = {k: {kk: round(vv, 4) for kk, vv in v.items()}
+                                            for k, v in d.items()}
+            continue
         # the smoothing folded into the RMS norm in front of the layer (x taken as the norm's input)
         g = w8.fold_norm_weight(torch.ones(L.K, dtype=torch.float32, device=L.x.device), L.inv_s)
         t = timed(lambda i: w8.rmsnorm_quant_rows(xs[i % nx], g, 1e-5, L.qx, L.sx), reps)
@@ -304,9 +318,68 @@ def kernel_breakdown(layers, reps):
     t_16 = sum(v["dense16_gemm"]["us"] for v in out.values())
     out["w8a8_vs_dense16"] = {"gemm_speedup": round(t_16 / t_w8, 3),
                               "gemm_plus_act_quant_speedup": round(t_16 / (t_w8 + t_q), 3)}
-    t_8 = sum(v["gemm_dequant_e4m3"]["us"] for v in out.values() if "gemm_dequant_e4m3" in v)
-    out["e4m3_vs_int8"] = {"gemm_time_ratio": round(t_8 / t_w8, 3)}
+    if not lean:
+        t_8 = sum(v["gemm_dequant_e4m3"]["us"] for v in out.values() if "gemm_dequant_e4m3" in v)
+        out["e4m3_vs_int8"] = {"gemm_time_ratio": round(t_8 / t_w8, 3)}
     return out
+
+
+def calibration_volume(wl, layers, reps):
+    """Step 1 at the calibration volume the page recommends (512 samples of
+    2048 tokens, 1,048,576 tokens per layer): (a) the streaming form, one call
+    per 2048-token batch as the batches arrive, 512 calls cycling over the
+    layer's distinct batches (at least 420 MB, past the 256 MB last-level
+    cache), timed from a captured graph; (b) one call per slice of at least
+    1 GiB of tokens, two distinct slices in turn."""
+    import torch
+
+    from w8a8_int8_amd import synth
+
+    w8 = layers[0].w8
+    out = {}
+    for li, L in enumerate(layers):
+        if L.name not in ("qkv", "down"):
+            continue
+        nb = len(L.cal)
+        t = graph_time(lambda i: w8.channel_amax(L.cal[i % nb], L.amax_x), 512)
+        by = L.cal[0].numel() * 2
+        d = {"per_batch_stream": dict(batches=512, distinct_batches=nb, us_per_batch=round(t * 1e6, 3),
+                                      total_ms=round(t * 512e3, 3), GBs=round(by / t / 1e9, 1),
+                                      frac_hbm=round(by / t / 1e9 / PEAK_HBM_GBS, 4))}
+        rows = max(wl.cal_batch, -(-(1 << 30) // (2 * L.K)))
+        rows = -(-rows // wl.cal_batch) * wl.cal_batch
+        slices = [synth.calibration(wl, li, rows, chunk=10_000 + j, device=L.x.device)
+                  for j in range(2)]
+        t = graph_time(lambda i: w8.channel_amax(slices[i % 2], L.amax_x), max(4, reps // 4))
+        by = slices[0].numel() * 2
+        d["one_call_per_slice"] = dict(tokens=rows, GB=round(by / 1e9, 3), us=round(t * 1e6, 2),
+                                       GBs=round(by / t / 1e9, 1),
+                                       frac_hbm=round(by / t / 1e9 / PEAK_HBM_GBS, 4),
+                                       full_set_ms=round(t * (wl.cal_tokens / rows) * 1e3, 3))
+        del slices
+        torch.cuda.empty_cache()
+        out[f"{L.name}_{L.K}"] = d
+    return out
+
+
+def other_workload(name, alpha, reps, dev):
+    """The per-kernel pass (lean) on another workload, or its few-token sweep."""
+    import torch
+
+    from w8a8_int8_amd import synth
+
+    wl = synth.WORKLOADS[name]
+    layers = [Layer(wl, li, 1, alpha, dev) for li in range(len(wl.layers))]
+    for L in layers:
+        L.step(0)
+    torch.cuda.synchronize()
+    if wl.M[0] <= 32:
+        res = {"decode_sweep": decode_sweep(wl, layers, max(reps, 20))}
+    else:
+        res = {"M": wl.M[0], "act_dtype": wl.dtype, **kernel_breakdown(layers, reps, lean=True)}
+    del layers
+    torch.cuda.empty_cache()
+    return res
 
 
 def decode_sweep(wl, layers, reps):
@@ -397,6 +470,73 @@ def cpu_baseline(wl, layers, alpha, min_seconds=10.0):
                        f"(smooth+quant, exact INT8 GEMM, dequant) at M={wl.M[0]}")}
 
 
+def ceilings(dev):
+    """The box's practical ceilings, from the probes in libw8a8_probe.so (not
+    part of the path): read-only streaming and a plain copy over buffers past
+    the 256 MB last-level cache, and back-to-back INT8 MFMAs from registers
+    with each block's shader clock, for three operand patterns."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "w8a8_int8_amd", "libw8a8_probe.so"))
+    vp, sz, ci = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.w8a8probe_read.argtypes = [vp, sz, vp, ci, ci, vp]
+    lib.w8a8probe_copy.argtypes = [vp, vp, sz, ci, vp]
+    lib.w8a8probe_mfma.argtypes = [ci, ci, ci, ci, ci, ci, vp, vp, vp]
+    st = lambda: torch.cuda.current_stream().cuda_stream  # noqa: E731
+    out = {}
+    n = 2 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    src.view(torch.int32).copy_(torch.arange(n // 4, dtype=torch.int32, device=dev))
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    reads = {}
+    for chunked in (0, 1):
+        for blocks in (1024, 2048, 4096, 8192, 16384):
+            t = graph_time(lambda i: lib.w8a8probe_read(src.data_ptr(), n, sink.data_ptr(), blocks,
+                                                        chunked, st()), 10)
+            reads[("chunked_" if chunked else "grid_stride_") + str(blocks)] = round(n / t / 1e9, 1)
+    out["read_only_stream_GBs"] = {"bytes": n, "by_layout_and_blocks": reads,
+                                   "best": max(reads.values())}
+    half = n // 2
+    dst = torch.empty(half, dtype=torch.uint8, device=dev)
+    copies = {}
+    for blocks in (2048, 4096, 8192, 16384):
+        t = graph_time(lambda i: lib.w8a8probe_copy(src.data_ptr(), dst.data_ptr(), half, blocks, st()), 10)
+        copies[str(blocks)] = round(2 * half / t / 1e9, 1)
+    t = graph_time(lambda i: dst.copy_(src[:half]), 10)
+    out["copy_GBs"] = {"bytes_each_way": half, "by_blocks": copies, "best": max(copies.values()),
+                       "torch_copy": round(2 * half / t / 1e9, 1)}
+    del src, dst
+    blocks = 256
+    clocks = torch.zeros(2 * blocks, dtype=torch.int64, device=dev)
+    mf = {}
+    for shape, waves, chains in ((0, 8, 4), (0, 8, 8), (0, 4, 8), (1, 8, 4), (1, 8, 8), (1, 8, 16)):
+        per = 65536.0 if shape == 0 else 32768.0  # int ops per instruction
+        # the same int ops per SIMD in every case
+        iters = int(20000 * 4 // chains * 8 // waves * (65536.0 / per))
+        name = "32x32x32" if shape == 0 else "16x16x64"
+        for pattern, label in ((0, "zero_operands"), (1, "random_bytes"), (2, "codes_below_32")):
+            lib.w8a8probe_mfma(blocks, 200, pattern, waves, chains, shape, clocks.data_ptr(),
+                               sink.data_ptr(), st())
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            lib.w8a8probe_mfma(blocks, iters, pattern, waves, chains, shape, clocks.data_ptr(),
+                               sink.data_ptr(), st())
+            b.record()
+            b.synchronize()
+            t = a.elapsed_time(b) * 1e-3
+            c = clocks.view(blocks, 2).double().cpu()
+            ghz = (c[:, 0] / c[:, 1] * 0.1).median().item()  # s_memrealtime ticks at 100 MHz
+            ops = blocks * waves * iters * chains * per
+            mf[f"{name}_{waves}waves_{chains}chains_{label}"] = {
+                "POPS": round(ops / t / 1e15, 3), "frac_of_5_POPS": round(ops / t / 1e15 / 5.0, 4),
+                "clock_GHz": round(ghz, 3),
+                "frac_of_clock_scaled_peak": round(ops / t / 1e15 / (5.0 * ghz / 2.4), 4)}
+    out["mfma_i8_only"] = {"blocks": blocks, **mf}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -413,6 +553,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = "cuda:0"
+    if args.ceilings:
+        print(json.dumps({"ceilings": ceilings(dev)}), flush=True)
+        return
     wl = synth.WORKLOADS[args.workload]
     n_batches = max(1, min(args.steps + args.warmup, wl.cal_tokens // wl.cal_batch))
     if args.copy_probe_mib:
@@ -468,7 +611,13 @@ def main():
     kernels = kernel_breakdown(layers, args.kernel_reps)
     if decode:
         kernels["decode_sweep"] = decode_sweep(wl, layers, max(args.kernel_reps, 20))
+    else:
+        kernels["calibration_volume"] = calibration_volume(wl, layers, args.kernel_reps)
     print("[bench] per-kernel pass done", file=sys.stderr, flush=True)
+    others = {}
+    for name in [n for n in args.other_workloads.split(",") if n and n != wl.name]:
+        others[name] = other_workload(name, args.alpha, args.kernel_reps, dev)
+        print(f"[bench] per-kernel pass of {name} done", file=sys.stderr, flush=True)
 
     traffic = pmc_traffic(wl.name)
     rec = {
@@ -517,6 +666,8 @@ def main():
         },
         "kernels": kernels,
     }
+    if others:
+        rec["other_workloads"] = others
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(wl, layers, args.alpha)
