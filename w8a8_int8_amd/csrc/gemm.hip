@@ -204,15 +204,22 @@ __device__ __forceinline__ void tile_of(int bid, int m_tiles, int n_tiles, int& 
 }
 
 // Scheduling hint for the compiler, for one k step of the tiled kernel (see
-// kstep there): column P of NP issues its NQ MFMAs, then its fragment read
-// for the next step (two while P < NQ, each FR chunks) and a share of the
+// kstep there): the step's first MFMA, then the NQ double-buffered fragment
+// reads of the next step; then column P of NP finishes its NQ MFMAs and reads
+// its in-place fragment (FR chunks) for the next step, with a share of the
 // NVM global (LDS-mode) loads, so that no wave stalls on a memory queue
 // while its matrix pipe idles.
 template <int P, int NP, int NQ, int FR, int NVM>
 __device__ __forceinline__ void interleave_cols() {
   constexpr int VPC = (NVM + NP - 1) / NP;  // VMEMs per column
-  __builtin_amdgcn_sched_group_barrier(0x008, NQ, 0);
-  __builtin_amdgcn_sched_group_barrier(0x100, FR * (P < NQ ? 2 : 1), 0);
+  if constexpr (P == 0) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, FR * NQ, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NQ - 1, 0);
+  } else {
+    __builtin_amdgcn_sched_group_barrier(0x008, NQ, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, FR, 0);
   if constexpr (P * VPC < NVM)
     __builtin_amdgcn_sched_group_barrier(0x010, NVM - P * VPC < VPC ? NVM - P * VPC : VPC, 0);
   if constexpr (P + 1 < NP) interleave_cols<P + 1, NP, NQ, FR, NVM>();
@@ -341,9 +348,11 @@ __device__ __forceinline__ void gemm_tile(const int8_t* __restrict__ qa,
   // row (f < FR).  Of the two operands, the one with more fragments per wave
   // (P, NP of them) is read in place: fragment p of the next k step goes into
   // the registers of fragment p as soon as the MFMAs of column p have been
-  // issued.  The other (Q, NQ <= NP) is double-buffered; its fragment q of
-  // the next step is read after column q.  So a wave holds NP + 2 NQ
-  // fragments instead of 2 (NP + NQ).
+  // issued.  The other (Q, NQ <= NP) is double-buffered, and all of its
+  // fragments of the next step are read with the step's first MFMA, since
+  // the next step's first column needs every one of them (measured 3-5%
+  // faster on the 256 x 128 tile than reading fragment q after column q).
+  // So a wave holds NP + 2 NQ fragments instead of 2 (NP + NQ).
   constexpr bool kAin = FM >= FN;  // the activation fragments are read in place
   constexpr int NP = kAin ? FM : FN, NQ = kAin ? FN : FM;
   v4i fp[NP * FR], fq0[NQ * FR], fq1[NQ * FR];
@@ -365,6 +374,10 @@ __device__ __forceinline__ void gemm_tile(const int8_t* __restrict__ qa,
   // fragment p (and fragment p of Q) of step rkk of stage rst.
   auto kstep = [&](const v4i* cq, v4i* nq, bool rd, int rst, int rkk) {
     const int8_t* slot = lds + (rst % NST) * SLOT;
+    if (rd) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) read_frag(slot, rkk, !kAin, q, nq + q * FR);
+    }
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
 #pragma unroll
@@ -374,10 +387,7 @@ __device__ __forceinline__ void gemm_tile(const int8_t* __restrict__ qa,
         else
           acc[p][q] = MmaKind<OUT>::mma(fp + p * FR, cq + q * FR, acc[p][q]);
       }
-      if (rd) {
-        read_frag(slot, rkk, kAin, p, fp + p * FR);
-        if (p < NQ) read_frag(slot, rkk, !kAin, p, nq + p * FR);
-      }
+      if (rd) read_frag(slot, rkk, kAin, p, fp + p * FR);
     }
   };
 
@@ -953,12 +963,19 @@ hipError_t launch_gemm(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N,
   if (!tiled_only && M <= 16) return launch_skinny<1>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
   if (!tiled_only && M <= 32 && N < 16384)
     return launch_skinny<2>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
-  // Pick the tile whose last wave of blocks over 256 CUs is fullest, with a
-  // small preference for the larger tile (more MACs per byte of LDS traffic).
+  // Pick the tile whose last wave of blocks over 256 CUs is fullest, weighted
+  // by the tile's output rate per CU relative to 256 x 256 (eff).  INT8
+  // (16 x 16 x 64 MFMAs), measured per wave of blocks at K = 4096 on
+  // Llama-2-7B-shaped codes: 256 x 256 about 50 us, 256 x 192 44 us,
+  // 256 x 128 37 us, so eff 1, 0.85 and 0.68.  The 16-bit and FP8 forms
+  // (32 x 32 MFMAs) follow the operand bytes per MFMA, which fall with
+  // BM * BN / (BM + BN).
   struct Cand { int bm, bn; double eff; };
-  // eff: operand bytes per MFMA, which the load-return path into LDS limits,
-  // fall with the tile's BM * BN / (BM + BN)
-  const Cand cands[] = {{256, 256, 1.0}, {256, 128, 0.92}, {128, 128, 0.8}, {256, 192, 0.96}};
+  const bool i8 = out_mode <= 2;
+  const Cand cands[] = {{256, 256, 1.0},
+                        {256, 128, i8 ? 0.68 : 0.92},
+                        {128, 128, i8 ? 0.6 : 0.8},
+                        {256, 192, i8 ? 0.85 : 0.96}};
   int best = 0;
   double best_score = -1.0;
   for (int i = 0; i < 4; ++i) {
@@ -972,14 +989,15 @@ hipError_t launch_gemm(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N,
   }
   // Two tile shapes in one grid when the 256 x 256 tiles leave the last wave
   // part-empty: whole waves of them, then 256 x 192 tiles over the remaining
-  // channels.  The estimate counts waves of blocks times the cycles per stage
-  // measured for each tile at the same clock (2339 for 256 x 256, 1853 for
-  // 256 x 192, 1404 for 256 x 128); the split is taken when it is 3% or more
-  // below the single shape's.  Measured: gate_up 4096 -> 22016 at 2048 tokens
-  // 155 -> 152 us, and the OPT-30B 7168-channel layers 2% faster.
+  // channels.  The estimate counts waves of blocks times the time of a wave
+  // of each tile (in cycles per stage, 2339 for 256 x 256; INT8: 2063 for
+  // 256 x 192 and 1715 for 256 x 128, from the wave times above; 16-bit and
+  // FP8: 1853 and 1404, per-block timelines); the split is taken when it is 3%
+  // or more below the single shape's.  Measured: gate_up 4096 -> 22016 at
+  // 2048 tokens 155 -> 152 us, and the OPT-30B 7168-channel layers 2% faster.
   if (cands[best].bm == 256) {
     const int64_t mt = (M + 255) / 256;
-    const int64_t cyc[4] = {2339, 1404, 0, 1853};
+    const int64_t cyc[4] = {2339, i8 ? 1715 : 1404, 0, i8 ? 2063 : 1853};
     const int64_t tiles = mt * ((N + cands[best].bn - 1) / cands[best].bn);
     const int64_t single = (tiles + 255) / 256 * cyc[best];
     const int64_t w = mt * ((N + 255) / 256) / 256;
