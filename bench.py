@@ -498,6 +498,21 @@ def ceilings(dev):
             reads[("chunked_" if chunked else "grid_stride_") + str(blocks)] = round(n / t / 1e9, 1)
     out["read_only_stream_GBs"] = {"bytes": n, "by_layout_and_blocks": reads,
                                    "best": max(reads.values())}
+    # the same read at the sizes of single kernels of the path (rotated over
+    # copies past the last-level cache), the best layout and block count:
+    # a fixed cost per launch dominates the small sizes
+    sizes = {}
+    for mb in (16, 25, 50, 100, 200, 400, 800):
+        nb = mb << 20
+        parts = max(2, -(-(768 << 20) // nb))
+        bufs = [src[(j % (n // nb)) * nb:(j % (n // nb) + 1) * nb] for j in range(min(parts, n // nb))]
+        best = 0.0
+        for blocks in (1024, 2048, 4096, 8192):
+            t = graph_time(lambda i: lib.w8a8probe_read(bufs[i % len(bufs)].data_ptr(), nb, sink.data_ptr(),
+                                                        blocks, 1, st()), 20)
+            best = max(best, nb / t / 1e9)
+        sizes[f"{mb}MiB"] = round(best, 1)
+    out["read_only_stream_GBs"]["by_size_best"] = sizes
     half = n // 2
     dst = torch.empty(half, dtype=torch.uint8, device=dev)
     copies = {}

@@ -6,7 +6,7 @@
 //                    with 16-byte loads, 8 in flight per lane, folded into a
 //                    register (the practical ceiling of the amax kernels)
 //   w8a8probe_copy   a plain copy, 16 bytes per lane (read + write)
-//   w8a8probe_mfma   v_mfma_i32_32x32x32_i8 back to back from registers
+//   w8a8probe_mfma   v_mfma_i32_32x32x32_i8 or _16x16x64_i8 back to back from registers
 //                    (no memory traffic), 4 or 8 waves per block, with each block's
 //                    shader-clock cycles (s_memtime) and 100 MHz wall-clock
 //                    ticks (s_memrealtime) recorded around its loop, so the
