@@ -620,6 +620,9 @@ def main():
     achieved = ops_per_launch / gemm_launch_avg / 1e12
     # few tokens (decode): the GEMM streams the weight and is HBM-bound
     decode = wl.M[0] <= 32
+    # the kernel the launcher picks for that token count (one or two tokens:
+    # whole weight rows streamed; up to 32: 16-channel matrix-core blocks)
+    decode_kernel = "k_gemv_rows" if wl.M[0] <= 2 else "k_gemm_skinny"
     bytes_per_launch = sum(L.gemm_bytes() for L in layers) / len(layers)
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
 
@@ -668,13 +671,13 @@ def main():
             "avg_launch_us": round(gemm_launch_avg * 1e6, 3),
             "event_steps": len(ev_steps),
         } if not decode else {
-            "kernel": "gemm_dequant (k_gemm_skinny)",
+            "kernel": f"gemm_dequant ({decode_kernel})",
             "bound": "hbm",
             "achieved": round(bytes_per_launch / gemm_launch_avg / 1e9, 2),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(bytes_per_launch / gemm_launch_avg / 1e9 / PEAK_HBM_GBS, 4),
-            "traffic": pmc_traffic(wl.name, "gemm_skinny"),
+            "traffic": pmc_traffic(wl.name, decode_kernel.replace("k_", "")),
             "bytes_per_launch": bytes_per_launch,
             "avg_launch_us": round(gemm_launch_avg * 1e6, 3),
             "event_steps": len(ev_steps),

@@ -122,3 +122,38 @@ def test_few_token_kernel_loads_stay_in_bounds(M, N, K):
     MT = -(-M // 16)
     for n0 in sorted({0, (N - 1) // 16 * 16}):
         assert_in_bounds(skinny_loads(M, N, K, n0, MT), M, N, K)
+
+
+def gemv_loads(M, N, K, n0, MT, R=4):
+    """Loads of one block of the row-streaming kernel (one or two tokens):
+    thread t reads 16-byte chunk c = t + 256 j of each of the block's R weight
+    rows and of the MT token slots' activation rows, JB chunks per pass."""
+    kc = K // 16
+    segs = -(-kc // 256)
+    JB = 1 if segs <= 1 else 2 if segs == 2 else 4
+    tid = np.arange(256)
+    nr = min(R, N - n0)
+    out = []
+    c0 = tid.copy()
+    while True:
+        live = c0 < kc  # threads still in the pass loop
+        if not live.any():
+            break
+        for j in range(JB):
+            c = c0 + 256 * j
+            inb = c < kc
+            for r in range(R):
+                vo = np.where(inb, r * K + 16 * c, K_OOB)[live]
+                out.append(("b", n0, vo, 0, nr * K))
+            for t in range(MT):
+                vo = np.where(inb, t * K + 16 * c, K_OOB)[live]
+                out.append(("a", 0, vo, 0, M * K))
+        c0 = c0 + 256 * JB
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16384, 4096), (2, 4096, 16384), (1, 8, 16), (2, 24, 4112),
+                                   (1, 8192, 11008), (2, 16, 131072)])
+def test_row_streaming_kernel_loads_stay_in_bounds(M, N, K):
+    for n0 in sorted({0, (N - 1) // 4 * 4}):
+        assert_in_bounds(gemv_loads(M, N, K, n0, M), M, N, K)

@@ -1,5 +1,6 @@
-"""GPU parity of the runtime forward at few tokens (M <= 32): the skinny
-kernel up to 16 tokens, and from 17 to 32 the INT8 product split along K into
+"""GPU parity of the runtime forward at few tokens (M <= 32): the
+row-streaming kernel up to 2 tokens, the skinny kernel up to 16, and from 17
+to 32 the INT8 product split along K into
 int32 partial slices that a second kernel sums exactly.  Integer accumulation
 is order free, so the output must equal the oracle's bit for bit, and equal
 the unsplit gemm_dequant path's.
@@ -46,7 +47,7 @@ def _make_layer(N, K, dtype, seed):
     return p
 
 
-@pytest.mark.parametrize("M", [1, 5, 8, 16, 17, 31, 32])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 16, 17, 31, 32])
 @pytest.mark.parametrize("N,K", [(4096, 16384), (16384, 4096), (12288, 4096), (136, 80),
                                  (520, 1040), (264, 65536), (8, 16), (4104, 4112)])
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])

@@ -162,7 +162,8 @@ def rand_codes(rows, cols, seed):
 
 
 # shapes cover the four tile configurations (128x128, 256x128, 256x192, 256x256), the
-# few-token kernels (skinny: M <= 16 and M <= 32; 64-channel blocks over the whole
+# few-token kernels (row streaming: M <= 2, one to four 4 KiB row segments in flight
+# and ragged K; skinny: M <= 16 and M <= 32; 64-channel blocks over the whole
 # of K: 12 to 16 tokens on at least 12288 channels), ragged M, N and K tails, K = 0
 # and empty outputs
 GEMM_SHAPES = [(1, 8, 16), (37, 136, 80), (300, 520, 1040), (64, 512, 512),
@@ -170,7 +171,9 @@ GEMM_SHAPES = [(1, 8, 16), (37, 136, 80), (300, 520, 1040), (64, 512, 512),
                (5, 16, 0), (0, 8, 32), (8, 0, 32),
                (1, 4096, 16384), (3, 8, 64), (16, 520, 1040), (17, 136, 80), (32, 264, 4112),
                (33, 136, 80), (32, 16384, 272), (3000, 6000, 272), (2048, 12288, 144),
-               (12, 12288, 1040), (16, 16392, 272), (13, 24576, 4112)]
+               (12, 12288, 1040), (16, 16392, 272), (13, 24576, 4112),
+               (1, 8, 0), (2, 24, 4112), (2, 8, 8192), (1, 8192, 11008),
+               (1, 16, 131072), (2, 40, 12304), (3, 24, 4112)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
@@ -180,7 +183,7 @@ def test_gemm_i32(M, N, K):
     assert np.array_equal(c, oracle.gemm_i32(host(qa), host(qb)))
 
 
-@pytest.mark.parametrize("M,K", [(33, 28672), (300, 131072), (8, 131072)])
+@pytest.mark.parametrize("M,K", [(33, 28672), (300, 131072), (8, 131072), (1, 131072), (2, 131072)])
 def test_gemm_i32_extremes(M, K):
     """All +127 against all -127 up to the largest K the int32 accumulator
     allows (W8A8_MAX_K): -16129 K = -2114060288 at K = 131072, inside int32."""

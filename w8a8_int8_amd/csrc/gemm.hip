@@ -78,6 +78,8 @@ namespace {
 constexpr int kGroupM = 8;       // token tiles per ordering group
 constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
 constexpr int kOob = 0x40000000;  // voffset that is out of range for every resource here
+constexpr int kGemvRows = 4;      // output channels per block of the row-streaming kernel
+constexpr int kGemvMaxM = 2;      // token counts that take the row-streaming kernel
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -725,6 +727,143 @@ hipError_t launch_skinny(const int8_t* qa, const int8_t* qb, int64_t M, int64_t 
   return hipGetLastError();
 }
 
+// Weight-row streaming for one or two tokens.  Here the product is a few
+// dot products per weight row, and what bounds it is how fast the weight
+// streams from HBM; the matrix-core layout (16 rows x 64 bytes per load
+// instruction) streams it slower than whole rows do.  A 256-thread block owns
+// R consecutive output channels; thread t holds the 16-byte chunks t, t + 256,
+// ... of each of its rows, so every block-wide load instruction reads 4 KiB
+// of one row contiguously, with the non-temporal hint (the weight is read
+// once).  JB chunks per row are in flight at a time (R * JB loads per
+// thread), with the activation chunks of the same k range for the MT token
+// slots (rows past M read as zero through their buffer resource).  Products
+// accumulate exactly in int32 with v_dot4 (four int8 products per
+// instruction); each wave reduces its MT * R partial sums by a butterfly
+// (halving the live values at each exchange), the four waves' sums add
+// through LDS, and the same dequant epilogue as the tiled kernel follows.
+template <int MT, int R, int JB, int OUT>
+__global__ __launch_bounds__(256) void k_gemv_rows(const int8_t* __restrict__ qa,
+                                                   const int8_t* __restrict__ qb, int M, int N,
+                                                   int K, const float* __restrict__ sa,
+                                                   const float* __restrict__ sb,
+                                                   void* __restrict__ out) {
+  constexpr int V = MT * R;  // partial sums per thread, a power of two
+  static_assert((V & (V - 1)) == 0 && V <= 64, "butterfly over a power of two");
+  constexpr int kNt = 2;  // cache policy: non-temporal
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = blockIdx.x * R;
+  const int nr = min(R, N - n0);
+  const rsrc_t rw = make_rsrc(qb + (int64_t)n0 * K, (unsigned)nr * (unsigned)K);
+  const rsrc_t rx = make_rsrc(qa, (unsigned)M * (unsigned)K);
+  const int kc = K / 16;  // 16-byte chunks per row
+  int acc[MT][R];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[t][r] = 0;
+  for (int c0 = tid; c0 < kc; c0 += 256 * JB) {
+    v4i w[R][JB], x[MT][JB];
+#pragma unroll
+    for (int j = 0; j < JB; ++j) {
+      const int c = c0 + 256 * j;
+      const bool in = c < kc;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        w[r][j] = __builtin_amdgcn_raw_buffer_load_b128(rw, in ? r * K + 16 * c : kOob, 0, kNt);
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        x[t][j] = __builtin_amdgcn_raw_buffer_load_b128(rx, in ? t * K + 16 * c : kOob, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < JB; ++j)
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          int a = acc[t][r];
+          a = __builtin_amdgcn_sdot4(w[r][j].x, x[t][j].x, a, false);
+          a = __builtin_amdgcn_sdot4(w[r][j].y, x[t][j].y, a, false);
+          a = __builtin_amdgcn_sdot4(w[r][j].z, x[t][j].z, a, false);
+          a = __builtin_amdgcn_sdot4(w[r][j].w, x[t][j].w, a, false);
+          acc[t][r] = a;
+        }
+  }
+  // Butterfly: at the exchange over lane distance d, a lane keeps the upper
+  // half of its live values when bit d of its lane index is set, sends the
+  // other half to its partner and adds what the partner sends back.  After
+  // log2(V) exchanges one value is live, the sum over those lanes of value
+  // idx; the remaining exchanges add it over the low lane bits.
+  int v[V];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int r = 0; r < R; ++r) v[t * R + r] = acc[t][r];
+  int idx = 0;
+#pragma unroll
+  for (int s = 0; (V >> s) > 1; ++s) {
+    const int d = 32 >> s, h = V >> (s + 1);
+    const bool up = (lane & d) != 0;
+#pragma unroll
+    for (int i = 0; i < h; ++i) {
+      const int send = up ? v[i] : v[i + h];
+      const int keep = up ? v[i + h] : v[i];
+      v[i] = keep + __shfl_xor(send, d, 64);
+    }
+    if (up) idx += h;
+  }
+  constexpr int kLow = 64 / V;  // lanes that share one value index
+#pragma unroll
+  for (int d = kLow / 2; d >= 1; d >>= 1) v[0] += __shfl_xor(v[0], d, 64);
+  __shared__ int red[4][V];
+  if ((lane & (kLow - 1)) == 0) red[wave][idx] = v[0];
+  __syncthreads();
+  if (tid >= V) return;
+  const int t = tid / R, r = tid % R;
+  const int m = t, n = n0 + r;
+  if (m >= M || r >= nr) return;
+  const int c = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+  if (OUT == 0) {
+    ((int32_t*)out)[(int64_t)m * N + n] = c;
+  } else {
+    float y = (float)c;
+    y = y * sa[m];
+    y = y * sb[n];
+    // Keep the fp32 product as a value of its own: a lone product followed
+    // by a narrowing conversion may otherwise be compiled into one
+    // mixed-precision FMA that rounds the exact product to 16 bits once,
+    // where the epilogue rounds it to fp32 first.
+    asm volatile("" : "+v"(y));
+    ((unsigned short*)out)[(int64_t)m * N + n] = OUT == 1 ? f32_to_f16_rne(y) : f32_to_bf16_rne(y);
+  }
+}
+
+template <int MT, int JB>
+void launch_gemv_jb(const int8_t* qa, const int8_t* qb, int M, int N, int K, const float* sa,
+                    const float* sb, void* out, int mode, hipStream_t st) {
+  constexpr int R = kGemvRows;
+  const dim3 grid((unsigned)((N + R - 1) / R)), block(256);
+  if (mode == 0)
+    hipLaunchKernelGGL((k_gemv_rows<MT, R, JB, 0>), grid, block, 0, st, qa, qb, M, N, K, sa, sb, out);
+  else if (mode == 1)
+    hipLaunchKernelGGL((k_gemv_rows<MT, R, JB, 1>), grid, block, 0, st, qa, qb, M, N, K, sa, sb, out);
+  else
+    hipLaunchKernelGGL((k_gemv_rows<MT, R, JB, 2>), grid, block, 0, st, qa, qb, M, N, K, sa, sb, out);
+}
+
+// JB: as many 4 KiB row segments in flight as a row has, up to four.
+template <int MT>
+hipError_t launch_gemv(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N, int64_t K,
+                       const float* sa, const float* sb, void* out, int mode, hipStream_t st) {
+  const int64_t segs = (K / 16 + 255) / 256;
+  if (segs <= 1)
+    launch_gemv_jb<MT, 1>(qa, qb, (int)M, (int)N, (int)K, sa, sb, out, mode, st);
+  else if (segs == 2)
+    launch_gemv_jb<MT, 2>(qa, qb, (int)M, (int)N, (int)K, sa, sb, out, mode, st);
+  else
+    launch_gemv_jb<MT, 4>(qa, qb, (int)M, (int)N, (int)K, sa, sb, out, mode, st);
+  return hipGetLastError();
+}
+
 // Split-K few-token GEMM (the runtime forward's path for 17 <= M <= 32, where
 // the skinny kernel's per-16-channel re-reading of the activations costs more
 // than splitting K; measured slower than the skinny kernel below 17).  A block
@@ -960,6 +1099,13 @@ hipError_t launch_gemm(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N,
   // Otherwise the skinny kernel; between 17 and 32 tokens it reads two
   // activation fragments per step, and the tiled kernel is as fast once N
   // alone gives it 128 or more blocks.
+  // One or two tokens: whole weight rows streamed (measured 9-19% faster
+  // than the skinny kernel on the OPT-6.7B decode layers; at four tokens two
+  // to three times slower).
+  if (!tiled_only && M <= kGemvMaxM) {
+    if (M == 1) return launch_gemv<1>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
+    return launch_gemv<2>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
+  }
   if (!tiled_only && M <= 16) return launch_skinny<1>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
   if (!tiled_only && M <= 32 && N < 16384)
     return launch_skinny<2>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
