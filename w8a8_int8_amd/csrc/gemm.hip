@@ -28,7 +28,7 @@
 //
 // K pipeline: K advances BK = 128 bytes per stage (one full cache line per
 // operand row) through NST LDS slots (2 to 4, as many as 160 KB of LDS holds
-// for the tile).  Operand rows go from global memory straight into LDS with
+// for the tile; the 256 x 256 tile keeps a third slot for its weights).  Operand rows go from global memory straight into LDS with
 // buffer loads in LDS mode (16 B per lane, each wave instruction fills 1 KiB
 // of LDS), NST - 1 or NST - 2 stages in flight while one is computed, and a
 // wave never holds global data in registers.  Which waves issue a stage's
@@ -80,6 +80,8 @@ constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format 
 constexpr int kOob = 0x40000000;  // voffset that is out of range for every resource here
 constexpr int kGemvRows = 4;      // output channels per block of the row-streaming kernel
 constexpr int kGemvMaxM = 2;      // token counts that take the row-streaming kernel
+constexpr int kEarlyCols = 1;     // in-place fragments read early before a stage barrier
+constexpr bool kDeepB = true;     // single-shape 256 x 256 tile: a third weight slot
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -211,20 +213,24 @@ __device__ __forceinline__ void tile_of(int bid, int m_tiles, int n_tiles, int& 
 // its in-place fragment (FR chunks) for the next step, with a share of the
 // NVM global (LDS-mode) loads, so that no wave stalls on a memory queue
 // while its matrix pipe idles.
-template <int P, int NP, int NQ, int FR, int NVM>
+// EARLY: the step before a stage barrier, where the next step's fragment of
+// the last column is read with the first MFMA too (into a register set of its
+// own) rather than after that column's MFMAs.
+template <int P, int NP, int NQ, int FR, int NVM, bool EARLY = false>
 __device__ __forceinline__ void interleave_cols() {
   constexpr int VPC = (NVM + NP - 1) / NP;  // VMEMs per column
+  constexpr int EC = EARLY ? kEarlyCols : 0;
   if constexpr (P == 0) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, FR * NQ, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, FR * NQ + EC * FR, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, NQ - 1, 0);
   } else {
     __builtin_amdgcn_sched_group_barrier(0x008, NQ, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x100, FR, 0);
+  if constexpr (P < NP - EC) __builtin_amdgcn_sched_group_barrier(0x100, FR, 0);
   if constexpr (P * VPC < NVM)
     __builtin_amdgcn_sched_group_barrier(0x010, NVM - P * VPC < VPC ? NVM - P * VPC : VPC, 0);
-  if constexpr (P + 1 < NP) interleave_cols<P + 1, NP, NQ, FR, NVM>();
+  if constexpr (P + 1 < NP) interleave_cols<P + 1, NP, NQ, FR, NVM, EARLY>();
 }
 
 
@@ -234,7 +240,7 @@ __device__ __forceinline__ void interleave_cols() {
 // tell the LDS-mode loads of later stages from the fragment reads of the
 // current one and waits for every outstanding load before the first reads
 // (measured 12% slower on the 256 x 192 tile).
-constexpr int kTileLds = 3 * (256 + 128) * 128;
+constexpr int kTileLds = 2 * 256 * 128 + 3 * 256 * 128;  // 160 KiB, the whole LDS
 __shared__ __attribute__((aligned(1024))) int8_t lds[kTileLds];
 
 // One output tile (token tile tm, channel tile tn) of the tiled GEMM.  OUT as
@@ -242,7 +248,7 @@ __shared__ __attribute__((aligned(1024))) int8_t lds[kTileLds];
 // BK bytes per stage through NST LDS slots.  N is the number of channels this
 // call covers (qb, sb and out start at its first one) and ldc the row stride
 // of out in elements.
-template <int BM, int BN, int BK, int NST, int WGM, int WGN, int OUT>
+template <int BM, int BN, int BK, int NST, int WGM, int WGN, int OUT, bool DEEP = false>
 __device__ __forceinline__ void gemm_tile(const int8_t* __restrict__ qa,
                                           const int8_t* __restrict__ qb, int M, int N, int K,
                                           const float* __restrict__ sa,
@@ -262,11 +268,21 @@ __device__ __forceinline__ void gemm_tile(const int8_t* __restrict__ qa,
   constexpr int LB = BN / RPI / NW;             // ... weights
   constexpr int L = LA + LB;
   constexpr int SLOT = (BM + BN) * BK;          // bytes per LDS stage
+  // Two-slot tiles with 8 waves may keep three weight slots: the weight
+  // stage then goes out two stages ahead instead of one.
+  constexpr bool kHalfT = NST == 2 && WGM * WGN == 8;
+  constexpr int NSA = NST;
+  constexpr int NSB =
+      (DEEP && kHalfT && BN == 256 && (NST * BM + (NST + 1) * BN) * BK <= kTileLds) ? NST + 1 : NST;
+  // With as many weight as activation slots, stage s holds its activation
+  // and weight rows side by side in one (BM + BN) x BK slot; otherwise the
+  // activation slots come first, then the weight slots.
+  constexpr bool kSym = NSA == NSB;
   static_assert(LA >= 1 && LB >= 1 && LA * RPI * NW == BM && LB * RPI * NW == BN &&
                 FM >= 1 && FN >= 1 && FM * MB == WM && FN * MB == WN && KK % 2 == 0 &&
                 (MB / RPW) % CPR == 0, "unsupported tile");
   static_assert(NST >= 2 && (NST - 1) * 2 * L < 64, "unsupported pipeline depth");  // vmcnt range
-  static_assert(NST * SLOT <= kTileLds, "LDS size");
+  static_assert(NSA * BM * BK + NSB * BN * BK <= kTileLds, "LDS size");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -307,9 +323,16 @@ __device__ __forceinline__ void gemm_tile(const int8_t* __restrict__ qa,
   // moves no data, keeps every wave's per-stage load count constant (so
   // fixed vmcnt values serve every iteration) and only touches the slot that
   // the stage would have used, which no live stage occupies.
+  auto slot_a = [&](int st) -> int8_t* {
+    return kSym ? lds + (st % NST) * SLOT : lds + (st % NSA) * BM * BK;
+  };
+  auto slot_b = [&](int st) -> int8_t* {
+    return kSym ? lds + (st % NST) * SLOT + BM * BK : lds + NSA * BM * BK + (st % NSB) * BN * BK;
+  };
   auto dma = [&](int st, int j0, int j1) {
     const int k0 = st * BK;
-    int8_t* slot = lds + (st % NST) * SLOT;
+    int8_t* sa_ = slot_a(st);
+    int8_t* sb_ = slot_b(st);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int ro = h * (NW / 2) * RPI * K;
@@ -319,14 +342,46 @@ __device__ __forceinline__ void gemm_tile(const int8_t* __restrict__ qa,
         if (h * L + i < j0 || h * L + i >= j1) continue;
         const int vo = (k0 + kc_a[i] >= K) ? kOob : voff_a[i] + ro;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ra, (lds_void_t*)(slot + (i * NW + w) * 1024), 16, vo, k0, 0, 0);
+            ra, (lds_void_t*)(sa_ + (i * NW + w) * 1024), 16, vo, k0, 0, 0);
       }
 #pragma unroll
       for (int i = 0; i < LB; ++i) {
         if (h * L + LA + i < j0 || h * L + LA + i >= j1) continue;
         const int vo = (k0 + kc_b[i] >= K) ? kOob : voff_b[i] + ro;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rb, (lds_void_t*)(slot + BM * BK + (i * NW + w) * 1024), 16, vo, k0, 0, 0);
+            rb, (lds_void_t*)(sb_ + (i * NW + w) * 1024), 16, vo, k0, 0, 0);
+      }
+    }
+  };
+  // The two-slot tiles' loads (issued by waves 0 .. NW/2 - 1 for themselves
+  // and for wave + NW/2): all activation loads of stage sta, then all weight
+  // loads of stage stb (a negative stage: none).
+  auto dma2 = [&](int sta, int stb) {
+#pragma unroll
+    for (int op = 0; op < 2; ++op) {
+      const int st = op == 0 ? sta : stb;
+      if (st < 0) continue;
+      const int k0 = st * BK;
+      int8_t* slot = op == 0 ? slot_a(st) : slot_b(st);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int ro = h * (NW / 2) * RPI * K;
+        const int w = wave + h * (NW / 2);
+        if (op == 0) {
+#pragma unroll
+          for (int i = 0; i < LA; ++i) {
+            const int vo = (k0 + kc_a[i] >= K) ? kOob : voff_a[i] + ro;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra, (lds_void_t*)(slot + (i * NW + w) * 1024), 16, vo, k0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < LB; ++i) {
+            const int vo = (k0 + kc_b[i] >= K) ? kOob : voff_b[i] + ro;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rb, (lds_void_t*)(slot + (i * NW + w) * 1024), 16, vo, k0, 0, 0);
+          }
+        }
       }
     }
   };
@@ -337,7 +392,7 @@ __device__ __forceinline__ void gemm_tile(const int8_t* __restrict__ qa,
   const int fr = lane % MB, fk = lane / MB;
   const int fsw = (fr / RPW) % CPR;
   const int off_a = (wm * WM + fr) * BK;
-  const int off_b = BM * BK + (wn * WN + fr) * BK;
+  const int off_b = (wn * WN + fr) * BK;
 
   typedef typename MmaKind<OUT>::acc_t acc_t;
   acc_t acc[FN][FM];
@@ -357,41 +412,56 @@ __device__ __forceinline__ void gemm_tile(const int8_t* __restrict__ qa,
   // So a wave holds NP + 2 NQ fragments instead of 2 (NP + NQ).
   constexpr bool kAin = FM >= FN;  // the activation fragments are read in place
   constexpr int NP = kAin ? FM : FN, NQ = kAin ? FN : FM;
-  v4i fp[NP * FR], fq0[NQ * FR], fq1[NQ * FR];
-  auto read_frag = [&](const int8_t* slot, int kk, bool act, int i, v4i* dst) {
+  constexpr int EC = kEarlyCols < NP ? kEarlyCols : NP;
+  v4i fp[NP * FR], fq0[NQ * FR], fq1[NQ * FR], fx[EC * FR];
+  auto read_frag = [&](int st, int kk, bool act, int i, v4i* dst) {
+    const int8_t* slot = act ? slot_a(st) : slot_b(st);
     const int base = act ? off_a + i * MB * BK : off_b + i * MB * BK;
 #pragma unroll
     for (int f = 0; f < FR; ++f)
       dst[f] = *(const v4i*)(slot + base + (((FR * (LPR * kk + fk) + f) ^ fsw) << 4));
   };
   auto read_all = [&](int st, int kk, v4i* fq) {
-    const int8_t* slot = lds + (st % NST) * SLOT;
 #pragma unroll
-    for (int p = 0; p < NP; ++p) read_frag(slot, kk, kAin, p, fp + p * FR);
+    for (int p = 0; p < NP; ++p) read_frag(st, kk, kAin, p, fp + p * FR);
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) read_frag(slot, kk, !kAin, q, fq + q * FR);
+    for (int q = 0; q < NQ; ++q) read_frag(st, kk, !kAin, q, fq + q * FR);
   };
 
-  // One k step: column p issues its NQ MFMAs, then (when `rd`) the reads of
-  // fragment p (and fragment p of Q) of step rkk of stage rst.
-  auto kstep = [&](const v4i* cq, v4i* nq, bool rd, int rst, int rkk) {
-    const int8_t* slot = lds + (rst % NST) * SLOT;
+  // One k step: the reads of the Q fragments of step rkk of stage rst go
+  // out with the first MFMA; then column p issues its NQ MFMAs and (when
+  // `rd`) reads its P fragment of step rkk in place.  In the step before a
+  // stage barrier (early) the last column's next fragment is read at the
+  // start as well, into fx, so that the reads a wave must wait for at the
+  // barrier were issued a column of MFMAs earlier; the step after the barrier
+  // (use_fx) takes that column's operand from fx.
+  auto kstep = [&](const v4i* cq, v4i* nq, bool rd, int rst, int rkk, auto early_tag,
+                   auto use_fx_tag) {
+    constexpr bool kEarly = decltype(early_tag)::value;
+    constexpr bool kUseFx = decltype(use_fx_tag)::value;
     if (rd) {
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) read_frag(slot, rkk, !kAin, q, nq + q * FR);
+      for (int q = 0; q < NQ; ++q) read_frag(rst, rkk, !kAin, q, nq + q * FR);
+      if constexpr (kEarly) {
+#pragma unroll
+        for (int e = 0; e < EC; ++e) read_frag(rst, rkk, kAin, NP - EC + e, fx + e * FR);
+      }
     }
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
+      const v4i* cp = (kUseFx && p >= NP - EC) ? fx + (p - (NP - EC)) * FR : fp + p * FR;
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
         if constexpr (kAin)
-          acc[q][p] = MmaKind<OUT>::mma(cq + q * FR, fp + p * FR, acc[q][p]);
+          acc[q][p] = MmaKind<OUT>::mma(cq + q * FR, cp, acc[q][p]);
         else
-          acc[p][q] = MmaKind<OUT>::mma(fp + p * FR, cq + q * FR, acc[p][q]);
+          acc[p][q] = MmaKind<OUT>::mma(cp, cq + q * FR, acc[p][q]);
       }
-      if (rd) read_frag(slot, rkk, kAin, p, fp + p * FR);
+      if (rd && !(kEarly && p >= NP - EC)) read_frag(rst, rkk, kAin, p, fp + p * FR);
     }
   };
+  const std::false_type kNo{};
+  const std::true_type kYes{};
 
   // Pipeline (stage s lives in slot s % NST).  Iteration kt computes stage kt
   // as KK k steps (64 bytes deep for INT8 and FP8, 32 for fp16 / bf16); the
@@ -409,7 +479,11 @@ __device__ __forceinline__ void gemm_tile(const int8_t* __restrict__ qa,
   //    PER per step, each wave its own; NST-2 stages stay in flight.
   //  - NST == 2 with 8 waves: the loads of stage kt+2 go into slot kt right
   //    after the barrier, all issued by waves 0..3 (one per SIMD), each its
-  //    own and those of wave + 4, while waves 4..7 only compute.
+  //    own and those of wave + 4, while waves 4..7 only compute.  The
+  //    256 x 256 tile of the single-shape kernel keeps a third weight slot
+  //    (the whole 160 KiB of LDS): its weight loads go out two stages ahead
+  //    (measured 4-11% faster on the OPT-30B and Llama-2-70B layers, equal
+  //    on the others; slower inside the two-shape grid and on 256 x 192).
   //  - NST == 2 with 4 waves: each wave issues its own after the barrier.
   constexpr bool kSpread = NST >= 3;
   constexpr bool kHalf = !kSpread && NW == 8;
@@ -421,43 +495,72 @@ __device__ __forceinline__ void gemm_tile(const int8_t* __restrict__ qa,
   // only compute: with a run-time branch on the role inside the loop, the
   // accumulators would meet at every join, where the register allocator
   // copies them.
+  // Two-slot tiles with a third weight slot (NSB = 3): the prologue issues
+  // activations 0, weights 0, weights 1, activations 1, weights 2, and the
+  // barrier of iteration kt activations kt+2 and weights kt+3, so at each
+  // barrier only the weights of the next-but-one stage may still be in flight.
+  constexpr int LAW = 2 * LA, LBW = 2 * LB;  // a loading wave's loads per stage and operand
+  static_assert(kSpread || kHalf, "pipeline");
+  constexpr int kWaitBarrier = kSpread ? (NST - 2) * LW : (NSB == 3 ? LBW : 0);
+  constexpr int kWaitFirst = kSpread ? (NST - 2) * LW : (NSB == 3 ? 2 * LBW + LAW : LW);
   auto kloop = [&](auto loads_tag) {
     constexpr bool kLoads = decltype(loads_tag)::value;
     // prologue: the stages in flight before iteration 0
-    constexpr int PRE = kSpread ? NST - 1 : NST;
     if constexpr (kLoads) {
+      if constexpr (kSpread) {
 #pragma unroll
-      for (int st = 0; st < PRE; ++st) dma(st, 0, LW);
+        for (int st = 0; st < NST - 1; ++st) dma(st, 0, LW);
+      } else if constexpr (NSB == 3) {
+        dma2(0, 0);
+        dma2(-1, 1);
+        dma2(1, 2);
+      } else {
+        dma(0, 0, LW);
+        dma(1, 0, LW);
+      }
     }
-    wait_vmcnt<(PRE - 1) * LW>();  // stage 0 landed
+    wait_vmcnt<kWaitFirst>();  // stage 0 landed
     block_barrier();
     read_all(0, 0, fq0);
     for (int kt = 0; kt < nk - 1; ++kt) {
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
+      // the steps before the barrier step: all but the last one plain
+      auto pre = [&](auto kk_tag) {
+        constexpr int kk = decltype(kk_tag)::value;
         v4i* cq = (kk & 1) ? fq1 : fq0;
         v4i* nq = (kk & 1) ? fq0 : fq1;
-        if (kk + 1 < KK) {
-          if constexpr (kSpread) {
-            dma(kt + NST - 1, kk * PER, min((kk + 1) * PER, LW));
-            kstep(cq, nq, true, kt, kk + 1);
-            interleave_cols<0, NP, NQ, FR, PER>();
-          } else {
-            kstep(cq, nq, true, kt, kk + 1);
-            interleave_cols<0, NP, NQ, FR, 0>();
-          }
+        constexpr bool kE = kk == KK - 2;
+        if constexpr (kSpread) {
+          dma(kt + NST - 1, kk * PER, min((kk + 1) * PER, LW));
+          kstep(cq, nq, true, kt, kk + 1, std::integral_constant<bool, kE>{}, kNo);
+          interleave_cols<0, NP, NQ, FR, PER, kE>();
         } else {
-          wait_vmcnt<(NST - 2) * LW>();  // this wave's loads of stage kt+1 landed
-          wait_lgkmcnt0();               // this wave's reads of slot kt are done
-          block_barrier();               // every wave: stage kt+1 landed, slot kt free
-          if constexpr (!kSpread && kLoads) {
-            dma(kt + NST, 0, LW);
-            kstep(cq, nq, true, kt + 1, 0);
-            interleave_cols<0, NP, NQ, FR, LW>();
-          } else {
-            kstep(cq, nq, true, kt + 1, 0);
-            interleave_cols<0, NP, NQ, FR, 0>();
-          }
+          kstep(cq, nq, true, kt, kk + 1, std::integral_constant<bool, kE>{}, kNo);
+          interleave_cols<0, NP, NQ, FR, 0, kE>();
+        }
+      };
+      pre(std::integral_constant<int, 0>{});
+      if constexpr (KK > 2) pre(std::integral_constant<int, 1>{});
+      if constexpr (KK > 3) pre(std::integral_constant<int, 2>{});
+      static_assert(KK <= 4, "k steps per stage");
+      {
+        constexpr int kk = KK - 1;
+        v4i* cq = (kk & 1) ? fq1 : fq0;
+        v4i* nq = (kk & 1) ? fq0 : fq1;
+        // the previous step's MFMAs stay ahead of the waits
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<kWaitBarrier>();  // this wave's loads of stage kt+1 landed
+        wait_lgkmcnt0();             // this wave's reads of slot kt are done
+        block_barrier();             // every wave: stage kt+1 landed, slot kt free
+        if constexpr (!kSpread && kLoads) {
+          if constexpr (NSB == 3)
+            dma2(kt + 2, kt + 3);
+          else
+            dma(kt + 2, 0, LW);
+          kstep(cq, nq, true, kt + 1, 0, kNo, kYes);
+          interleave_cols<0, NP, NQ, FR, LW>();
+        } else {
+          kstep(cq, nq, true, kt + 1, 0, kNo, kYes);
+          interleave_cols<0, NP, NQ, FR, 0>();
         }
       }
     }
@@ -465,7 +568,7 @@ __device__ __forceinline__ void gemm_tile(const int8_t* __restrict__ qa,
     for (int kk = 0; kk < KK; ++kk) {
       v4i* cq = (kk & 1) ? fq1 : fq0;
       v4i* nq = (kk & 1) ? fq0 : fq1;
-      kstep(cq, nq, kk + 1 < KK, nk - 1, kk + 1);
+      kstep(cq, nq, kk + 1 < KK, nk - 1, kk + 1, kNo, kNo);
     }
     wait_vmcnt<0>();  // no LDS-mode load may outlive the block's LDS
   };
@@ -577,7 +680,7 @@ k_gemm_i8(const int8_t* __restrict__ qa, const int8_t* __restrict__ qb, int M, i
           int m_tiles, int n_tiles) {
   int tm, tn;
   tile_of(blockIdx.x, m_tiles, n_tiles, tm, tn);
-  gemm_tile<BM, BN, BK, NST, WGM, WGN, OUT>(qa, qb, M, N, K, sa, sb, out, N, tm, tn);
+  gemm_tile<BM, BN, BK, NST, WGM, WGN, OUT, kDeepB>(qa, qb, M, N, K, sa, sb, out, N, tm, tn);
 }
 
 // Two tile shapes in one grid, for a channel count whose tiles of the larger
