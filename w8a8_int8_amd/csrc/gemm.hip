@@ -1248,7 +1248,12 @@ hipError_t launch_gemm(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N,
     const int64_t mt = (M + 255) / 256;
     const int64_t cyc[4] = {2339, i8 ? 1715 : 1404, 0, i8 ? 2063 : 1853};
     const int64_t tiles = mt * ((N + cands[best].bn - 1) / cands[best].bn);
-    const int64_t single = (tiles + 255) / 256 * cyc[best];
+    // The single-shape 256 x 256 tile streams its weights two stages ahead;
+    // on long rows that makes it about 11% faster than inside the two-shape
+    // grid (OPT-30B fc2, K = 28672: 651 -> 616 us), while at K = 4096 and
+    // 7168 the two-shape grid stays ahead (measured).
+    const int64_t c_single = (best == 0 && K >= 16384) ? 2100 : cyc[best];
+    const int64_t single = (tiles + 255) / 256 * c_single;
     const int64_t w = mt * ((N + 255) / 256) / 256;
     if (w >= 1 && (w * 256) % mt == 0 && w * 256 / mt * 256 < N) {
       const int64_t nt1 = w * 256 / mt;
