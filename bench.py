@@ -621,8 +621,8 @@ def main():
     # few tokens (decode): the GEMM streams the weight and is HBM-bound
     decode = wl.M[0] <= 32
     # the kernel the launcher picks for that token count (one or two tokens:
-    # whole weight rows streamed; up to 32: 16-channel matrix-core blocks)
-    decode_kernel = "k_gemv_rows" if wl.M[0] <= 2 else "k_gemm_skinny"
+    # whole weight rows streamed; up to 32: weight pieces transposed in LDS)
+    decode_kernel = "k_gemv_rows" if wl.M[0] <= 2 else "k_gemm_fewtok"
     bytes_per_launch = sum(L.gemm_bytes() for L in layers) / len(layers)
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
 

@@ -96,12 +96,18 @@ def test_workspace_bytes():
     assert lib.w8a8_linear_workspace_bytes(1, 8, 16) == 256 + 256  # one split: no partials
     assert lib.w8a8_linear_workspace_bytes(2048, 4096, 4096) == 2048 * 4096 + 2048 * 4
     assert lib.w8a8_linear_workspace_bytes(-1, 8, 16) == 0
-    # 32 tokens: 4096 outputs are 64 blocks of 64 channels, so K = 16384 splits four ways
-    assert lib.w8a8_linear_workspace_bytes(32, 4096, 16384) == 32 * 16384 + 256 + 4 * 32 * 4096 * 4
-    assert lib.w8a8_linear_workspace_bytes(32, 16384, 4096) == 32 * 4096 + 256  # 256 blocks: no split
-    assert lib.w8a8_linear_workspace_bytes(16, 4096, 16384) == 16 * 16384 + 256  # unsplit kernel
-    assert lib.w8a8_linear_workspace_bytes(32, 12288, 4096) == 32 * 4096 + 256  # 192 tiles: one range
-    assert lib.w8a8_linear_workspace_bytes(32, 8192, 4096) == 32 * 4096 + 256 + 2 * 32 * 8192 * 4
+    # 17-32 tokens split K only below 2048 output channels: 1024 outputs are 16
+    # blocks of 64 channels, and K = 16384 (256 steps of 64) splits eight ways
+    # (at least 32 steps per split); K = 4096 two ways
+    assert lib.w8a8_linear_workspace_bytes(32, 1024, 16384) == 32 * 16384 + 256 + 8 * 32 * 1024 * 4
+    assert lib.w8a8_linear_workspace_bytes(32, 1024, 4096) == 32 * 4096 + 256 + 2 * 32 * 1024 * 4
+    # (slices rounded up to 256 bytes)
+    assert lib.w8a8_linear_workspace_bytes(17, 2040, 4096) == 17 * 4096 + 256 + (2 * 17 * 2040 * 4 + 64)
+    # from 2048 channels the unsplit few-token kernel: no partial slices
+    assert lib.w8a8_linear_workspace_bytes(32, 2048, 16384) == 32 * 16384 + 256
+    assert lib.w8a8_linear_workspace_bytes(32, 4096, 16384) == 32 * 16384 + 256
+    assert lib.w8a8_linear_workspace_bytes(32, 16384, 4096) == 32 * 4096 + 256
+    assert lib.w8a8_linear_workspace_bytes(16, 1024, 16384) == 16 * 16384 + 256  # below 17 tokens
 
 
 @cpu_only

@@ -100,28 +100,40 @@ def test_the_scalar_offset_is_not_a_row_offset():
                                      row_offset_in_scalar=True), M, N, K)
 
 
-def skinny_loads(M, N, K, n0, MT, NW=8, U=8):
-    """Loads of one block of the few-token kernel: 16 weight rows, all of K."""
+def fewtok_loads(M, N, K, n0, MT, NW, CG):
+    """Loads of one block of the 3-32 token kernel: 16 CG weight rows in
+    256-byte pieces (wave w takes a contiguous range of the pieces), and the
+    activation fragments of the same k range for MT token slots."""
     lane = np.arange(64)
+    lr, lc = lane // 16, lane % 16
     r16, kq = lane % 16, lane // 16
-    nsteps = -(-K // 64)
-    out = []
-    recs_w = min(16, N - n0) * K
+    npc = -(-K // 256)
+    per = -(-npc // NW)
+    recs_w = min(16 * CG, N - n0) * K
     recs_x = M * K
-    for st in range(nsteps + NW * U):  # steps past the end are issued out of range
-        k0 = st * 64
-        out_k = (st >= nsteps) | (k0 + kq * 16 >= K)
-        out.append(("b", n0, np.where(out_k, K_OOB, r16 * K + kq * 16), k0, recs_w))
-        for t in range(MT):
-            out.append(("a", 0, np.where(out_k, K_OOB, (t * 16 + r16) * K + kq * 16), k0, recs_x))
+    out = []
+    for w in range(NW):
+        for p in range(w * per, min(npc, (w + 1) * per)):
+            kb = 256 * p
+            for c in range(CG):
+                for i in range(4):
+                    row = 16 * c + 4 * i + lr
+                    col = kb + 16 * lc
+                    out.append(("b", n0, np.where(col < K, row * K + col, K_OOB), 0, recs_w))
+            for s in range(4):
+                for t in range(MT):
+                    col = kb + 64 * s + 16 * kq
+                    out.append(("a", 0, np.where(col < K, (16 * t + r16) * K + col, K_OOB), 0, recs_x))
     return out
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 16392, 4096), (13, 136, 1040), (31, 4104, 16384)])
+@pytest.mark.parametrize("M,N,K", [(3, 16392, 4096), (13, 136, 1040), (31, 4104, 16384), (17, 8, 16),
+                                   (32, 12288, 4112), (5, 24, 65536)])
 def test_few_token_kernel_loads_stay_in_bounds(M, N, K):
     MT = -(-M // 16)
-    for n0 in sorted({0, (N - 1) // 16 * 16}):
-        assert_in_bounds(skinny_loads(M, N, K, n0, MT), M, N, K)
+    NW, CG = (4, 2) if N >= 16 * 2 * 384 else (8, 1)
+    for n0 in sorted({0, (N - 1) // (16 * CG) * (16 * CG)}):
+        assert_in_bounds(fewtok_loads(M, N, K, n0, MT, NW, CG), M, N, K)
 
 
 def gemv_loads(M, N, K, n0, MT, R=4):

@@ -1,6 +1,7 @@
 """GPU parity of the runtime forward at few tokens (M <= 32): the
-row-streaming kernel up to 2 tokens, the skinny kernel up to 16, and from 17
-to 32 the INT8 product split along K into
+row-streaming kernel up to 2 tokens, the few-token kernel (weight pieces
+transposed through LDS) up to 32, and from 17 to 32 on fewer than 2048
+channels the INT8 product split along K into
 int32 partial slices that a second kernel sums exactly.  Integer accumulation
 is order free, so the output must equal the oracle's bit for bit, and equal
 the unsplit gemm_dequant path's.
@@ -77,7 +78,7 @@ def test_linear_decode_split_k(dtype, N, K, M):
 def test_linear_decode_repeat_calls_bit_identical():
     """The partial slices are overwritten on every call: a second call with
     other activations, then the first again, reproduces the first output."""
-    N, K, M = 4096, 16384, 32
+    N, K, M = 1024, 16384, 32
     p = layer(N, K, torch.float16, 3)
     g = torch.Generator(device="cpu").manual_seed(9)
     xa = torch.randn((M, K), generator=g).half().to(DEV)
@@ -90,7 +91,7 @@ def test_linear_decode_repeat_calls_bit_identical():
 
 
 def test_linear_workspace_too_small_is_rejected():
-    N, K, M = 4096, 16384, 32
+    N, K, M = 1024, 16384, 32
     p = layer(N, K, torch.float16, 5)
     x = torch.zeros((M, K), dtype=torch.float16, device=DEV)
     need = w8.linear_workspace_bytes(M, N, K)

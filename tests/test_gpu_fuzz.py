@@ -2,7 +2,7 @@
 
 Shapes are drawn small (the oracle finishes each in well under a second) but
 cover empty inputs, ragged tails of every tile size, the few-token GEMM paths
-(skinny and split-K), zero rows, dead channels, both 16-bit input types, the
+(row streaming, LDS-transposed pieces and split-K), zero rows, dead channels, both 16-bit input types, the
 FP8 quantizer, the RMS-norm fold and the dense 16-bit product.
 """
 from __future__ import annotations

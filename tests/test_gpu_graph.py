@@ -21,9 +21,10 @@ def fill(t: torch.Tensor, seed: int, scale: float = 1.0):
     t.copy_((torch.randn(t.shape, generator=g) * scale).to(t.dtype))
 
 
-# 8 tokens: skinny GEMM; 24 tokens on 4096 channels: split-K with partial
-# slices and the reduction kernel; 512 tokens: the tiled GEMM
-@pytest.mark.parametrize("M,N", [(8, 12288), (24, 4096), (512, 12288)])
+# 8 and 24 tokens on 4096 or more channels: the few-token GEMM; 24 tokens on
+# 1024 channels: split-K with partial slices and the reduction kernel; 512
+# tokens: the tiled GEMM
+@pytest.mark.parametrize("M,N", [(8, 12288), (24, 4096), (24, 1024), (512, 12288)])
 def test_path_replays_match_eager(M, N):
     K = 4096
     xc = torch.empty((2048, K), dtype=torch.float16, device=DEV)

@@ -163,9 +163,8 @@ def rand_codes(rows, cols, seed):
 
 # shapes cover the four tile configurations (128x128, 256x128, 256x192, 256x256), the
 # few-token kernels (row streaming: M <= 2, one to four 4 KiB row segments in flight
-# and ragged K; skinny: M <= 16 and M <= 32; 64-channel blocks over the whole
-# of K: 12 to 16 tokens on at least 12288 channels), ragged M, N and K tails, K = 0
-# and empty outputs
+# and ragged K; weight pieces through LDS: 3 to 32 tokens, one channel group per wave below
+# 12288 channels and two from there), ragged M, N and K tails, K = 0 and empty outputs
 GEMM_SHAPES = [(1, 8, 16), (37, 136, 80), (300, 520, 1040), (64, 512, 512),
                (2048, 4096, 256), (4000, 8184, 272), (4096, 8192, 144), (513, 264, 4112),
                (5, 16, 0), (0, 8, 32), (8, 0, 32),
