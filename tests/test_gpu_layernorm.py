@@ -72,7 +72,7 @@ def stress_rows(x):
     return x
 
 
-@pytest.mark.parametrize("rows,cols", [(4, 16), (5, 48), (64, 512), (1025, 4096), (2050, 7168),
+@pytest.mark.parametrize("rows,cols", [(4, 16), (5, 48), (9, 4096), (7, 11008), (64, 512), (1025, 4096), (2050, 7168),
                                        (33, 28672), (5, 65536)])
 def test_layernorm_quant_rows(rows, cols):
     x, gamma, beta, inv_s = case(rows, cols, rows * 7 + cols, offset=0.3)
