@@ -337,15 +337,17 @@ w8a8_status_t w8a8_gemm_dequant_e4m3(const uint8_t* qa, const float* sa, const u
 
 /* Bytes of workspace w8a8_linear needs for M tokens, K input and N output
  * channels: the INT8 activations and their per-token scales, then, for
- * 17 <= M <= 32 when the product is split along K, the int32 partial sums
- * (S x M x N); each part 256-byte aligned.  0 for negative sizes. */
+ * 17 <= M <= 32 on fewer than 2048 output channels, where the product is
+ * split along K, the int32 partial sums (S x M x N); each part 256-byte
+ * aligned.  0 for negative sizes. */
 size_t w8a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
  * Runtime forward of one smoothed W8A8 linear layer (steps 3 + 4 + 5):
  * (qX, sx) = scale_quant_rows(x, inv_s) into the workspace, then
  * y = gemm_dequant(qX, sx, qw, sw).  No host sync.  For 17 <= M <= 32
- * (decode batches) the product may be split along K over more blocks: each
+ * (decode batches) on fewer than 2048 output channels the product is split
+ * along K over more blocks: each
  * block adds its int32 partial sums exactly, a second kernel adds the S slices
  * (integer addition, exact) and applies the same epilogue, so y is
  * bit-identical to gemm_dequant's.
