@@ -128,10 +128,10 @@ def fewtok_loads(M, N, K, n0, MT, NW, CG):
 
 
 @pytest.mark.parametrize("M,N,K", [(3, 16392, 4096), (13, 136, 1040), (31, 4104, 16384), (17, 8, 16),
-                                   (32, 12288, 4112), (5, 24, 65536)])
+                                   (32, 12288, 4112), (5, 24, 65536), (20, 12296, 272)])
 def test_few_token_kernel_loads_stay_in_bounds(M, N, K):
     MT = -(-M // 16)
-    NW, CG = (4, 2) if N >= 16 * 2 * 384 else (8, 1)
+    NW, CG = (8, 1) if N < 12288 else (8, 4) if MT == 2 else (4, 2)
     for n0 in sorted({0, (N - 1) // (16 * CG) * (16 * CG)}):
         assert_in_bounds(fewtok_loads(M, N, K, n0, MT, NW, CG), M, N, K)
 

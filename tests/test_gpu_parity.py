@@ -164,7 +164,7 @@ def rand_codes(rows, cols, seed):
 # shapes cover the four tile configurations (128x128, 256x128, 256x192, 256x256), the
 # few-token kernels (row streaming: M <= 2, one to four 4 KiB row segments in flight
 # and ragged K; weight pieces through LDS: 3 to 32 tokens, one channel group per wave below
-# 12288 channels and two from there), ragged M, N and K tails, K = 0 and empty outputs
+# 12288 channels and two or four from there), ragged M, N and K tails, K = 0 and empty outputs
 GEMM_SHAPES = [(1, 8, 16), (37, 136, 80), (300, 520, 1040), (64, 512, 512),
                (2048, 4096, 256), (4000, 8184, 272), (4096, 8192, 144), (513, 264, 4112),
                (5, 16, 0), (0, 8, 32), (8, 0, 32),
@@ -172,7 +172,7 @@ GEMM_SHAPES = [(1, 8, 16), (37, 136, 80), (300, 520, 1040), (64, 512, 512),
                (33, 136, 80), (32, 16384, 272), (3000, 6000, 272), (2048, 12288, 144),
                (12, 12288, 1040), (16, 16392, 272), (13, 24576, 4112),
                (1, 8, 0), (2, 24, 4112), (2, 8, 8192), (1, 8192, 11008),
-               (1, 16, 131072), (2, 40, 12304), (3, 24, 4112)]
+               (1, 16, 131072), (2, 40, 12304), (3, 24, 4112), (20, 12296, 4112), (31, 12352, 80)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)

@@ -739,8 +739,12 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_fewtok(
   const int n0 = blockIdx.x * 16 * CG;
   const rsrc_t rw = make_rsrc(qb + (int64_t)n0 * K, (unsigned)min(16 * CG, N - n0) * (unsigned)K);
   const rsrc_t rx = make_rsrc(qa, (unsigned)M * (unsigned)K);
-  __shared__ v4i wl[NW][CG][16 * 16];  // a wave's 16 rows x 16 chunks per group
-  __shared__ v4i red[NW][CG * MT][64];
+  // a wave's 16 rows x 16 chunks per group during the K loop; the waves'
+  // partial sums afterwards, in the same LDS
+  constexpr int kWl = NW * CG * 256, kRed = NW * CG * MT * 64;
+  __shared__ v4i lbuf[kWl > kRed ? kWl : kRed];
+  v4i(*wl)[CG][256] = (v4i(*)[CG][256])lbuf;
+  v4i(*red)[CG * MT][64] = (v4i(*)[CG * MT][64])lbuf;
   const int np = (K + 255) / 256;  // 256-byte pieces per row
   const int per = (np + NW - 1) / NW;
   const int p0 = wave * per, p1 = min(np, p0 + per);
@@ -791,6 +795,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_fewtok(
   }
 
   // exact sum of the waves' partials; fragment f is finished by wave f % NW
+  __syncthreads();  // every wave is done with its pieces in LDS
 #pragma unroll
   for (int c = 0; c < CG; ++c)
 #pragma unroll
@@ -839,17 +844,20 @@ void launch_fewtok_cfg(const int8_t* qa, const int8_t* qb, int M, int N, int K, 
 }
 
 // Shape choice, measured on the OPT-6.7B decode layers at 1-32 tokens: with
-// at least 384 blocks of 32 channels (N >= 12288) each wave takes two
-// channel groups, which halves the activation re-reads, and four waves split
-// K; with fewer channels one group per wave and eight waves per block, so
-// that about 2048 waves stream.
+// 12288 or more channels each wave takes several channel groups, which
+// share the activation fragments (up to 16 tokens two groups and four waves
+// splitting K; from 17 tokens, where the activations are two fragments per
+// step, four groups and eight waves); with fewer channels one group per wave
+// and eight waves per block, so that enough waves stream.
 template <int MT>
 hipError_t launch_fewtok(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N, int64_t K,
                          const float* sa, const float* sb, void* out, int mode, hipStream_t st) {
-  if (N >= 16 * 2 * 384)
-    launch_fewtok_cfg<MT, 4, 2>(qa, qb, (int)M, (int)N, (int)K, sa, sb, out, mode, st);
-  else
+  if (N < 12288)
     launch_fewtok_cfg<MT, 8, 1>(qa, qb, (int)M, (int)N, (int)K, sa, sb, out, mode, st);
+  else if constexpr (MT == 2)
+    launch_fewtok_cfg<MT, 8, 4>(qa, qb, (int)M, (int)N, (int)K, sa, sb, out, mode, st);
+  else
+    launch_fewtok_cfg<MT, 4, 2>(qa, qb, (int)M, (int)N, (int)K, sa, sb, out, mode, st);
   return hipGetLastError();
 }
 
