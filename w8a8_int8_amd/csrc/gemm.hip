@@ -28,7 +28,8 @@
 //
 // K pipeline: K advances BK = 128 bytes per stage (one full cache line per
 // operand row) through NST LDS slots (2 to 4, as many as 160 KB of LDS holds
-// for the tile; the 256 x 256 tile keeps a third slot for its weights).  Operand rows go from global memory straight into LDS with
+// for the tile; the single-shape 256 x 256 tile keeps a third slot for its
+// weights).  Operand rows go from global memory straight into LDS with
 // buffer loads in LDS mode (16 B per lane, each wave instruction fills 1 KiB
 // of LDS), NST - 1 or NST - 2 stages in flight while one is computed, and a
 // wave never holds global data in registers.  Which waves issue a stage's
@@ -42,8 +43,9 @@
 // FP8, 32 for fp16 / bf16) of (BM / WGM / MB) x (BN / WGN / MB) MFMAs.  The
 // fragment reads are software pipelined: the next k step's fragments are read
 // while the current step's MFMAs run (the larger operand in place, column by
-// column), and the next stage's first fragments are read (after the stage
-// barrier) while the last step's MFMAs run.  One
+// column; before a stage barrier the last column's fragment early, into
+// registers of its own), and the next stage's first fragments are read (after
+// the stage barrier) while the last step's MFMAs run.  One
 // barrier per stage; it is a plain s_barrier (no memory fence), with the
 // needed waits explicit: each wave waits for its own LDS-mode loads of the
 // next stage (vmcnt) and for its own LDS reads of the slot that is about to
@@ -59,9 +61,10 @@
 // Edges: the buffer resource of each operand tile ends at its last valid row,
 // and every row offset is part of the range-checked vector offset, so rows
 // past M or N load as zero without a memory access; chunks past K use an
-// out-of-range offset and load as zero too.  Blocks are dispatched round-robin over the 8 XCDs;
-// tile indices are remapped so each XCD (own L2) gets a contiguous run of
-// tiles, ordered token-tile fastest in groups of 8 token tiles.
+// out-of-range offset and load as zero too.  Blocks are dispatched
+// round-robin over the 8 XCDs; tile indices are remapped so each XCD (own L2)
+// gets a contiguous run of tiles, ordered token-tile fastest in groups of 8
+// token tiles.
 //
 // The same pipeline serves the dense fp16 / bf16 product (the comparison
 // baseline) and the FP8 E4M3 variant; few-token shapes go to k_gemv_rows (one
