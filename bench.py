@@ -7,7 +7,8 @@ of the Llama-2-7B-shaped decoder block (prefill, M = 2048 tokens):
   2. max|W_j| over the weight, smoothing factors s and 1/s (1 and these in one
      launch, w8a8_calibrate_smooth), fold s into W and quantize it per output
      channel
-  3. smooth X (X / s) and quantize it per token
+  3. smooth X (X / s) and quantize it per token (2's fold + quantize and this
+     in one launch, w8a8_scale_quant_pair)
   4.+5. INT8 GEMM with the fused dequant epilogue -> fp16 Y
 All inputs are resident in HBM before the timed region.
 
@@ -205,13 +206,12 @@ class Layer:
     def step(self, i, ev=None):
         """One pass of the path for this layer: calibration batch i folded into
         the running max|X_j|, max|W_j| and the smoothing factors (one launch),
-        the weight folded and quantized, the activations smoothed and
-        quantized, and the INT8 GEMM with its dequant epilogue."""
+        the weight folded and quantized and the activations smoothed and
+        quantized (one launch), and the INT8 GEMM with its dequant epilogue."""
         w8 = self.w8
         w8.calibrate_smooth(self.cal[i % len(self.cal)], self.w, self.alpha, self.amax_x,
                             self.amax_w, self.s, self.inv_s, self.scratch)
-        w8.scale_quant_rows(self.w, self.s, self.qw, self.sw)
-        w8.scale_quant_rows(self.x, self.inv_s, self.qx, self.sx)
+        w8.scale_quant_pair(self.w, self.s, self.x, self.inv_s, self.qw, self.sw, self.qx, self.sx)
         if ev is not None:
             ev[0].record()
         w8.gemm_dequant(self.qx, self.sx, self.qw, self.sw, self.x.dtype, self.y)
@@ -282,6 +282,10 @@ def kernel_breakdown(layers, reps, lean=False):
         d["fold_quant_weight"] = hbm(t, L.w.numel() * 3 + 4 * (L.N + L.K))
         t = timed(lambda i: w8.scale_quant_rows(xs[i % nx], L.inv_s, L.qx, L.sx), reps)
         d["smooth_quant_act"] = hbm(t, L.x.numel() * 3 + 4 * (L.M + L.K))
+        # the step's form: both in one launch
+        t = timed(lambda i: w8.scale_quant_pair(ws[i % nw], L.s, xs[i % nx], L.inv_s, L.qw, L.sw,
+                                                L.qx, L.sx), reps)
+        d["quant_pair"] = hbm(t, (L.w.numel() + L.x.numel()) * 3 + 4 * (L.N + L.M + 2 * L.K))
         t = timed(lambda i: w8.gemm_dequant(L.qx, L.sx, L.qw, L.sw, L.x.dtype, L.y), reps)
         ops = L.gemm_ops()
         d["gemm_dequant"] = dict(us=t * 1e6, TOPS=ops / t / 1e12, frac_mfma=ops / t / 1e12 / PEAK_INT8_TOPS)

@@ -13,6 +13,7 @@
  *      fold s into W and quantize W per output channel w8a8_channel_amax (on W)
  *                                                       + w8a8_scale_quant_rows
  *   3. X diag(s)^-1 and per-token INT8 quantization    w8a8_scale_quant_rows
+ *      2 (weight fold + quant) and 3 in one launch      w8a8_scale_quant_pair
  *      ... folded into the RMS norm that produces X     w8a8_fold_norm_weight (offline)
  *                                                       + w8a8_rmsnorm_quant_rows
  *      ... or into a LayerNorm (fp16)                   w8a8_layernorm_quant_rows
@@ -56,7 +57,7 @@
 extern "C" {
 #endif
 
-#define W8A8_ABI_VERSION 5
+#define W8A8_ABI_VERSION 6
 
 /* Largest K for which 127 * 127 * K fits int32, so that every accumulator
  * (and every partial sum) of the INT8 product is exact in int32. */
@@ -171,6 +172,28 @@ w8a8_status_t w8a8_calibrate_smooth(const void* x_cal, int64_t cal_rows, const v
  */
 w8a8_status_t w8a8_scale_quant_rows(const void* x, int dtype, int64_t rows, int64_t cols,
                                     const float* col_scale, int8_t* q, float* row_scale,
+                                    hipStream_t stream);
+
+/*
+ * Steps 2 (weights) and 3 (activations) of one layer in a single launch, as
+ * soon as the layer's s and inv_s exist.  Page section "平滑化変換の数学": the
+ * smoothed product is (X s^-1)(s W), so with K input channels
+ *   (qw, sw) = w8a8_scale_quant_rows(w [N x K], col_scale = s)
+ *   (qx, sx) = w8a8_scale_quant_rows(x [M x K], col_scale = inv_s)
+ * with every output bit identical to those two calls.  One grid covers the
+ * rows of both matrices (a block takes rows of one of them only), which saves
+ * one launch's ramp and tail.
+ *
+ *   w, qw, sw  [N x K] fp16/bf16 input, [N x K] int8 codes, [N] fp32 scales.
+ *   x, qx, sx  [M x K] input of the same dtype, [M x K] codes, [M] scales.
+ *   s, inv_s   [K] fp32 column scales.
+ *   Alignment, cols (= K) and row limits as in w8a8_scale_quant_rows, and
+ *   M + N < 2^31.  The two matrices' outputs must not overlap.
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, HIP (the checks of both matrices).
+ */
+w8a8_status_t w8a8_scale_quant_pair(const void* w, int64_t N, const float* s, int8_t* qw,
+                                    float* sw, const void* x, int64_t M, const float* inv_s,
+                                    int8_t* qx, float* sx, int dtype, int64_t K,
                                     hipStream_t stream);
 
 /*

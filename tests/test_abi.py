@@ -36,11 +36,11 @@ def declared_symbols():
 def test_library_loads_and_exports_header_symbols():
     lib = _lib.load()
     syms = declared_symbols()
-    assert len(syms) == 18
+    assert len(syms) == 19
     for s in syms:
         assert hasattr(lib, s), s
         assert s in _lib.PROTOTYPES, s
-    assert lib.w8a8_abi_version() == 5
+    assert lib.w8a8_abi_version() == 6
 
 
 def declared_prototypes():
@@ -151,6 +151,26 @@ def test_scale_quant_rows_rejects():
     assert f(P, 0, 4, 16, PODD, P, P, 0) == EALIGN
     assert f(P, 0, 4, 16, P, PODD, P, 0) == EALIGN
     assert f(P, 0, 4, 16, P, P, P + 2, 0) == EALIGN
+
+
+@cpu_only
+def test_scale_quant_pair_rejects():
+    """Each matrix is checked as w8a8_scale_quant_rows checks it, before any launch."""
+    f = _lib.load().w8a8_scale_quant_pair
+    # w, N, s, qw, sw, x, M, inv_s, qx, sx, dtype, K, stream
+    assert f(0, 4, P, P, P, P, 4, P, P, P, 0, 16, 0) == ENULL
+    assert f(P, 4, P, P, P, P, 4, P, P, 0, 0, 16, 0) == ENULL
+    assert f(0, 0, P, 0, 0, 0, 0, P, 0, 0, 0, 16, 0) == OK  # no rows: no launch
+    assert f(P, 4, P, P, P, P, 4, P, P, P, 2, 16, 0) == EDTYPE
+    assert f(P, -4, P, P, P, P, 4, P, P, P, 0, 16, 0) == ESHAPE
+    assert f(P, 4, P, P, P, P, -4, P, P, P, 0, 16, 0) == ESHAPE
+    assert f(P, 4, P, P, P, P, 4, P, P, P, 0, 24, 0) == ESHAPE  # K % 16
+    assert f(P, 4, P, P, P, P, 4, P, P, P, 0, 65536 + 16, 0) == ESHAPE
+    assert f(P, 1 << 30, P, P, P, P, 1 << 30, P, P, P, 0, 16, 0) == ESHAPE  # M + N
+    assert f(PODD, 4, P, P, P, P, 4, P, P, P, 0, 16, 0) == EALIGN
+    assert f(P, 4, P, P, P, PODD, 4, P, P, P, 0, 16, 0) == EALIGN
+    assert f(P, 4, P, P, P, P, 4, PODD, P, P, 0, 16, 0) == EALIGN
+    assert f(P, 4, P, P, P, P, 4, P, P, P + 2, 0, 16, 0) == EALIGN
 
 
 @cpu_only

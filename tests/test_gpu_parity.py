@@ -153,6 +153,29 @@ def test_scale_quant_rows(dtype, rows, cols):
     assert not (host(q) == -128).any()
 
 
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("N,M,K", [(8, 1, 16), (136, 37, 80), (4096, 2048, 4096), (1027, 3, 9008),
+                                   (5, 4100, 11008), (0, 9, 512), (9, 0, 512), (3, 2, 65536),
+                                   (0, 0, 64)])
+def test_scale_quant_pair(dtype, N, M, K):
+    """Weight (col_scale s) and activations (col_scale inv_s) in one launch:
+    each matrix's codes and scales equal the oracle's, bit for bit."""
+    w = rand_act(N, K, dtype, seed=N + 5 * K)
+    x = rand_act(M, K, dtype, seed=M + 7 * K + 1)
+    if N > 2:
+        w[1] = 0
+    if M > 2:
+        x[2] = 0
+    g = torch.Generator(device="cpu").manual_seed(K + 11)
+    s = torch.exp(torch.rand(K, generator=g) * 8 - 4).to(DEV)
+    inv_s = torch.exp(torch.rand(K, generator=g) * 8 - 4).to(DEV)
+    qw, sw, qx, sx = w8.scale_quant_pair(w, s, x, inv_s)
+    for q, d, a, c in ((qw, sw, w, s), (qx, sx, x, inv_s)):
+        q_or, d_or = oracle.scale_quant_rows(np_bits(a), dt_name(a), host(c))
+        assert np.array_equal(host(q), q_or)
+        assert np.array_equal(host(d).view(np.uint32), d_or.view(np.uint32))
+
+
 # ---------------------------------------------------------------- step 4
 
 
@@ -359,7 +382,8 @@ def _workload_cases():
 @pytest.mark.parametrize("name,li,alpha", _workload_cases())
 def test_workload_layer(name, li, alpha):
     """Full-size layer through the calls the benchmark times, against the oracle:
-    amax, s, inv_s, qW, sw, qX and sx in full; C of sampled token rows against
+    amax, s, inv_s, qW, sw, qX and sx in full (from the separate calls and from
+    the one-launch pair); C of sampled token rows against
     the oracle's product, all of C by the Freivalds check, then every element
     of the runtime forward's Y against the oracle's dequant of that C."""
     wl = synth.WORKLOADS[name]
@@ -373,6 +397,9 @@ def test_workload_layer(name, li, alpha):
 
     amax_x = w8.channel_amax(xc)
     p = w8.prepare_weight(w, amax_x, alpha)
+    # the benchmark step's form of the two quantizations: one launch
+    M0 = wl.M[0]
+    pair = w8.scale_quant_pair(w, p["s"], x_all[:M0].contiguous(), p["inv_s"])
     torch.cuda.synchronize()
 
     ax_or = oracle.channel_amax(np_bits(xc), dname)
@@ -387,6 +414,8 @@ def test_workload_layer(name, li, alpha):
     del w_np
     assert np.array_equal(host(p["qw"]), qw_or)
     assert np.array_equal(host(p["sw"]).view(np.uint32), sw_or.view(np.uint32))
+    assert np.array_equal(host(pair[0]), qw_or)
+    assert np.array_equal(host(pair[1]).view(np.uint32), sw_or.view(np.uint32))
 
     ys = {}
     for M in wl.M:
@@ -399,6 +428,9 @@ def test_workload_layer(name, li, alpha):
         qx_or, sx_or = oracle.scale_quant_rows(np_bits(x), dname, inv_or)
         assert np.array_equal(host(qx), qx_or)
         assert np.array_equal(host(sx).view(np.uint32), sx_or.view(np.uint32))
+        if M == M0:
+            assert np.array_equal(host(pair[2]), qx_or)
+            assert np.array_equal(host(pair[3]).view(np.uint32), sx_or.view(np.uint32))
         rows = _sample_rows(M, seed=M + li)
         c_or = oracle.gemm_i32(qx_or[rows], qw_or)
         y_or = oracle.dequant(c_or, sx_or[rows], sw_or, dname)

@@ -7,11 +7,12 @@ from .api import (calibrate_smooth, calibrate_smooth_scratch, channel_amax, fold
                   fold_norm_weight, gemm_dequant, gemm_dequant_e4m3, gemm_float, gemm_i32,
                   layernorm_quant_rows, linear, linear_noalloc, linear_workspace_bytes,
                   prepare_weight,
-                  rmsnorm_quant_rows, scale_quant_rows, scale_quant_rows_e4m3, smooth_factors)
+                  rmsnorm_quant_rows, scale_quant_pair, scale_quant_rows, scale_quant_rows_e4m3,
+                  smooth_factors)
 
 __all__ = [
-    "channel_amax", "smooth_factors", "scale_quant_rows", "gemm_i32", "gemm_dequant",
-    "gemm_float", "linear", "linear_noalloc", "linear_workspace_bytes", "prepare_weight",
+    "channel_amax", "smooth_factors", "scale_quant_rows", "scale_quant_pair", "gemm_i32",
+    "gemm_dequant", "gemm_float", "linear", "linear_noalloc", "linear_workspace_bytes", "prepare_weight",
     "scale_quant_rows_e4m3", "gemm_dequant_e4m3", "fold_norm_weight", "rmsnorm_quant_rows",
     "fold_layernorm", "layernorm_quant_rows", "calibrate_smooth", "calibrate_smooth_scratch",
 ]

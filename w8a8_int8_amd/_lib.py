@@ -22,6 +22,8 @@ PROTOTYPES = {
     "w8a8_calibrate_smooth": (c_int, [c_vp, c_i64, c_vp, c_i64, c_int, c_i64, ctypes.c_double,
                                       c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
     "w8a8_scale_quant_rows": (c_int, [c_vp, c_int, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp]),
+    "w8a8_scale_quant_pair": (c_int, [c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp,
+                                      c_int, c_i64, c_vp]),
     "w8a8_fold_norm_weight": (c_int, [c_vp, c_vp, c_i64, c_vp, c_vp]),
     "w8a8_rmsnorm_quant_rows": (c_int, [c_vp, c_int, c_i64, c_i64, c_vp, ctypes.c_float, c_vp, c_vp,
                                         c_vp]),
@@ -39,7 +41,7 @@ PROTOTYPES = {
     "w8a8_linear_noalloc": (c_int, [c_vp, c_int, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_vp]),
 }
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 W8A8_F16, W8A8_BF16 = 0, 1
 
 _lib = None

@@ -142,6 +142,34 @@ def scale_quant_rows(x: torch.Tensor, col_scale: torch.Tensor,
     return q, row_scale
 
 
+def scale_quant_pair(w: torch.Tensor, s: torch.Tensor, x: torch.Tensor, inv_s: torch.Tensor,
+                     qw: Optional[torch.Tensor] = None, sw: Optional[torch.Tensor] = None,
+                     qx: Optional[torch.Tensor] = None, sx: Optional[torch.Tensor] = None):
+    """(qw, sw, qx, sx): scale_quant_rows(w, s) and scale_quant_rows(x, inv_s) in one launch."""
+    _dev(w, s, x, inv_s)
+    N, K = w.shape
+    M = x.shape[0]
+    if x.dtype != w.dtype:
+        raise TypeError(f"w is {w.dtype} but x is {x.dtype}")
+    _need(x, w.dtype, (M, K))
+    _need(s, torch.float32, (K,))
+    _need(inv_s, torch.float32, (K,))
+    qw = torch.empty((N, K), dtype=torch.int8, device=w.device) if qw is None else qw
+    sw = torch.empty(N, dtype=torch.float32, device=w.device) if sw is None else sw
+    qx = torch.empty((M, K), dtype=torch.int8, device=w.device) if qx is None else qx
+    sx = torch.empty(M, dtype=torch.float32, device=w.device) if sx is None else sx
+    _dev(qw, sw, qx, sx)
+    _need(qw, torch.int8, (N, K))
+    _need(sw, torch.float32, (N,))
+    _need(qx, torch.int8, (M, K))
+    _need(sx, torch.float32, (M,))
+    lib = _lib.load()
+    _lib.check("w8a8_scale_quant_pair", lib.w8a8_scale_quant_pair(
+        _ptr(w), N, _ptr(s), _ptr(qw), _ptr(sw), _ptr(x), M, _ptr(inv_s), _ptr(qx), _ptr(sx),
+        _dtype_code(w), K, _stream()))
+    return qw, sw, qx, sx
+
+
 def fold_norm_weight(gamma: torch.Tensor, inv_s: torch.Tensor,
                      g: Optional[torch.Tensor] = None) -> torch.Tensor:
     """g = gamma * inv_s (fp32): the smoothing folded into an RMS norm's weight."""

@@ -161,6 +161,18 @@ w8a8_status_t w8a8_scale_quant_rows(const void* x, int dtype, int64_t rows, int6
                                                   false, 0.0f, q, row_scale, 0, stream));
 }
 
+w8a8_status_t w8a8_scale_quant_pair(const void* w, int64_t N, const float* s, int8_t* qw,
+                                    float* sw, const void* x, int64_t M, const float* inv_s,
+                                    int8_t* qx, float* sx, int dtype, int64_t K,
+                                    hipStream_t stream) {
+  w8a8_status_t st = check_quant(w, dtype, N, K, s, qw, sw);
+  if (st == W8A8_OK) st = check_quant(x, dtype, M, K, inv_s, qx, sx);
+  if (st != W8A8_OK) return st;
+  if (M + N >= kMaxRows) return W8A8_ERR_SHAPE;
+  return hip_status(w8a8::launch_scale_quant_pair(w, N, s, qw, sw, x, M, inv_s, qx, sx,
+                                                  dtype == W8A8_BF16, K, stream));
+}
+
 w8a8_status_t w8a8_scale_quant_rows_e4m3(const void* x, int dtype, int64_t rows, int64_t cols,
                                          const float* col_scale, uint8_t* q, float* row_scale,
                                          hipStream_t stream) {

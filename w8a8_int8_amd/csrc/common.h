@@ -31,6 +31,11 @@ hipError_t launch_calibrate_smooth(const void* xc, int64_t cal_rows, const void*
 hipError_t launch_scale_quant_rows(const void* x, bool bf16, int64_t rows, int64_t cols,
                                    const float* col_scale, bool norm, float eps, void* q,
                                    float* row_scale, int fmt, hipStream_t st);
+// The weight (n rows, col_scale s) and the activations (m rows, col_scale
+// inv_s) of one layer, both with k columns, quantized to INT8 in one launch.
+hipError_t launch_scale_quant_pair(const void* w, int64_t n, const float* s, void* qw, float* sw,
+                                   const void* x, int64_t m, const float* inv_s, void* qx,
+                                   float* sx, bool bf16, int64_t k, hipStream_t st);
 hipError_t launch_fold(const float* a, const float* b, int64_t n, float* out, hipStream_t st);
 // LayerNorm fold (fp16 rows): per-token INT8 of LayerNorm(x; gamma, beta) * inv_s
 // given g = RN32(gamma * inv_s) and b = RN32(beta * inv_s).

@@ -95,17 +95,32 @@ __device__ __forceinline__ float wave_sum(float v) {
 // per-token quantizer does not change under a positive factor common to the
 // row, so the norm's factor only enters the scale; the codes are those of
 // x * g.
+// One matrix of the launch: rows of cols8 16-byte chunks, its column scales,
+// codes and row scales.
+struct RowSet {
+  const v4u* x;
+  int64_t rows;
+  const float4* col_scale;
+  uint2* q;
+  float* row_scale;
+};
+
+// Blocks [0, b_first) take the rows of set a, blocks from b_first on those of
+// set b (both with cols8 chunks per row): two matrices with the same row
+// length, such as a layer's weight and its activations, quantize in one launch.
 template <int CPT, int R, bool BF16, int FMT, bool NORM>
-__global__ __launch_bounds__(1024) void k_scale_quant_rows(const v4u* __restrict__ x, int64_t rows,
-                                                           int cols8,
-                                                           const float4* __restrict__ col_scale,
-                                                           float eps,
-                                                           uint2* __restrict__ q,
-                                                           float* __restrict__ row_scale) {
+__global__ __launch_bounds__(1024) void k_scale_quant_rows(RowSet a, RowSet b, unsigned b_first,
+                                                           int cols8, float eps) {
+  const bool in_b = blockIdx.x >= b_first;
+  const v4u* __restrict__ x = in_b ? b.x : a.x;
+  const int64_t rows = in_b ? b.rows : a.rows;
+  const float4* __restrict__ col_scale = in_b ? b.col_scale : a.col_scale;
+  uint2* __restrict__ q = in_b ? b.q : a.q;
+  float* __restrict__ row_scale = in_b ? b.row_scale : a.row_scale;
   const int tid = threadIdx.x;
   const int G = blockDim.x;
   const int lane = tid % kWave, wave = tid / kWave, nwaves = G / kWave;
-  const int64_t row0 = (int64_t)blockIdx.x * R;
+  const int64_t row0 = (int64_t)(in_b ? blockIdx.x - b_first : blockIdx.x) * R;
 
   // all of this block's input loads first
   v4u xv[R][CPT];
@@ -218,37 +233,37 @@ __global__ __launch_bounds__(1024) void k_scale_quant_rows(const v4u* __restrict
   }
 }
 
+RowSet row_set(const void* x, int64_t rows, const float* cs, void* q, float* row_scale) {
+  return RowSet{(const v4u*)x, rows, (const float4*)cs, (uint2*)q, row_scale};
+}
+
 template <int CPT, int R, bool BF16, int FMT, bool NORM>
-void launch_one(const void* x, int64_t rows, int cols8, int G, const float* cs, float eps, void* q,
-                float* row_scale, hipStream_t st) {
-  const unsigned blocks = (unsigned)((rows + R - 1) / R);
+void launch_one(const RowSet& a, const RowSet& b, int cols8, int G, float eps, hipStream_t st) {
+  const unsigned blocks_a = (unsigned)((a.rows + R - 1) / R);
+  const unsigned blocks = blocks_a + (unsigned)((b.rows + R - 1) / R);
   hipLaunchKernelGGL((k_scale_quant_rows<CPT, R, BF16, FMT, NORM>), dim3(blocks), dim3(G), 0, st,
-                     (const v4u*)x, rows, cols8, (const float4*)cs, eps, (uint2*)q, row_scale);
+                     a, b, blocks_a, cols8, eps);
 }
 
 template <int CPT, int R>
-hipError_t launch_cfg(const void* x, bool bf16, int fmt, int64_t rows, int cols8, int G,
-                      const float* cs, bool norm, float eps, void* q, float* row_scale,
-                      hipStream_t st) {
+hipError_t launch_cfg(const RowSet& a, const RowSet& b, bool bf16, int fmt, int cols8, int G,
+                      bool norm, float eps, hipStream_t st) {
   if (norm) {  // RMS norm fold (INT8 only)
-    if (bf16) launch_one<CPT, R, true, 0, true>(x, rows, cols8, G, cs, eps, q, row_scale, st);
-    else launch_one<CPT, R, false, 0, true>(x, rows, cols8, G, cs, eps, q, row_scale, st);
+    if (bf16) launch_one<CPT, R, true, 0, true>(a, b, cols8, G, eps, st);
+    else launch_one<CPT, R, false, 0, true>(a, b, cols8, G, eps, st);
   } else if (fmt == 0) {
-    if (bf16) launch_one<CPT, R, true, 0, false>(x, rows, cols8, G, cs, eps, q, row_scale, st);
-    else launch_one<CPT, R, false, 0, false>(x, rows, cols8, G, cs, eps, q, row_scale, st);
+    if (bf16) launch_one<CPT, R, true, 0, false>(a, b, cols8, G, eps, st);
+    else launch_one<CPT, R, false, 0, false>(a, b, cols8, G, eps, st);
   } else {
-    if (bf16) launch_one<CPT, R, true, 1, false>(x, rows, cols8, G, cs, eps, q, row_scale, st);
-    else launch_one<CPT, R, false, 1, false>(x, rows, cols8, G, cs, eps, q, row_scale, st);
+    if (bf16) launch_one<CPT, R, true, 1, false>(a, b, cols8, G, eps, st);
+    else launch_one<CPT, R, false, 1, false>(a, b, cols8, G, eps, st);
   }
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_scale_quant_rows(const void* x, bool bf16, int64_t rows, int64_t cols,
-                                   const float* col_scale, bool norm, float eps, void* q,
-                                   float* row_scale, int fmt, hipStream_t st) {
-  if (rows == 0) return hipSuccess;
+hipError_t launch_sets(const RowSet& a, const RowSet& b, bool bf16, int64_t cols, bool norm,
+                       float eps, int fmt, hipStream_t st) {
+  if (a.rows + b.rows == 0) return hipSuccess;
   const int cols8 = (int)(cols / 8);
   // Threads per row: two 16-byte chunks each (more for rows past 2048 chunks,
   // where the block size reaches 1024), a whole number of waves.  Rows per
@@ -263,27 +278,36 @@ hipError_t launch_scale_quant_rows(const void* x, bool bf16, int64_t rows, int64
   if (G > 1024) G = 1024;
   const int cpt = (cols8 + G - 1) / G;
   switch (cpt <= 1 ? 1 : cpt) {
-    case 1: return launch_cfg<1, 4>(x, bf16, fmt, rows, cols8, G, col_scale, norm, eps, q,
-                                          row_scale, st);
+    case 1: return launch_cfg<1, 4>(a, b, bf16, fmt, cols8, G, norm, eps, st);
     case 2:
       if (cols8 > 1024 && cols8 <= 1536)
-        return launch_cfg<2, 4>(x, bf16, fmt, rows, cols8, G, col_scale, norm, eps, q, row_scale,
-                                st);
-      return launch_cfg<2, 2>(x, bf16, fmt, rows, cols8, G, col_scale, norm, eps, q, row_scale, st);
-    case 3: return launch_cfg<3, 1>(x, bf16, fmt, rows, cols8, G, col_scale, norm, eps, q,
-                                          row_scale, st);
-    case 4: return launch_cfg<4, 1>(x, bf16, fmt, rows, cols8, G, col_scale, norm, eps, q,
-                                          row_scale, st);
-    case 5: return launch_cfg<5, 1>(x, bf16, fmt, rows, cols8, G, col_scale, norm, eps, q,
-                                          row_scale, st);
-    case 6: return launch_cfg<6, 1>(x, bf16, fmt, rows, cols8, G, col_scale, norm, eps, q,
-                                          row_scale, st);
-    case 7: return launch_cfg<7, 1>(x, bf16, fmt, rows, cols8, G, col_scale, norm, eps, q,
-                                          row_scale, st);
-    case 8: return launch_cfg<8, 1>(x, bf16, fmt, rows, cols8, G, col_scale, norm, eps, q,
-                                          row_scale, st);
+        return launch_cfg<2, 4>(a, b, bf16, fmt, cols8, G, norm, eps, st);
+      return launch_cfg<2, 2>(a, b, bf16, fmt, cols8, G, norm, eps, st);
+    case 3: return launch_cfg<3, 1>(a, b, bf16, fmt, cols8, G, norm, eps, st);
+    case 4: return launch_cfg<4, 1>(a, b, bf16, fmt, cols8, G, norm, eps, st);
+    case 5: return launch_cfg<5, 1>(a, b, bf16, fmt, cols8, G, norm, eps, st);
+    case 6: return launch_cfg<6, 1>(a, b, bf16, fmt, cols8, G, norm, eps, st);
+    case 7: return launch_cfg<7, 1>(a, b, bf16, fmt, cols8, G, norm, eps, st);
+    case 8: return launch_cfg<8, 1>(a, b, bf16, fmt, cols8, G, norm, eps, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+}  // namespace
+
+hipError_t launch_scale_quant_rows(const void* x, bool bf16, int64_t rows, int64_t cols,
+                                   const float* col_scale, bool norm, float eps, void* q,
+                                   float* row_scale, int fmt, hipStream_t st) {
+  const RowSet a = row_set(x, rows, col_scale, q, row_scale);
+  return launch_sets(a, row_set(nullptr, 0, nullptr, nullptr, nullptr), bf16, cols, norm, eps, fmt,
+                     st);
+}
+
+hipError_t launch_scale_quant_pair(const void* w, int64_t n, const float* s, void* qw, float* sw,
+                                   const void* x, int64_t m, const float* inv_s, void* qx,
+                                   float* sx, bool bf16, int64_t k, hipStream_t st) {
+  return launch_sets(row_set(w, n, s, qw, sw), row_set(x, m, inv_s, qx, sx), bf16, k, false, 0.0f,
+                     0, st);
 }
 
 // LayerNorm fold (fp16 rows), one row per block.  The smoothing's inv_s is
