@@ -96,18 +96,26 @@ def test_workspace_bytes():
     assert lib.w8a8_linear_workspace_bytes(1, 8, 16) == 256 + 256  # one split: no partials
     assert lib.w8a8_linear_workspace_bytes(2048, 4096, 4096) == 2048 * 4096 + 2048 * 4
     assert lib.w8a8_linear_workspace_bytes(-1, 8, 16) == 0
-    # 17-32 tokens split K only below 2048 output channels: 1024 outputs are 16
-    # blocks of 64 channels, and K = 16384 (256 steps of 64) splits eight ways
-    # (at least 32 steps per split); K = 4096 two ways
-    assert lib.w8a8_linear_workspace_bytes(32, 1024, 16384) == 32 * 16384 + 256 + 8 * 32 * 1024 * 4
-    assert lib.w8a8_linear_workspace_bytes(32, 1024, 4096) == 32 * 4096 + 256 + 2 * 32 * 1024 * 4
+    # 17-32 tokens split K below 12288 output channels when rows have 32 or more
+    # 256-byte pieces (or below 2048 channels): blocks of 64 channels, about
+    # 256 blocks, at least 8 pieces per split, at most 16 splits.  The
+    # workspace adds the int32 slices (splits x M x N) and one 4-byte counter
+    # per 64-channel group, each rounded up to 256 bytes.
+    # 1024 channels: 16 groups; K = 16384 is 64 pieces: 8 splits; K = 4096: 2
+    assert lib.w8a8_linear_workspace_bytes(32, 1024, 16384) == 32 * 16384 + 256 + 8 * 32 * 1024 * 4 + 256
+    assert lib.w8a8_linear_workspace_bytes(32, 1024, 4096) == 32 * 4096 + 256 + 2 * 32 * 1024 * 4 + 256
+    assert lib.w8a8_linear_workspace_bytes(24, 1024, 16384) == 24 * 16384 + 256 + 8 * 24 * 1024 * 4 + 256
     # (slices rounded up to 256 bytes)
-    assert lib.w8a8_linear_workspace_bytes(17, 2040, 4096) == 17 * 4096 + 256 + (2 * 17 * 2040 * 4 + 64)
-    # from 2048 channels the unsplit few-token kernel: no partial slices
-    assert lib.w8a8_linear_workspace_bytes(32, 2048, 16384) == 32 * 16384 + 256
-    assert lib.w8a8_linear_workspace_bytes(32, 4096, 16384) == 32 * 16384 + 256
+    assert lib.w8a8_linear_workspace_bytes(17, 2040, 4096) == 17 * 4096 + 256 + (2 * 17 * 2040 * 4 + 64) + 256
+    # 4096 channels: 64 groups, 4 splits; 2048: 32 groups, 8 splits
+    assert lib.w8a8_linear_workspace_bytes(32, 4096, 16384) == 32 * 16384 + 256 + 4 * 32 * 4096 * 4 + 256
+    assert lib.w8a8_linear_workspace_bytes(32, 2048, 16384) == 32 * 16384 + 256 + 8 * 32 * 2048 * 4 + 256
+    # unsplit: rows of 16 pieces from 2048 channels, 12288 channels or more,
+    # 16 tokens or fewer
+    assert lib.w8a8_linear_workspace_bytes(32, 4096, 4096) == 32 * 4096 + 256
     assert lib.w8a8_linear_workspace_bytes(32, 16384, 4096) == 32 * 4096 + 256
-    assert lib.w8a8_linear_workspace_bytes(16, 1024, 16384) == 16 * 16384 + 256  # below 17 tokens
+    assert lib.w8a8_linear_workspace_bytes(32, 12288, 16384) == 32 * 16384 + 256
+    assert lib.w8a8_linear_workspace_bytes(16, 1024, 16384) == 16 * 16384 + 256
 
 
 @cpu_only

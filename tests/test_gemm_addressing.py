@@ -100,20 +100,22 @@ def test_the_scalar_offset_is_not_a_row_offset():
                                      row_offset_in_scalar=True), M, N, K)
 
 
-def fewtok_loads(M, N, K, n0, MT, NW, CG):
+def fewtok_loads(M, N, K, n0, MT, NW, CG, S=1, sp=0):
     """Loads of one block of the 3-32 token kernel: 16 CG weight rows in
-    256-byte pieces (wave w takes a contiguous range of the pieces), and the
-    activation fragments of the same k range for MT token slots."""
+    256-byte pieces (wave w takes a contiguous range of the block's pieces:
+    all of them, or those of split sp of S), and the activation fragments of
+    the same k range for MT token slots."""
     lane = np.arange(64)
     lr, lc = lane // 16, lane % 16
     r16, kq = lane % 16, lane // 16
     npc = -(-K // 256)
-    per = -(-npc // NW)
+    q0, q1 = npc * sp // S, npc * (sp + 1) // S
+    per = -(-(q1 - q0) // NW)
     recs_w = min(16 * CG, N - n0) * K
     recs_x = M * K
     out = []
     for w in range(NW):
-        for p in range(w * per, min(npc, (w + 1) * per)):
+        for p in range(q0 + w * per, min(q1, q0 + (w + 1) * per)):
             kb = 256 * p
             for c in range(CG):
                 for i in range(4):
@@ -134,6 +136,62 @@ def test_few_token_kernel_loads_stay_in_bounds(M, N, K):
     NW, CG = (8, 1) if N < 12288 else (8, 4) if MT == 2 else (4, 2)
     for n0 in sorted({0, (N - 1) // (16 * CG) * (16 * CG)}):
         assert_in_bounds(fewtok_loads(M, N, K, n0, MT, NW, CG), M, N, K)
+
+
+def splitk_plan(M, N, K):
+    """(splits, groups) of the runtime forward's split-K form, or None."""
+    if M < 17 or M > 32 or N < 1 or N >= 12288 or K < 1:
+        return None
+    groups = -(-N // 64)
+    npc = -(-K // 256)
+    if npc < 32 and N >= 2048:
+        return None
+    s = min(-(-256 // groups), npc // 8, 16)
+    return (s, groups) if s >= 2 else None
+
+
+def splitk_slice_offsets(M, N, S, sp, n0, MT, CG=4):
+    """Byte offsets of the partial-slice stores of block (n0, sp) and of the
+    loads the last block of the group makes from the other slices: one
+    16-byte access per lane and fragment, rows m < M and channels n < N."""
+    lane = np.arange(64)
+    out = []
+    for f in range(CG * MT):
+        m = (f % MT) * 16 + lane % 16
+        n = n0 + (f // MT) * 16 + 4 * (lane // 16)
+        live = (m < M) & (n < N)
+        for s2 in range(S):
+            out.append((((s2 * M + m) * N + n) * 4)[live])
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", [(32, 4096, 16384), (24, 1024, 16384), (17, 2040, 4096),
+                                   (31, 2056, 8208), (24, 264, 65536), (20, 8192, 8192)])
+def test_split_k_loads_and_slices_stay_in_bounds(M, N, K):
+    S, groups = splitk_plan(M, N, K)
+    MT = -(-M // 16)
+    assert S * M * N * 4 < 2 ** 31  # the slices' buffer resource has a 32-bit size
+    for n0 in sorted({0, (groups - 1) * 64}):
+        for sp in range(S):
+            assert_in_bounds(fewtok_loads(M, N, K, n0, MT, 8, 4, S, sp), M, N, K)
+            for off in splitk_slice_offsets(M, N, S, sp, n0, MT):
+                assert (off >= 0).all() and (off + 16 <= S * M * N * 4).all()
+                assert (off % 16 == 0).all()
+    # the splits' piece ranges cover every piece once
+    npc = -(-K // 256)
+    cover = sorted(p for sp in range(S) for p in range(npc * sp // S, npc * (sp + 1) // S))
+    assert cover == list(range(npc))
+
+
+def test_split_k_plan_shapes():
+    """Which shapes split (the rule the launcher and the workspace size share)."""
+    assert splitk_plan(32, 4096, 16384) == (4, 64)
+    assert splitk_plan(32, 8192, 8192) == (2, 128)
+    assert splitk_plan(17, 1024, 16384) == (8, 16)
+    assert splitk_plan(16, 1024, 16384) is None
+    assert splitk_plan(32, 4096, 4096) is None
+    assert splitk_plan(32, 12288, 16384) is None
+    assert splitk_plan(32, 520, 1040) is None  # 5 pieces per row
 
 
 def gemv_loads(M, N, K, n0, MT, R=4):

@@ -1,10 +1,10 @@
 """GPU parity of the runtime forward at few tokens (M <= 32): the
 row-streaming kernel up to 2 tokens, the few-token kernel (weight pieces
-transposed through LDS) up to 32, and from 17 to 32 on fewer than 2048
-channels the INT8 product split along K into
-int32 partial slices that a second kernel sums exactly.  Integer accumulation
-is order free, so the output must equal the oracle's bit for bit, and equal
-the unsplit gemm_dequant path's.
+transposed through LDS) up to 32, and from 17 to 32 tokens on layers under
+12288 channels with long rows its split-K form: int32 partial slices handed
+over in memory, summed exactly by the last block of each channel group.
+Integer accumulation is order free, so the output must equal the oracle's bit
+for bit, and equal the unsplit gemm_dequant path's.
 """
 from __future__ import annotations
 
@@ -48,9 +48,10 @@ def _make_layer(N, K, dtype, seed):
     return p
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 16, 17, 31, 32])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 15, 16, 17, 31, 32])
 @pytest.mark.parametrize("N,K", [(4096, 16384), (16384, 4096), (12288, 4096), (136, 80),
-                                 (520, 1040), (264, 65536), (8, 16), (4104, 4112)])
+                                 (520, 1040), (264, 65536), (8, 16), (4104, 4112),
+                                 (2056, 8208), (1024, 16384), (8192, 8192), (2040, 4096)])
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
 def test_linear_decode_split_k(dtype, N, K, M):
     p = layer(N, K, dtype, N + K)
@@ -75,10 +76,11 @@ def test_linear_decode_split_k(dtype, N, K, M):
     assert np.array_equal(synth.to_numpy_bits(y).view(np.uint16), y_or.view(np.uint16))
 
 
-def test_linear_decode_repeat_calls_bit_identical():
-    """The partial slices are overwritten on every call: a second call with
-    other activations, then the first again, reproduces the first output."""
-    N, K, M = 1024, 16384, 32
+@pytest.mark.parametrize("N,K,M", [(1024, 16384, 32), (4096, 16384, 24)])
+def test_linear_decode_repeat_calls_bit_identical(N, K, M):
+    """The partial slices are overwritten and the counters cleared on every
+    call: a second call with other activations, then the first again,
+    reproduces the first output."""
     p = layer(N, K, torch.float16, 3)
     g = torch.Generator(device="cpu").manual_seed(9)
     xa = torch.randn((M, K), generator=g).half().to(DEV)

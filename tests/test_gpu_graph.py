@@ -22,8 +22,8 @@ def fill(t: torch.Tensor, seed: int, scale: float = 1.0):
 
 
 # 8 and 24 tokens on 4096 or more channels: the few-token GEMM; 24 tokens on
-# 1024 channels: split-K with partial slices and the reduction kernel; 512
-# tokens: the tiled GEMM
+# 1024 channels: its split-K form (partial slices in the workspace, counters
+# cleared by the quantization launch); 512 tokens: the tiled GEMM
 @pytest.mark.parametrize("M,N", [(8, 12288), (24, 4096), (24, 1024), (512, 12288)])
 def test_path_replays_match_eager(M, N):
     K = 4096

@@ -48,9 +48,11 @@ def _bits(t):
 
 
 @pytest.mark.parametrize("shapes,dtype", [
-    # prefill, a split-K few-token call (S > 1 partial sums in the scratch: fewer than
-    # 2048 channels), an unsplit 32-token call, then one token
-    ([(2048, 4096, 4096), (32, 1024, 16384), (32, 4096, 8192), (1, 4104, 1024)], torch.float16),
+    # prefill, two split-K few-token calls (partial slices and counters in the
+    # scratch; the second with fewer splits and smaller slices), an unsplit
+    # 32-token call, then one token
+    ([(2048, 4096, 4096), (32, 4096, 16384), (24, 1024, 16384), (32, 4096, 4096), (1, 4104, 1024)],
+     torch.float16),
     # the largest Llama-2-7B activation (2048 x 11008), then 17-32 tokens on a narrow layer
     ([(2048, 4096, 11008), (20, 1536, 4096), (5, 520, 1040)], torch.bfloat16),
 ])

@@ -258,18 +258,20 @@ w8a8_status_t w8a8_gemm_float(const void* a, const void* b, void* y, int dtype, 
                                       nullptr, y, dtype == W8A8_BF16 ? 4 : 3, stream));
 }
 
-// 17 to 32 tokens take the split-K path, whose int32 partial slices follow
-// the INT8 activations and their scales in the workspace.
+// Shapes that take the split-K path (splitk_plan): its int32 partial slices
+// and the arrival counters of its channel groups follow the INT8 activations
+// and their scales in the workspace.
 static bool linear_splitk(int64_t M, int64_t N, int64_t K) {
-  return w8a8::splitk_plan(M, N, K).steps_per_split > 0;
+  return w8a8::splitk_plan(M, N, K).splits > 0;
 }
 
 size_t w8a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N < 0 || K < 0) return 0;
   size_t b = round_up((size_t)M * (size_t)K, kWsAlign) + round_up((size_t)M * 4, kWsAlign);
   if (linear_splitk(M, N, K)) {
-    const int s = w8a8::splitk_plan(M, N, K).splits;
-    if (s > 1) b += round_up((size_t)s * (size_t)M * (size_t)N * 4, kWsAlign);
+    const w8a8::SplitkPlan p = w8a8::splitk_plan(M, N, K);
+    b += round_up((size_t)p.splits * (size_t)M * (size_t)N * 4, kWsAlign);
+    b += round_up((size_t)p.groups * 4, kWsAlign);
   }
   return b;
 }
@@ -306,14 +308,20 @@ namespace {
 struct LinearWs {
   int8_t* qx;
   float* sx;
-  int32_t* part;
+  int32_t* part;      // split-K partial slices (splits x M x N)
+  unsigned* counters;  // split-K arrival counters (one per channel group)
 };
 
-LinearWs linear_ws(const void* workspace, int64_t M, int64_t K) {
+LinearWs linear_ws(const void* workspace, int64_t M, int64_t N, int64_t K) {
   char* base = (char*)workspace;
   const size_t off_sx = round_up((size_t)M * (size_t)K, kWsAlign);
-  return LinearWs{(int8_t*)base, (float*)(base + off_sx),
-                  (int32_t*)(base + off_sx + round_up((size_t)M * 4, kWsAlign))};
+  const size_t off_part = off_sx + round_up((size_t)M * 4, kWsAlign);
+  size_t off_cnt = off_part;
+  if (linear_splitk(M, N, K))
+    off_cnt += round_up((size_t)w8a8::splitk_plan(M, N, K).splits * (size_t)M * (size_t)N * 4,
+                        kWsAlign);
+  return LinearWs{(int8_t*)base, (float*)(base + off_sx), (int32_t*)(base + off_part),
+                  (unsigned*)(base + off_cnt)};
 }
 
 w8a8_status_t check_linear(const void* x, int dtype, const float* inv_s, const int8_t* qw,
@@ -324,7 +332,7 @@ w8a8_status_t check_linear(const void* x, int dtype, const float* inv_s, const i
   if (!workspace || (!sw && N)) return W8A8_ERR_NULL;
   if (!aligned(workspace, kWsAlign)) return W8A8_ERR_ALIGN;
   if (ws_bytes < w8a8_linear_workspace_bytes(M, N, K)) return W8A8_ERR_ARG;
-  const LinearWs ws = linear_ws(workspace, M, K);
+  const LinearWs ws = linear_ws(workspace, M, N, K);
   w8a8_status_t st = check_quant(x, dtype, M, K, inv_s, ws.qx, ws.sx);
   if (st != W8A8_OK) return st;
   st = check_gemm(ws.qx, qw, y, M, N, K);
@@ -336,14 +344,17 @@ w8a8_status_t check_linear(const void* x, int dtype, const float* inv_s, const i
 w8a8_status_t launch_linear(const void* x, int dtype, const float* inv_s, const int8_t* qw,
                             const float* sw, void* y, int64_t M, int64_t N, int64_t K,
                             void* workspace, hipStream_t stream) {
-  const LinearWs ws = linear_ws(workspace, M, K);
+  const LinearWs ws = linear_ws(workspace, M, N, K);
   const bool bf16 = dtype == W8A8_BF16;
+  const bool split = linear_splitk(M, N, K);
+  // the quantization launch also clears the split-K counters
+  const int ncnt = split ? w8a8::splitk_plan(M, N, K).groups : 0;
   hipError_t e = w8a8::launch_scale_quant_rows(x, bf16, M, K, inv_s, false, 0.0f, ws.qx, ws.sx, 0,
-                                               stream);
+                                               stream, ws.counters, ncnt);
   if (e != hipSuccess) return W8A8_ERR_HIP;
-  if (linear_splitk(M, N, K))
+  if (split)
     return hip_status(w8a8::launch_gemm_splitk(ws.qx, qw, M, N, K, ws.sx, sw, y, bf16, ws.part,
-                                               stream));
+                                               ws.counters, stream));
   return hip_status(w8a8::launch_gemm(ws.qx, qw, M, N, K, ws.sx, sw, y, bf16 ? 2 : 1, stream));
 }
 

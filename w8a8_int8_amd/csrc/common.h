@@ -27,10 +27,12 @@ hipError_t launch_calibrate_smooth(const void* xc, int64_t cal_rows, const void*
                                    void* scratch, hipStream_t st);
 // fmt: 0 = symmetric INT8 codes, 1 = FP8 E4M3 codes.  norm (INT8 only): the
 // rows are RMS-norm inputs and col_scale the folded norm weight; the row scale
-// is divided by the row's rms (with eps).
+// is divided by the row's rms (with eps).  The same launch sets the nzero
+// words at `zero` to 0 (the split-K counters of the product that follows).
 hipError_t launch_scale_quant_rows(const void* x, bool bf16, int64_t rows, int64_t cols,
                                    const float* col_scale, bool norm, float eps, void* q,
-                                   float* row_scale, int fmt, hipStream_t st);
+                                   float* row_scale, int fmt, hipStream_t st,
+                                   unsigned* zero = nullptr, int nzero = 0);
 // The weight (n rows, col_scale s) and the activations (m rows, col_scale
 // inv_s) of one layer, both with k columns, quantized to INT8 in one launch.
 hipError_t launch_scale_quant_pair(const void* w, int64_t n, const float* s, void* qw, float* sw,
@@ -42,18 +44,22 @@ hipError_t launch_fold(const float* a, const float* b, int64_t n, float* out, hi
 hipError_t launch_layernorm_quant_rows(const void* x, int64_t rows, int64_t cols, const float* g,
                                        const float* b, float eps, void* q, float* row_scale,
                                        hipStream_t st);
-// Split-K few-token GEMM with the dequant epilogue (17 <= M <= 32): S int32
-// partial slices of M x N in `partials` (S from splitk_plan), summed exactly
-// by a second kernel.  With S == 1 there is one launch and `partials` is unused.
-constexpr int kSplitkCT = 4;  // 16-channel weight fragments per block
+// Split-K few-token GEMM with the dequant epilogue (kSplitkMinM <= M <= 32 on
+// narrow layers with long rows; splitk_plan): one launch over groups x splits
+// blocks.  Each block stores an int32 partial slice of M x N in `partials`
+// (splits slices) and counts itself on counters[group] (groups of them, zero
+// on entry, left at S); the last block of a group adds the slices and
+// dequantizes.
+constexpr int kSplitkCG = 4;     // 16-channel groups per block
+constexpr int kSplitkMinM = 17;  // fewest tokens that split
 struct SplitkPlan {
-  int splits;
-  int steps_per_split;  // 64-deep k steps per split; 0: shape not served
+  int splits;  // 0: shape not served (the unsplit kernels take it)
+  int groups;  // blocks per split, one counter each
 };
 SplitkPlan splitk_plan(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_splitk(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N, int64_t K,
                               const float* sa, const float* sb, void* y, bool bf16,
-                              int32_t* partials, hipStream_t st);
+                              int32_t* partials, unsigned* counters, hipStream_t st);
 // out_mode: 0 = int32 accumulators, 1 = fp16 dequant, 2 = bf16 dequant (int8
 // operands, K in bytes); 3 = fp16, 4 = bf16 dense product (16-bit operands,
 // K in elements, fp32 accumulation); 5 = fp16, 6 = bf16 dequant of FP8 E4M3

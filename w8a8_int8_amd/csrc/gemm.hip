@@ -68,8 +68,8 @@
 //
 // The same pipeline serves the dense fp16 / bf16 product (the comparison
 // baseline) and the FP8 E4M3 variant; few-token shapes go to k_gemv_rows (one
-// or two tokens) and k_gemm_fewtok (3 to 32), and, in the runtime forward on
-// narrow layers, to the split-K k_gemm_splitk (below).
+// or two tokens) and k_gemm_fewtok (3 to 32; in the runtime forward its
+// split-K form on narrow layers with long rows, below).
 #include <algorithm>
 #include <type_traits>
 
@@ -732,11 +732,48 @@ k_gemm_i8_two(const int8_t* __restrict__ qa, const int8_t* __restrict__ qb, int 
 // in the last piece are issued with out-of-range offsets.  The waves' int32
 // partial sums add exactly through LDS and the dequant epilogue follows, as
 // in the tiled kernel (a lane holds channels n .. n+3 of one token).
-template <int MT, int NW, int CG, int OUT>
+// The dequant epilogue of one lane's four channels n .. n+3 of token m (or
+// their int32 sums for OUT == 0), with the token's scale am and the
+// channels' scales bn.
+template <int OUT>
+__device__ __forceinline__ void fewtok_store(const v4i& cs, int m, int n, int N, float am,
+                                             float4 bn, void* __restrict__ out) {
+  if (OUT == 0) {
+    *(v4i*)((int32_t*)out + (int64_t)m * N + n) = cs;
+  } else {
+    const float wv[4] = {bn.x, bn.y, bn.z, bn.w};
+    unsigned short h[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float y = (float)cs[e];
+      y = y * am;
+      y = y * wv[e];
+      h[e] = OUT == 1 ? f32_to_f16_rne(y) : f32_to_bf16_rne(y);
+    }
+    uint2 o;
+    o.x = (unsigned)h[0] | ((unsigned)h[1] << 16);
+    o.y = (unsigned)h[2] | ((unsigned)h[3] << 16);
+    *(uint2*)((unsigned short*)out + (int64_t)m * N + n) = o;
+  }
+}
+
+// SPLIT: the block covers the pieces [np y / S, np (y + 1) / S) of split
+// y = blockIdx.y of S = gridDim.y, and the S blocks of one channel group meet
+// in memory.  Each stores its exact int32 partial slice (part[y][m][n]) with
+// the device-scope cache policy (sc1: the form the compiler gives
+// agent-scope atomic stores and loads on this target, coherent across the
+// XCDs' L2s), waits until the stores have completed, and counts itself on
+// the group's counter (zero on entry, a device-scope atomic).  The block that
+// brings the count to S adds the other slices, read with the same policy, to
+// its own sum held in registers and applies the epilogue.  No block waits
+// for another.
+template <int MT, int NW, int CG, int OUT, bool SPLIT>
 __global__ __launch_bounds__(64 * NW) void k_gemm_fewtok(
     const int8_t* __restrict__ qa, const int8_t* __restrict__ qb, int M, int N, int K,
-    const float* __restrict__ sa, const float* __restrict__ sb, void* __restrict__ out) {
-  constexpr int kNt = 2;  // cache policy: non-temporal
+    const float* __restrict__ sa, const float* __restrict__ sb, void* __restrict__ out,
+    int32_t* __restrict__ part, unsigned* __restrict__ counters) {
+  constexpr int kNt = 2;     // cache policy: non-temporal
+  constexpr int kDev = 16;   // cache policy: device scope (sc1)
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n0 = blockIdx.x * 16 * CG;
@@ -749,8 +786,10 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_fewtok(
   v4i(*wl)[CG][256] = (v4i(*)[CG][256])lbuf;
   v4i(*red)[CG * MT][64] = (v4i(*)[CG * MT][64])lbuf;
   const int np = (K + 255) / 256;  // 256-byte pieces per row
-  const int per = (np + NW - 1) / NW;
-  const int p0 = wave * per, p1 = min(np, p0 + per);
+  const int S = SPLIT ? (int)gridDim.y : 1, sp = SPLIT ? (int)blockIdx.y : 0;
+  const int q0 = (int)((int64_t)np * sp / S), q1 = (int)((int64_t)np * (sp + 1) / S);
+  const int per = (q1 - q0 + NW - 1) / NW;
+  const int p0 = q0 + wave * per, p1 = min(q1, p0 + per);
   const int lr = lane >> 4, lc = lane & 15;   // load: row within 4, 16-byte chunk
   const int r16 = lane & 15, kq = lane >> 4;  // fragment: row, chunk within the k step
 
@@ -804,46 +843,73 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_fewtok(
 #pragma unroll
     for (int t = 0; t < MT; ++t) red[wave][c * MT + t][lane] = acc[c][t];
   __syncthreads();
-  for (int f = wave; f < CG * MT; f += NW) {
+  constexpr int FW = (CG * MT + NW - 1) / NW;  // fragments finished per wave
+  v4i own[FW];
+  float am[FW];
+  float4 bn[FW];
+  // the slices: S x M x N int32 (the launcher keeps this under 2^31 bytes)
+  const rsrc_t rp = make_rsrc((const int8_t*)part, SPLIT ? (unsigned)S * (unsigned)M * (unsigned)N * 4u : 0u);
+#pragma unroll
+  for (int j = 0; j < FW; ++j) {
+    const int f = wave + j * NW;
+    if (f >= CG * MT) break;
     v4i cs = red[0][f][lane];
 #pragma unroll
     for (int w2 = 1; w2 < NW; ++w2) cs += red[w2][f][lane];
+    own[j] = cs;
     // lane holds channels n .. n+3 of token m
     const int m = (f % MT) * 16 + (lane & 15);
     const int n = n0 + (f / MT) * 16 + 4 * (lane >> 4);
     if (m >= M || n >= N) continue;
-    if (OUT == 0) {
-      *(v4i*)((int32_t*)out + (int64_t)m * N + n) = cs;
-    } else {
-      const float am = sa[m];
-      const float4 bn = *(const float4*)(sb + n);
-      const float wv[4] = {bn.x, bn.y, bn.z, bn.w};
-      unsigned short h[4];
+    // the scales now, so that the last block of a split does not wait for them
+    if (OUT != 0) {
+      am[j] = sa[m];
+      bn[j] = *(const float4*)(sb + n);
+    }
+    if (!SPLIT)
+      fewtok_store<OUT>(cs, m, n, N, am[j], bn[j], out);
+    else
+      __builtin_amdgcn_raw_buffer_store_b128(cs, rp, (unsigned)(((sp * M + m) * N + n) * 4), 0, kDev);
+  }
+  if constexpr (SPLIT) {
+    __shared__ unsigned last;
+    // this thread's slice stores have completed before the block is counted
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) last = atomicAdd(counters + blockIdx.x, 1u) == (unsigned)S - 1 ? 1u : 0u;
+    __syncthreads();
+    if (!last) return;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float y = (float)cs[e];
-        y = y * am;
-        y = y * wv[e];
-        h[e] = OUT == 1 ? f32_to_f16_rne(y) : f32_to_bf16_rne(y);
+    for (int j = 0; j < FW; ++j) {
+      const int f = wave + j * NW;
+      if (f >= CG * MT) break;
+      const int m = (f % MT) * 16 + (lane & 15);
+      const int n = n0 + (f / MT) * 16 + 4 * (lane >> 4);
+      if (m >= M || n >= N) continue;
+      v4i c = own[j];
+      for (int s2 = 0; s2 < S; ++s2) {
+        if (s2 == sp) continue;
+        c += __builtin_amdgcn_raw_buffer_load_b128(rp, (unsigned)(((s2 * M + m) * N + n) * 4), 0, kDev);
       }
-      uint2 o;
-      o.x = (unsigned)h[0] | ((unsigned)h[1] << 16);
-      o.y = (unsigned)h[2] | ((unsigned)h[3] << 16);
-      *(uint2*)((unsigned short*)out + (int64_t)m * N + n) = o;
+      fewtok_store<OUT>(c, m, n, N, am[j], bn[j], out);
     }
   }
 }
 
-template <int MT, int NW, int CG>
+template <int MT, int NW, int CG, bool SPLIT>
 void launch_fewtok_cfg(const int8_t* qa, const int8_t* qb, int M, int N, int K, const float* sa,
-                       const float* sb, void* out, int mode, hipStream_t st) {
-  const dim3 grid((unsigned)((N + 16 * CG - 1) / (16 * CG))), block(64 * NW);
+                       const float* sb, void* out, int mode, int splits, int32_t* part,
+                       unsigned* counters, hipStream_t st) {
+  const dim3 grid((unsigned)((N + 16 * CG - 1) / (16 * CG)), (unsigned)splits), block(64 * NW);
   if (mode == 0)
-    hipLaunchKernelGGL((k_gemm_fewtok<MT, NW, CG, 0>), grid, block, 0, st, qa, qb, M, N, K, sa, sb, out);
+    hipLaunchKernelGGL((k_gemm_fewtok<MT, NW, CG, 0, SPLIT>), grid, block, 0, st, qa, qb, M, N, K, sa, sb,
+                       out, part, counters);
   else if (mode == 1)
-    hipLaunchKernelGGL((k_gemm_fewtok<MT, NW, CG, 1>), grid, block, 0, st, qa, qb, M, N, K, sa, sb, out);
+    hipLaunchKernelGGL((k_gemm_fewtok<MT, NW, CG, 1, SPLIT>), grid, block, 0, st, qa, qb, M, N, K, sa, sb,
+                       out, part, counters);
   else
-    hipLaunchKernelGGL((k_gemm_fewtok<MT, NW, CG, 2>), grid, block, 0, st, qa, qb, M, N, K, sa, sb, out);
+    hipLaunchKernelGGL((k_gemm_fewtok<MT, NW, CG, 2, SPLIT>), grid, block, 0, st, qa, qb, M, N, K, sa, sb,
+                       out, part, counters);
 }
 
 // Shape choice, measured on the OPT-6.7B decode layers at 1-32 tokens: with
@@ -855,12 +921,13 @@ void launch_fewtok_cfg(const int8_t* qa, const int8_t* qb, int M, int N, int K, 
 template <int MT>
 hipError_t launch_fewtok(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N, int64_t K,
                          const float* sa, const float* sb, void* out, int mode, hipStream_t st) {
+  const int m = (int)M, n = (int)N, k = (int)K;
   if (N < 12288)
-    launch_fewtok_cfg<MT, 8, 1>(qa, qb, (int)M, (int)N, (int)K, sa, sb, out, mode, st);
+    launch_fewtok_cfg<MT, 8, 1, false>(qa, qb, m, n, k, sa, sb, out, mode, 1, nullptr, nullptr, st);
   else if constexpr (MT == 2)
-    launch_fewtok_cfg<MT, 8, 4>(qa, qb, (int)M, (int)N, (int)K, sa, sb, out, mode, st);
+    launch_fewtok_cfg<MT, 8, 4, false>(qa, qb, m, n, k, sa, sb, out, mode, 1, nullptr, nullptr, st);
   else
-    launch_fewtok_cfg<MT, 4, 2>(qa, qb, (int)M, (int)N, (int)K, sa, sb, out, mode, st);
+    launch_fewtok_cfg<MT, 4, 2, false>(qa, qb, m, n, k, sa, sb, out, mode, 1, nullptr, nullptr, st);
   return hipGetLastError();
 }
 
@@ -1001,144 +1068,6 @@ hipError_t launch_gemv(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N,
   return hipGetLastError();
 }
 
-// Split-K few-token GEMM (the runtime forward's path for 17 <= M <= 32 on
-// layers with fewer than 2048 output channels, where the unsplit few-token
-// kernel gets too few blocks).  A block
-// owns 16 * CT output channels and one of S contiguous ranges of 64-deep k
-// steps; its NW waves take the steps of that range in turn.  Per step a wave
-// loads CT weight fragments and MT activation fragments straight into
-// registers and issues CT * MT v_mfma_i32_16x16x64_i8, so each activation
-// fragment serves CT weight fragments.  The waves' int32 partials add exactly
-// through LDS.  With S == 1 the block applies the dequant epilogue itself;
-// otherwise it stores its int32 partial slice (rows < M) and
-// k_splitk_reduce adds the S slices exactly and dequantizes.
-template <int MT, int CT, int U, int OUT>
-__global__ __launch_bounds__(512) void k_gemm_splitk(const int8_t* __restrict__ qa,
-                                                     const int8_t* __restrict__ qb, int M, int N,
-                                                     int K, int steps_per_split,
-                                                     const float* __restrict__ sa,
-                                                     const float* __restrict__ sb,
-                                                     void* __restrict__ out) {
-  constexpr int NW = 8;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int n0 = blockIdx.x * 16 * CT;
-  const int split = blockIdx.y;
-  const int nsteps = (K + 63) / 64;
-  const int st0 = split * steps_per_split;
-  const int st1 = min(nsteps, st0 + steps_per_split);
-  const rsrc_t rw = make_rsrc(qb + (int64_t)n0 * K, (unsigned)min(16 * CT, N - n0) * (unsigned)K);
-  const rsrc_t rx = make_rsrc(qa, (unsigned)M * (unsigned)K);
-  const int r16 = lane & 15, kq = lane >> 4;  // fragment row, 16-byte k chunk
-  int voff_w[CT], voff_x[MT];
-#pragma unroll
-  for (int c = 0; c < CT; ++c) voff_w[c] = (c * 16 + r16) * K + kq * 16;
-#pragma unroll
-  for (int t = 0; t < MT; ++t) voff_x[t] = (t * 16 + r16) * K + kq * 16;
-
-  v4i acc[CT][MT];
-#pragma unroll
-  for (int c = 0; c < CT; ++c)
-#pragma unroll
-    for (int t = 0; t < MT; ++t) acc[c][t] = v4i{0, 0, 0, 0};
-  for (int s0 = st0 + wave; s0 < st1; s0 += NW * U) {
-    v4i w[U][CT], x[U][MT];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int st = s0 + u * NW;
-      const int k0 = st * 64;
-      const bool out_k = st >= st1 || k0 + kq * 16 >= K;
-#pragma unroll
-      for (int c = 0; c < CT; ++c)
-        w[u][c] = __builtin_amdgcn_raw_buffer_load_b128(rw, out_k ? kOob : voff_w[c], k0, 0);
-#pragma unroll
-      for (int t = 0; t < MT; ++t)
-        x[u][t] = __builtin_amdgcn_raw_buffer_load_b128(rx, out_k ? kOob : voff_x[t], k0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int c = 0; c < CT; ++c)
-#pragma unroll
-        for (int t = 0; t < MT; ++t)
-          acc[c][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[u][c], x[u][t], acc[c][t], 0, 0, 0);
-  }
-
-  // exact sum of the waves' partials; fragment f is finished by wave f % NW
-  __shared__ v4i red[NW][CT * MT][64];
-#pragma unroll
-  for (int c = 0; c < CT; ++c)
-#pragma unroll
-    for (int t = 0; t < MT; ++t) red[wave][c * MT + t][lane] = acc[c][t];
-  __syncthreads();
-  for (int f = wave; f < CT * MT; f += NW) {
-    v4i cs = red[0][f][lane];
-#pragma unroll
-    for (int w2 = 1; w2 < NW; ++w2) cs += red[w2][f][lane];
-    // lane holds channels n .. n+3 of token m
-    const int m = (f % MT) * 16 + (lane & 15);
-    const int n = n0 + (f / MT) * 16 + 4 * (lane >> 4);
-    if (m >= M || n >= N) continue;
-    if (OUT == 0) {
-      *(v4i*)((int32_t*)out + ((int64_t)split * M + m) * N + n) = cs;
-    } else {
-      const float am = sa[m];
-      const float4 bn = *(const float4*)(sb + n);
-      const float wv[4] = {bn.x, bn.y, bn.z, bn.w};
-      unsigned short h[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float y = (float)cs[e];
-        y = y * am;
-        y = y * wv[e];
-        h[e] = OUT == 1 ? f32_to_f16_rne(y) : f32_to_bf16_rne(y);
-      }
-      uint2 o;
-      o.x = (unsigned)h[0] | ((unsigned)h[1] << 16);
-      o.y = (unsigned)h[2] | ((unsigned)h[3] << 16);
-      *(uint2*)((unsigned short*)out + (int64_t)m * N + n) = o;
-    }
-  }
-}
-
-// Exact int32 sum of the S partial slices (S x M x N), then the dequant
-// epilogue; one thread per 4 consecutive channels of one token.
-template <int OUT>
-__global__ __launch_bounds__(256) void k_splitk_reduce(const int32_t* __restrict__ part, int S,
-                                                       int M, int N, const float* __restrict__ sa,
-                                                       const float* __restrict__ sb,
-                                                       void* __restrict__ y) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (m, n / 4)
-  const int n4 = N / 4;
-  if (i >= (int64_t)M * n4) return;
-  const int m = (int)(i / n4), n = (int)(i % n4) * 4;
-  v4i c = *(const v4i*)(part + (int64_t)m * N + n);
-  for (int s = 1; s < S; ++s) c += *(const v4i*)(part + ((int64_t)s * M + m) * N + n);
-  const float am = sa[m];
-  const float4 bn = *(const float4*)(sb + n);
-  const float wv[4] = {bn.x, bn.y, bn.z, bn.w};
-  unsigned short h[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    float v = (float)c[e];
-    v = v * am;
-    v = v * wv[e];
-    h[e] = OUT == 1 ? f32_to_f16_rne(v) : f32_to_bf16_rne(v);
-  }
-  uint2 o;
-  o.x = (unsigned)h[0] | ((unsigned)h[1] << 16);
-  o.y = (unsigned)h[2] | ((unsigned)h[3] << 16);
-  *(uint2*)((unsigned short*)y + (int64_t)m * N + n) = o;
-}
-
-template <int MT, int OUT>
-void launch_splitk_kernel(const int8_t* qa, const int8_t* qb, int M, int N, int K, int s, int spp,
-                          const float* sa, const float* sb, void* out, hipStream_t st) {
-  constexpr int CT = kSplitkCT, U = 3;
-  const dim3 grid((unsigned)((N + 16 * CT - 1) / (16 * CT)), (unsigned)s), block(512);
-  hipLaunchKernelGGL((k_gemm_splitk<MT, CT, U, OUT>), grid, block, 0, st, qa, qb, M, N, K, spp, sa,
-                     sb, out);
-}
 
 template <int BM, int BN, int BK, int NST, int WGM, int WGN>
 hipError_t launch_tile(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N, int64_t K,
@@ -1286,42 +1215,40 @@ hipError_t launch_gemm(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N,
 
 
 SplitkPlan splitk_plan(int64_t M, int64_t N, int64_t K) {
-  SplitkPlan p{1, 0};
-  // With 2048 or more output channels the unsplit few-token kernel has
-  // enough blocks (at 32 tokens on 16384 -> 4096 it matched the split
-  // product: 22.6 against 23.2 us), so only narrower layers are split.
-  if (M < 17 || M > 32 || N < 1 || N >= 2048 || K < 1) return p;
-  const int64_t tiles = (N + 16 * kSplitkCT - 1) / (16 * kSplitkCT);
-  const int64_t nsteps = (K + 63) / 64;
-  // about one block per CU, and at least 32 k steps (2 KiB of each weight row)
-  // per split
-  int64_t s = (256 + tiles - 1) / tiles;
-  s = std::min<int64_t>(s, std::max<int64_t>(1, nsteps / 32));
+  SplitkPlan p{0, 0};
+  if (M < kSplitkMinM || M > 32 || N < 1 || N >= 12288 || K < 1) return p;
+  // Below 12288 channels the unsplit few-token kernel gives each block one
+  // 16-channel group, and every block reads the whole activation rows: from
+  // 17 tokens (two 16-token fragments) that is more than the weight's bytes
+  // again.  The split form gives a block four groups and 1/S of K.  About one
+  // block per CU, at least 8 pieces of 256 bytes per split (one per wave), at
+  // most 16 splits; rows of fewer than 32 pieces split only under 2048
+  // channels, where the unsplit kernel would get fewer than 128 blocks.
+  // Measured in the runtime forward: at 24 and 32 tokens 7-17% faster on
+  // 16384 -> 4096, 11008 -> 4096 and 8192 -> 8192; at 16 tokens 1-8% slower;
+  // 4096 x 4096 is faster unsplit.
+  const int64_t groups = (N + 16 * kSplitkCG - 1) / (16 * kSplitkCG);
+  const int64_t np = (K + 255) / 256;
+  if (np < 32 && N >= 2048) return p;
+  int64_t s = (256 + groups - 1) / groups;
+  s = std::min<int64_t>(s, np / 8);
   s = std::min<int64_t>(s, 16);
+  if (s < 2) return p;
   p.splits = (int)s;
-  p.steps_per_split = (int)((nsteps + s - 1) / s);
+  p.groups = (int)groups;
   return p;
 }
 
 hipError_t launch_gemm_splitk(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N, int64_t K,
                               const float* sa, const float* sb, void* y, bool bf16,
-                              int32_t* partials, hipStream_t st) {
+                              int32_t* partials, unsigned* counters, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
   const SplitkPlan p = splitk_plan(M, N, K);
-  if (p.steps_per_split == 0) return hipErrorInvalidValue;
-  const int m = (int)M, n = (int)N, k = (int)K;
-  if (p.splits == 1) {
-    if (bf16) launch_splitk_kernel<2, 2>(qa, qb, m, n, k, 1, p.steps_per_split, sa, sb, y, st);
-    else launch_splitk_kernel<2, 1>(qa, qb, m, n, k, 1, p.steps_per_split, sa, sb, y, st);
-    return hipGetLastError();
-  }
-  launch_splitk_kernel<2, 0>(qa, qb, m, n, k, p.splits, p.steps_per_split, sa, sb, partials, st);
-  const int64_t threads = M * (N / 4);
-  const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
-  if (bf16)
-    hipLaunchKernelGGL(k_splitk_reduce<2>, grid, block, 0, st, partials, p.splits, m, n, sa, sb, y);
-  else
-    hipLaunchKernelGGL(k_splitk_reduce<1>, grid, block, 0, st, partials, p.splits, m, n, sa, sb, y);
+  if (p.splits == 0) return hipErrorInvalidValue;
+  const int m = (int)M, n = (int)N, k = (int)K, mode = bf16 ? 2 : 1;
+  static_assert(kSplitkMinM > 16, "two 16-token fragments");
+  launch_fewtok_cfg<2, 8, kSplitkCG, true>(qa, qb, m, n, k, sa, sb, y, mode, p.splits, partials,
+                                           counters, st);
   return hipGetLastError();
 }
 

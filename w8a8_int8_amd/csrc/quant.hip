@@ -108,9 +108,13 @@ struct RowSet {
 // Blocks [0, b_first) take the rows of set a, blocks from b_first on those of
 // set b (both with cols8 chunks per row): two matrices with the same row
 // length, such as a layer's weight and its activations, quantize in one launch.
+// Block 0 also clears `zero` (nzero words), at its end where the row's
+// registers are free: the counters of the product that follows in the same
+// stream, so that no separate fill is needed.
 template <int CPT, int R, bool BF16, int FMT, bool NORM>
 __global__ __launch_bounds__(1024) void k_scale_quant_rows(RowSet a, RowSet b, unsigned b_first,
-                                                           int cols8, float eps) {
+                                                           int cols8, float eps,
+                                                           unsigned* __restrict__ zero, int nzero) {
   const bool in_b = blockIdx.x >= b_first;
   const v4u* __restrict__ x = in_b ? b.x : a.x;
   const int64_t rows = in_b ? b.rows : a.rows;
@@ -231,39 +235,48 @@ __global__ __launch_bounds__(1024) void k_scale_quant_rows(RowSet a, RowSet b, u
       q[row * cols8 + c] = o;
     }
   }
+  if (blockIdx.x == 0)
+    for (int i = tid; i < nzero; i += G) zero[i] = 0u;
 }
 
 RowSet row_set(const void* x, int64_t rows, const float* cs, void* q, float* row_scale) {
   return RowSet{(const v4u*)x, rows, (const float4*)cs, (uint2*)q, row_scale};
 }
 
+struct Zero {
+  unsigned* p;
+  int n;
+};
+
 template <int CPT, int R, bool BF16, int FMT, bool NORM>
-void launch_one(const RowSet& a, const RowSet& b, int cols8, int G, float eps, hipStream_t st) {
+void launch_one(const RowSet& a, const RowSet& b, int cols8, int G, float eps, Zero z,
+                hipStream_t st) {
   const unsigned blocks_a = (unsigned)((a.rows + R - 1) / R);
-  const unsigned blocks = blocks_a + (unsigned)((b.rows + R - 1) / R);
+  unsigned blocks = blocks_a + (unsigned)((b.rows + R - 1) / R);
+  if (blocks == 0) blocks = 1;  // no rows: one block still clears z
   hipLaunchKernelGGL((k_scale_quant_rows<CPT, R, BF16, FMT, NORM>), dim3(blocks), dim3(G), 0, st,
-                     a, b, blocks_a, cols8, eps);
+                     a, b, blocks_a, cols8, eps, z.p, z.n);
 }
 
 template <int CPT, int R>
 hipError_t launch_cfg(const RowSet& a, const RowSet& b, bool bf16, int fmt, int cols8, int G,
-                      bool norm, float eps, hipStream_t st) {
+                      bool norm, float eps, Zero z, hipStream_t st) {
   if (norm) {  // RMS norm fold (INT8 only)
-    if (bf16) launch_one<CPT, R, true, 0, true>(a, b, cols8, G, eps, st);
-    else launch_one<CPT, R, false, 0, true>(a, b, cols8, G, eps, st);
+    if (bf16) launch_one<CPT, R, true, 0, true>(a, b, cols8, G, eps, z, st);
+    else launch_one<CPT, R, false, 0, true>(a, b, cols8, G, eps, z, st);
   } else if (fmt == 0) {
-    if (bf16) launch_one<CPT, R, true, 0, false>(a, b, cols8, G, eps, st);
-    else launch_one<CPT, R, false, 0, false>(a, b, cols8, G, eps, st);
+    if (bf16) launch_one<CPT, R, true, 0, false>(a, b, cols8, G, eps, z, st);
+    else launch_one<CPT, R, false, 0, false>(a, b, cols8, G, eps, z, st);
   } else {
-    if (bf16) launch_one<CPT, R, true, 1, false>(a, b, cols8, G, eps, st);
-    else launch_one<CPT, R, false, 1, false>(a, b, cols8, G, eps, st);
+    if (bf16) launch_one<CPT, R, true, 1, false>(a, b, cols8, G, eps, z, st);
+    else launch_one<CPT, R, false, 1, false>(a, b, cols8, G, eps, z, st);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_sets(const RowSet& a, const RowSet& b, bool bf16, int64_t cols, bool norm,
-                       float eps, int fmt, hipStream_t st) {
-  if (a.rows + b.rows == 0) return hipSuccess;
+                       float eps, int fmt, Zero z, hipStream_t st) {
+  if (a.rows + b.rows == 0 && z.n == 0) return hipSuccess;
   const int cols8 = (int)(cols / 8);
   // Threads per row: two 16-byte chunks each (more for rows past 2048 chunks,
   // where the block size reaches 1024), a whole number of waves.  Rows per
@@ -278,17 +291,17 @@ hipError_t launch_sets(const RowSet& a, const RowSet& b, bool bf16, int64_t cols
   if (G > 1024) G = 1024;
   const int cpt = (cols8 + G - 1) / G;
   switch (cpt <= 1 ? 1 : cpt) {
-    case 1: return launch_cfg<1, 4>(a, b, bf16, fmt, cols8, G, norm, eps, st);
+    case 1: return launch_cfg<1, 4>(a, b, bf16, fmt, cols8, G, norm, eps, z, st);
     case 2:
       if (cols8 > 1024 && cols8 <= 1536)
-        return launch_cfg<2, 4>(a, b, bf16, fmt, cols8, G, norm, eps, st);
-      return launch_cfg<2, 2>(a, b, bf16, fmt, cols8, G, norm, eps, st);
-    case 3: return launch_cfg<3, 1>(a, b, bf16, fmt, cols8, G, norm, eps, st);
-    case 4: return launch_cfg<4, 1>(a, b, bf16, fmt, cols8, G, norm, eps, st);
-    case 5: return launch_cfg<5, 1>(a, b, bf16, fmt, cols8, G, norm, eps, st);
-    case 6: return launch_cfg<6, 1>(a, b, bf16, fmt, cols8, G, norm, eps, st);
-    case 7: return launch_cfg<7, 1>(a, b, bf16, fmt, cols8, G, norm, eps, st);
-    case 8: return launch_cfg<8, 1>(a, b, bf16, fmt, cols8, G, norm, eps, st);
+        return launch_cfg<2, 4>(a, b, bf16, fmt, cols8, G, norm, eps, z, st);
+      return launch_cfg<2, 2>(a, b, bf16, fmt, cols8, G, norm, eps, z, st);
+    case 3: return launch_cfg<3, 1>(a, b, bf16, fmt, cols8, G, norm, eps, z, st);
+    case 4: return launch_cfg<4, 1>(a, b, bf16, fmt, cols8, G, norm, eps, z, st);
+    case 5: return launch_cfg<5, 1>(a, b, bf16, fmt, cols8, G, norm, eps, z, st);
+    case 6: return launch_cfg<6, 1>(a, b, bf16, fmt, cols8, G, norm, eps, z, st);
+    case 7: return launch_cfg<7, 1>(a, b, bf16, fmt, cols8, G, norm, eps, z, st);
+    case 8: return launch_cfg<8, 1>(a, b, bf16, fmt, cols8, G, norm, eps, z, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -297,17 +310,18 @@ hipError_t launch_sets(const RowSet& a, const RowSet& b, bool bf16, int64_t cols
 
 hipError_t launch_scale_quant_rows(const void* x, bool bf16, int64_t rows, int64_t cols,
                                    const float* col_scale, bool norm, float eps, void* q,
-                                   float* row_scale, int fmt, hipStream_t st) {
+                                   float* row_scale, int fmt, hipStream_t st, unsigned* zero,
+                                   int nzero) {
   const RowSet a = row_set(x, rows, col_scale, q, row_scale);
   return launch_sets(a, row_set(nullptr, 0, nullptr, nullptr, nullptr), bf16, cols, norm, eps, fmt,
-                     st);
+                     Zero{zero, nzero}, st);
 }
 
 hipError_t launch_scale_quant_pair(const void* w, int64_t n, const float* s, void* qw, float* sw,
                                    const void* x, int64_t m, const float* inv_s, void* qx,
                                    float* sx, bool bf16, int64_t k, hipStream_t st) {
   return launch_sets(row_set(w, n, s, qw, sw), row_set(x, m, inv_s, qx, sx), bf16, k, false, 0.0f,
-                     0, st);
+                     0, Zero{nullptr, 0}, st);
 }
 
 // LayerNorm fold (fp16 rows), one row per block.  The smoothing's inv_s is
