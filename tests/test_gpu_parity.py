@@ -233,6 +233,38 @@ def test_gemm_dequant(out, M, N, K):
     assert_y_close(np_bits(y), y_or, name)
 
 
+@pytest.mark.parametrize("out", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("M,N,K", [(1, 136, 256), (2, 264, 512), (8, 520, 256), (24, 1032, 1040),
+                                   (300, 520, 272)])
+def test_gemm_dequant_extreme_scales(out, M, N, K):
+    """Channel scales spread over the output format's whole exponent range
+    (fp32 subnormals 2^-149 up to 2^127 for bf16, 2^-40 .. 2^30 for fp16) and
+    token scales near 1, so that the fp32 products and the 16-bit outputs
+    reach subnormals, ties and values past the format's range (which round
+    to infinity) in every row: every epilogue (row streaming, few-token,
+    tiled) rounds as the oracle does, bit for bit."""
+    qa, qb = rand_codes(M, K, 5 * M + K), rand_codes(N, K, 7 * N + K)
+    g = torch.Generator(device="cpu").manual_seed(M + N + K)
+    lo, hi = (-149.0, 127.0) if out == torch.bfloat16 else (-40.0, 30.0)
+    sb = torch.exp2(torch.linspace(lo, hi, N) + 0.5 * torch.rand(N, generator=g)).clamp(
+        max=2.0 ** 127).to(DEV)
+    sa = torch.exp2(torch.randint(-8, 9, (M,), generator=g).float()
+                    + torch.rand(M, generator=g)).to(DEV)
+    y = w8.gemm_dequant(qa, sa, qb, sb, out)
+    name = "f16" if out == torch.float16 else "bf16"
+    with np.errstate(over="ignore"):
+        y_or = oracle.dequant(oracle.gemm_i32(host(qa), host(qb)), host(sa), host(sb), name)
+    got = np_bits(y).view(np.uint16)
+    want = y_or.view(np.uint16)
+    assert np.array_equal(got, want)
+    # the case mix the test is for
+    exp_bits = (want >> (10 if name == "f16" else 7)) & (0x1F if name == "f16" else 0xFF)
+    mant = want & (0x3FF if name == "f16" else 0x7F)
+    top = 0x1F if name == "f16" else 0xFF
+    assert ((exp_bits == 0) & (mant != 0)).any()  # subnormal outputs
+    assert (exp_bits == top).any()  # infinities
+
+
 def _tile_of_shape(M, N):
     """The tiled kernel's tile choice for an M x N output (restated from the
     launcher: fullest last wave of blocks over 256 CUs, times the useful

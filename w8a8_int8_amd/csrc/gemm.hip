@@ -186,10 +186,11 @@ __device__ __forceinline__ void block_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// The hardware conversion (v_cvt_pk_bf16_f32 on this target, two values per
+// instruction) rounds to nearest even and keeps fp32 subnormals, as the
+// kernels' fp32 denormal mode does.
 __device__ __forceinline__ unsigned short f32_to_bf16_rne(float f) {
-  unsigned u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (unsigned short)(u >> 16);
+  return __builtin_bit_cast(unsigned short, (__bf16)f);
 }
 
 __device__ __forceinline__ unsigned short f32_to_f16_rne(float f) {
