@@ -361,8 +361,9 @@ w8a8_status_t w8a8_gemm_dequant_e4m3(const uint8_t* qa, const float* sa, const u
 /* Bytes of workspace w8a8_linear needs for M tokens, K input and N output
  * channels: the INT8 activations and their per-token scales, then, where the
  * product is split along K (17 <= M <= 32 on fewer than 12288 output
- * channels, with rows of 32 or more 256-byte pieces, K > 7936, or under 2048
- * channels of 16 or more, K > 3840), the int32 partial sums (S x M x N) and one 4-byte counter
+ * channels with rows of 32 or more 256-byte pieces, K > 7936; 3 <= M <= 16 on
+ * fewer than 2048 channels with rows of 64 or more, K > 16128), the int32
+ * partial sums (S x M x N) and one 4-byte counter
  * per 64 output channels; each part 256-byte aligned.  0 for negative
  * sizes. */
 size_t w8a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
@@ -371,7 +372,7 @@ size_t w8a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * Runtime forward of one smoothed W8A8 linear layer (steps 3 + 4 + 5):
  * (qX, sx) = scale_quant_rows(x, inv_s) into the workspace, then
  * y = gemm_dequant(qX, sx, qw, sw).  No host sync.  On the split shapes
- * (decode batches of 17 to 32 tokens on narrow layers with long rows; see
+ * (decode batches on narrow layers with long rows; see
  * w8a8_linear_workspace_bytes) the product is split along K over more blocks
  * in the same launch: each block stores its exact int32 partial sums in the
  * workspace and the last block of each 64-channel group adds the S slices

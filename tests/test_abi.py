@@ -96,26 +96,32 @@ def test_workspace_bytes():
     assert lib.w8a8_linear_workspace_bytes(1, 8, 16) == 256 + 256  # one split: no partials
     assert lib.w8a8_linear_workspace_bytes(2048, 4096, 4096) == 2048 * 4096 + 2048 * 4
     assert lib.w8a8_linear_workspace_bytes(-1, 8, 16) == 0
-    # 17-32 tokens split K below 12288 output channels when rows have 32 or more
-    # 256-byte pieces (or below 2048 channels): blocks of 64 channels, about
-    # 256 blocks, at least 8 pieces per split, at most 16 splits.  The
-    # workspace adds the int32 slices (splits x M x N) and one 4-byte counter
-    # per 64-channel group, each rounded up to 256 bytes.
-    # 1024 channels: 16 groups; K = 16384 is 64 pieces: 8 splits; K = 4096: 2
+    # The runtime forward splits K at 17-32 tokens below 12288 output channels
+    # when rows have 32 or more 256-byte pieces, and at 3-16 tokens below 2048
+    # channels when they have 64 or more: blocks of 64 channels, about 256
+    # blocks, at least 8 pieces per split, at most 16 splits.  The workspace
+    # adds the int32 slices (splits x M x N) and one 4-byte counter per
+    # 64-channel group, each rounded up to 256 bytes.
+    # 1024 channels: 16 groups; K = 16384 is 64 pieces: 8 splits
     assert lib.w8a8_linear_workspace_bytes(32, 1024, 16384) == 32 * 16384 + 256 + 8 * 32 * 1024 * 4 + 256
-    assert lib.w8a8_linear_workspace_bytes(32, 1024, 4096) == 32 * 4096 + 256 + 2 * 32 * 1024 * 4 + 256
     assert lib.w8a8_linear_workspace_bytes(24, 1024, 16384) == 24 * 16384 + 256 + 8 * 24 * 1024 * 4 + 256
-    # (slices rounded up to 256 bytes)
-    assert lib.w8a8_linear_workspace_bytes(17, 2040, 4096) == 17 * 4096 + 256 + (2 * 17 * 2040 * 4 + 64) + 256
+    assert lib.w8a8_linear_workspace_bytes(8, 1024, 16384) == 8 * 16384 + 256 + 8 * 8 * 1024 * 4 + 256
+    assert lib.w8a8_linear_workspace_bytes(3, 1024, 16384) == 3 * 16384 + 256 + (8 * 3 * 1024 * 4) + 256
     # 4096 channels: 64 groups, 4 splits; 2048: 32 groups, 8 splits
     assert lib.w8a8_linear_workspace_bytes(32, 4096, 16384) == 32 * 16384 + 256 + 4 * 32 * 4096 * 4 + 256
     assert lib.w8a8_linear_workspace_bytes(32, 2048, 16384) == 32 * 16384 + 256 + 8 * 32 * 2048 * 4 + 256
-    # unsplit: rows of 16 pieces from 2048 channels, 12288 channels or more,
-    # 16 tokens or fewer
+    # (slices rounded up to 256 bytes): 2040 channels, 32 pieces: 32 groups, 4 splits
+    assert lib.w8a8_linear_workspace_bytes(17, 2040, 8192) == 17 * 8192 + 256 + (4 * 17 * 2040 * 4 + 128) + 256
+    # unsplit: rows of 16 pieces at 17-32 tokens, at 3-16 tokens rows of fewer
+    # than 64 pieces or 2048 channels or more, 12288 channels or more, 1-2 tokens
+    assert lib.w8a8_linear_workspace_bytes(32, 1024, 4096) == 32 * 4096 + 256
+    assert lib.w8a8_linear_workspace_bytes(17, 2040, 4096) == 17 * 4096 + 256
     assert lib.w8a8_linear_workspace_bytes(32, 4096, 4096) == 32 * 4096 + 256
+    assert lib.w8a8_linear_workspace_bytes(16, 1024, 8192) == 16 * 8192 + 256
+    assert lib.w8a8_linear_workspace_bytes(16, 2048, 16384) == 16 * 16384 + 256
     assert lib.w8a8_linear_workspace_bytes(32, 16384, 4096) == 32 * 4096 + 256
     assert lib.w8a8_linear_workspace_bytes(32, 12288, 16384) == 32 * 16384 + 256
-    assert lib.w8a8_linear_workspace_bytes(16, 1024, 16384) == 16 * 16384 + 256
+    assert lib.w8a8_linear_workspace_bytes(2, 1024, 16384) == 2 * 16384 + 256
 
 
 @cpu_only

@@ -140,11 +140,11 @@ def test_few_token_kernel_loads_stay_in_bounds(M, N, K):
 
 def splitk_plan(M, N, K):
     """(splits, groups) of the runtime forward's split-K form, or None."""
-    if M < 17 or M > 32 or N < 1 or N >= 12288 or K < 1:
+    if M < 3 or M > 32 or N < 1 or N >= 12288 or K < 1:
         return None
     groups = -(-N // 64)
     npc = -(-K // 256)
-    if npc < 32 and N >= 2048:
+    if (npc < 32) if M >= 17 else (N >= 2048 or npc < 64):
         return None
     s = min(-(-256 // groups), npc // 8, 16)
     return (s, groups) if s >= 2 else None
@@ -165,8 +165,9 @@ def splitk_slice_offsets(M, N, S, sp, n0, MT, CG=4):
     return out
 
 
-@pytest.mark.parametrize("M,N,K", [(32, 4096, 16384), (24, 1024, 16384), (17, 2040, 4096),
-                                   (31, 2056, 8208), (24, 264, 65536), (20, 8192, 8192)])
+@pytest.mark.parametrize("M,N,K", [(32, 4096, 16384), (24, 1024, 16384), (5, 1024, 16384),
+                                   (31, 2056, 8208), (16, 264, 65536), (20, 8192, 8192),
+                                   (17, 2040, 8192), (3, 2040, 16400)])
 def test_split_k_loads_and_slices_stay_in_bounds(M, N, K):
     S, groups = splitk_plan(M, N, K)
     MT = -(-M // 16)
@@ -188,7 +189,11 @@ def test_split_k_plan_shapes():
     assert splitk_plan(32, 4096, 16384) == (4, 64)
     assert splitk_plan(32, 8192, 8192) == (2, 128)
     assert splitk_plan(17, 1024, 16384) == (8, 16)
-    assert splitk_plan(16, 1024, 16384) is None
+    assert splitk_plan(16, 1024, 16384) == (8, 16)
+    assert splitk_plan(16, 2048, 16384) is None
+    assert splitk_plan(16, 1024, 8192) is None
+    assert splitk_plan(2, 1024, 16384) is None
+    assert splitk_plan(32, 1024, 4096) is None
     assert splitk_plan(32, 4096, 4096) is None
     assert splitk_plan(32, 12288, 16384) is None
     assert splitk_plan(32, 520, 1040) is None  # 5 pieces per row

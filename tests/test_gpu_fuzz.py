@@ -199,16 +199,18 @@ def test_fuzz_gemm_float(case):
 
 @pytest.mark.parametrize("case", range(8))
 def test_fuzz_linear_split_k(case):
-    """17-32 tokens with K long enough that the runtime forward splits it:
-    under 2048 channels from 4096 columns, up to 12280 channels from 8192."""
+    """Token counts and K for which the runtime forward splits K: 3-32 tokens
+    under 2048 channels with rows of 64 or more 256-byte pieces, 17-32 tokens
+    up to 12280 channels with rows of 32 or more."""
     rng = np.random.default_rng(7000 + case)
     dtype = torch.float16 if case % 2 == 0 else torch.bfloat16
-    M = int(rng.integers(17, 33))
     if case < 4:
-        K = 16 * int(rng.integers(256, 1024))
+        M = int(rng.integers(3, 33))
+        K = 16 * int(rng.integers(1009, 2048))
         N = 8 * int(rng.integers(1, 256))
     else:
-        K = 16 * int(rng.integers(512, 1024))
+        M = int(rng.integers(17, 33))
+        K = 16 * int(rng.integers(497, 1024))
         N = 8 * int(rng.integers(256, 1536))
     w = torch.from_numpy((rng.standard_normal((N, K)) * 0.02).astype(np.float32)).to(dtype).to(DEV)
     xc = rand_x(rng, 64, K, dtype)

@@ -22,11 +22,14 @@ def fill(t: torch.Tensor, seed: int, scale: float = 1.0):
 
 
 # 8 and 24 tokens on 4096 or more channels: the few-token GEMM; 24 tokens on
-# 1024 channels: its split-K form (partial slices in the workspace, counters
-# cleared by the quantization launch); 512 tokens: the tiled GEMM
-@pytest.mark.parametrize("M,N", [(8, 12288), (24, 4096), (24, 1024), (512, 12288)])
-def test_path_replays_match_eager(M, N):
-    K = 4096
+# 1024 channels with 8192 columns: its split-K form (partial slices in the
+# workspace, counters cleared by the quantization launch); 512 tokens: the
+# tiled GEMM.  form "pair": the benchmark step's calls (both quantizations in
+# one launch, then gemm_dequant) instead of the runtime forward.
+@pytest.mark.parametrize("M,N,K,form", [(8, 12288, 4096, "linear"), (24, 4096, 4096, "linear"),
+                                        (24, 1024, 8192, "linear"), (512, 12288, 4096, "linear"),
+                                        (512, 4096, 4096, "pair"), (24, 4096, 4096, "pair")])
+def test_path_replays_match_eager(M, N, K, form):
     xc = torch.empty((2048, K), dtype=torch.float16, device=DEV)
     w = torch.empty((N, K), dtype=torch.float16, device=DEV)
     x = torch.empty((M, K), dtype=torch.float16, device=DEV)
@@ -38,11 +41,18 @@ def test_path_replays_match_eager(M, N):
     ws = torch.empty(w8.linear_workspace_bytes(M, N, K), dtype=torch.uint8, device=DEV)
     scratch = w8.calibrate_smooth_scratch(K, DEV)
 
+    qx = torch.empty((M, K), dtype=torch.int8, device=DEV)
+    sx = torch.empty(M, **f32)
+
     def path():
         ax.zero_()  # a fill kernel, not a memset node
         w8.calibrate_smooth(xc, w, 0.5, ax, aw, s, inv_s, scratch)
-        w8.scale_quant_rows(w, s, qw, sw)
-        w8.linear(x, inv_s, qw, sw, y, ws)
+        if form == "pair":
+            w8.scale_quant_pair(w, s, x, inv_s, qw, sw, qx, sx)
+            w8.gemm_dequant(qx, sx, qw, sw, torch.float16, y)
+        else:
+            w8.scale_quant_rows(w, s, qw, sw)
+            w8.linear(x, inv_s, qw, sw, y, ws)
 
     fill(xc, 1, 3.0); fill(w, 2, 0.02); fill(x, 3, 3.0)
     path()  # warm up outside capture

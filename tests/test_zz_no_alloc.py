@@ -53,8 +53,11 @@ def _bits(t):
     # 32-token call, then one token
     ([(2048, 4096, 4096), (32, 4096, 16384), (24, 1024, 16384), (32, 4096, 4096), (1, 4104, 1024)],
      torch.float16),
-    # the largest Llama-2-7B activation (2048 x 11008), then 17-32 tokens on a narrow layer
-    ([(2048, 4096, 11008), (20, 1536, 4096), (5, 520, 1040)], torch.bfloat16),
+    # the largest Llama-2-7B activation (2048 x 11008), then 17-32 tokens on a narrow
+    # layer with long rows (split), a narrow short-row call (unsplit), one at 5 tokens
+    # split on a narrower layer, and one on a tiny layer
+    ([(2048, 4096, 11008), (20, 1536, 8192), (20, 1536, 4096), (5, 1024, 16384), (5, 520, 1040)],
+     torch.bfloat16),
 ])
 def test_noalloc_matches_linear_on_calls_in_a_row(shapes, dtype):
     for i, (M, N, K) in enumerate(shapes):

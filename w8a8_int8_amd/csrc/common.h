@@ -44,14 +44,13 @@ hipError_t launch_fold(const float* a, const float* b, int64_t n, float* out, hi
 hipError_t launch_layernorm_quant_rows(const void* x, int64_t rows, int64_t cols, const float* g,
                                        const float* b, float eps, void* q, float* row_scale,
                                        hipStream_t st);
-// Split-K few-token GEMM with the dequant epilogue (kSplitkMinM <= M <= 32 on
-// narrow layers with long rows; splitk_plan): one launch over groups x splits
+// Split-K few-token GEMM with the dequant epilogue (3 <= M <= 32 on narrow
+// layers with long rows; splitk_plan): one launch over groups x splits
 // blocks.  Each block stores an int32 partial slice of M x N in `partials`
 // (splits slices) and counts itself on counters[group] (groups of them, zero
 // on entry, left at S); the last block of a group adds the slices and
 // dequantizes.
-constexpr int kSplitkCG = 4;     // 16-channel groups per block
-constexpr int kSplitkMinM = 17;  // fewest tokens that split
+constexpr int kSplitkCG = 4;  // 16-channel groups per block
 struct SplitkPlan {
   int splits;  // 0: shape not served (the unsplit kernels take it)
   int groups;  // blocks per split, one counter each

@@ -1217,20 +1217,24 @@ hipError_t launch_gemm(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N,
 
 SplitkPlan splitk_plan(int64_t M, int64_t N, int64_t K) {
   SplitkPlan p{0, 0};
-  if (M < kSplitkMinM || M > 32 || N < 1 || N >= 12288 || K < 1) return p;
+  if (M < 3 || M > 32 || N < 1 || N >= 12288 || K < 1) return p;
   // Below 12288 channels the unsplit few-token kernel gives each block one
-  // 16-channel group, and every block reads the whole activation rows: from
-  // 17 tokens (two 16-token fragments) that is more than the weight's bytes
-  // again.  The split form gives a block four groups and 1/S of K.  About one
-  // block per CU, at least 8 pieces of 256 bytes per split (one per wave), at
-  // most 16 splits; rows of fewer than 32 pieces split only under 2048
-  // channels, where the unsplit kernel would get fewer than 128 blocks.
-  // Measured in the runtime forward: at 24 and 32 tokens 7-17% faster on
-  // 16384 -> 4096, 11008 -> 4096 and 8192 -> 8192; at 16 tokens 1-8% slower;
-  // 4096 x 4096 is faster unsplit.
-  const int64_t groups = (N + 16 * kSplitkCG - 1) / (16 * kSplitkCG);
+  // 16-channel group, and every block reads the whole activation rows; under
+  // 2048 channels it also gets fewer than 128 blocks.  The split form gives a
+  // block four groups and 1/S of K, and pays a hand-over of partial sums
+  // through memory, which long rows amortize.  Measured on the few-token
+  // kernels alone and in the runtime forward:
+  //   17-32 tokens, rows of 32 or more 256-byte pieces: 7-17% faster on
+  //     16384 -> 4096, 11008 -> 4096 and 8192 -> 8192, up to 45% on
+  //     16384 -> 1024; at 16 pieces (4096 -> 1024, 1536, 4096) slower;
+  //   3-16 tokens, under 2048 channels with rows of 64 or more pieces:
+  //     9-67% faster (16384 -> 1024, 65536 -> 264); at 32 pieces and on
+  //     wider layers level or slower.
+  // About one block per CU, at least 8 pieces per split (one per wave), at
+  // most 16 splits.
   const int64_t np = (K + 255) / 256;
-  if (np < 32 && N >= 2048) return p;
+  if (M >= 17 ? np < 32 : (N >= 2048 || np < 64)) return p;
+  const int64_t groups = (N + 16 * kSplitkCG - 1) / (16 * kSplitkCG);
   int64_t s = (256 + groups - 1) / groups;
   s = std::min<int64_t>(s, np / 8);
   s = std::min<int64_t>(s, 16);
@@ -1247,9 +1251,12 @@ hipError_t launch_gemm_splitk(const int8_t* qa, const int8_t* qb, int64_t M, int
   const SplitkPlan p = splitk_plan(M, N, K);
   if (p.splits == 0) return hipErrorInvalidValue;
   const int m = (int)M, n = (int)N, k = (int)K, mode = bf16 ? 2 : 1;
-  static_assert(kSplitkMinM > 16, "two 16-token fragments");
-  launch_fewtok_cfg<2, 8, kSplitkCG, true>(qa, qb, m, n, k, sa, sb, y, mode, p.splits, partials,
-                                           counters, st);
+  if (M <= 16)
+    launch_fewtok_cfg<1, 8, kSplitkCG, true>(qa, qb, m, n, k, sa, sb, y, mode, p.splits, partials,
+                                             counters, st);
+  else
+    launch_fewtok_cfg<2, 8, kSplitkCG, true>(qa, qb, m, n, k, sa, sb, y, mode, p.splits, partials,
+                                             counters, st);
   return hipGetLastError();
 }
 
