@@ -129,11 +129,20 @@ def fewtok_loads(M, N, K, n0, MT, NW, CG, S=1, sp=0):
     return out
 
 
+def fewtok_config(M, N):
+    """(MT, NW, CG) of the few-token kernel (launch_gemm / launch_fewtok)."""
+    MT = 1 if M <= 16 else 2 if M <= 32 else 4 if M <= 64 else 8
+    if MT >= 4:
+        return MT, 4, 1 if N <= 4096 else 2 if N <= 8192 else 4
+    return (MT,) + ((8, 1) if N < 12288 else (8, 4) if MT == 2 else (4, 2))
+
+
 @pytest.mark.parametrize("M,N,K", [(3, 16392, 4096), (13, 136, 1040), (31, 4104, 16384), (17, 8, 16),
-                                   (32, 12288, 4112), (5, 24, 65536), (20, 12296, 272)])
+                                   (32, 12288, 4112), (5, 24, 65536), (20, 12296, 272),
+                                   (33, 4104, 4112), (64, 8200, 272), (37, 12288, 65536),
+                                   (65, 8192, 4112), (128, 4096, 16), (100, 24, 8208)])
 def test_few_token_kernel_loads_stay_in_bounds(M, N, K):
-    MT = -(-M // 16)
-    NW, CG = (8, 1) if N < 12288 else (8, 4) if MT == 2 else (4, 2)
+    MT, NW, CG = fewtok_config(M, N)
     for n0 in sorted({0, (N - 1) // (16 * CG) * (16 * CG)}):
         assert_in_bounds(fewtok_loads(M, N, K, n0, MT, NW, CG), M, N, K)
 

@@ -76,6 +76,30 @@ def test_linear_decode_split_k(dtype, N, K, M):
     assert np.array_equal(synth.to_numpy_bits(y).view(np.uint16), y_or.view(np.uint16))
 
 
+@pytest.mark.parametrize("M", [33, 48, 64, 65, 96, 128, 129])
+@pytest.mark.parametrize("N,K", [(4096, 4096), (4104, 1040), (8192, 2064), (12288, 1024), (12296, 272),
+                                 (520, 1040), (8, 16)])
+def test_linear_mid_tokens(N, K, M):
+    """33 to 128 tokens: the few-token kernel with four or eight token
+    fragments on layers of up to 12288 / 8192 channels, the tiled kernel
+    beyond; bit for bit against the oracle and the gemm_dequant call."""
+    dtype = torch.float16 if M % 2 else torch.bfloat16
+    p = layer(N, K, dtype, N + K)
+    g = torch.Generator(device="cpu").manual_seed(M * 5 + N)
+    x = torch.randn((M, K), generator=g)
+    x[:, :2] *= 40.0
+    x = x.to(dtype).to(DEV)
+    y = w8.linear(x, p["inv_s"], p["qw"], p["sw"])
+    name = "f16" if dtype == torch.float16 else "bf16"
+    qx_or, sx_or = oracle.scale_quant_rows(synth.to_numpy_bits(x), name, host(p["inv_s"]))
+    y_or = oracle.dequant(oracle.gemm_i32(qx_or, p["qw_host"]), sx_or, host(p["sw"]), name)
+    assert np.array_equal(synth.to_numpy_bits(y).view(np.uint16), y_or.view(np.uint16))
+    qx = torch.from_numpy(qx_or).to(DEV)
+    sx = torch.from_numpy(sx_or).to(DEV)
+    y2 = w8.gemm_dequant(qx, sx, p["qw"], p["sw"], dtype)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
 @pytest.mark.parametrize("N,K,M", [(1024, 16384, 32), (4096, 16384, 24)])
 def test_linear_decode_repeat_calls_bit_identical(N, K, M):
     """The partial slices are overwritten and the counters cleared on every
