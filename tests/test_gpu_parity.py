@@ -184,11 +184,13 @@ def rand_codes(rows, cols, seed):
     return torch.randint(-127, 128, (rows, cols), generator=g, dtype=torch.int8).to(DEV)
 
 
-# shapes cover the four tile configurations (128x128, 256x128, 256x192, 256x256), the
-# few-token kernels (row streaming: M <= 2, one to four 4 KiB row segments in flight
-# and ragged K; weight pieces through LDS: 3 to 32 tokens, one channel group per wave below
-# 12288 channels and two or four from there), ragged M, N and K tails, K = 0 and empty outputs
+# shapes cover the five tile configurations (128x32, 128x128, 256x128, 256x192, 256x256),
+# the few-token kernels (row streaming: M <= 2, one to four 4 KiB row segments in flight
+# and ragged K; weight pieces through LDS: 3 to 128 tokens, one to four channel groups per
+# block), ragged M, N and K tails, K = 0 and empty outputs
 GEMM_SHAPES = [(1, 8, 16), (37, 136, 80), (300, 520, 1040), (64, 512, 512),
+               (48, 4096, 4096), (100, 8192, 272), (64, 12288, 272), (65, 4104, 1040),
+               (129, 4096, 1040), (256, 4104, 4112), (200, 32, 16),
                (2048, 4096, 256), (4000, 8184, 272), (4096, 8192, 144), (513, 264, 4112),
                (5, 16, 0), (0, 8, 32), (8, 0, 32),
                (1, 4096, 16384), (3, 8, 64), (16, 520, 1040), (17, 136, 80), (32, 264, 4112),
@@ -221,7 +223,7 @@ def test_gemm_i32_extremes(M, K):
 @pytest.mark.parametrize("out", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("M,N,K", [(37, 136, 80), (300, 520, 1040), (2048, 4096, 256),
                                    (4000, 8184, 272), (5, 16, 0), (1, 4104, 4112), (32, 264, 1040),
-                                   (3000, 6000, 272)])
+                                   (3000, 6000, 272), (96, 8200, 528), (160, 4096, 1040)])
 def test_gemm_dequant(out, M, N, K):
     qa, qb = rand_codes(M, K, M + K), rand_codes(N, K, N + 2 * K + 1)
     g = torch.Generator(device="cpu").manual_seed(M * N)
@@ -267,8 +269,11 @@ def test_gemm_dequant_extreme_scales(out, M, N, K):
 
 def _tile_of_shape(M, N):
     """The tiled kernel's tile choice for an M x N output (restated from the
-    launcher: fullest last wave of blocks over 256 CUs, times the useful
+    launcher: 128 x 32 tiles for 129-256 tokens on up to 4096 channels;
+    otherwise the fullest last wave of blocks over 256 CUs, times the useful
     fraction of padded token rows, times a per-tile preference)."""
+    if 128 < M <= 256 and N <= 4096:
+        return (128, 32)
     best, best_score = None, -1.0
     for bm, bn, eff in ((256, 256, 1.0), (256, 128, 0.92), (128, 128, 0.8), (256, 192, 0.96)):
         tiles = -(-M // bm) * -(-N // bn)
@@ -290,8 +295,9 @@ def _tile_of_shape(M, N):
 
 
 @pytest.mark.parametrize("M,N,K,tile", [(2000, 24560, 272, (256, 256)), (2000, 12280, 272, (256, 192)),
-                                        (2000, 4088, 1040, (256, 128)), (130, 1000, 1040, (128, 128)),
-                                        (2000, 22000, 272, "two"), (4000, 7160, 1040, "two")])
+                                        (2000, 4088, 1040, (256, 128)), (300, 1000, 1040, (128, 128)),
+                                        (2000, 22000, 272, "two"), (4000, 7160, 1040, "two"),
+                                        (200, 4000, 1040, (128, 32)), (130, 1000, 272, (128, 32))])
 def test_gemm_tiles_ragged(M, N, K, tile):
     """Each tile of the tiled kernel, and the grid of two tile shapes (whole
     waves of 256 x 256 tiles, then 256 x 192 tiles over the last channels),
