@@ -72,7 +72,7 @@ TILES = [  # BM, BN, NST, WGM, WGN: every tile the launcher can pick
     (256, 192, 2, 4, 2),
     (256, 128, 3, 4, 2),
     (128, 128, 4, 2, 2),
-    (128, 32, 6, 4, 1),
+    (128, 32, 4, 4, 1),
 ]
 
 

@@ -269,10 +269,10 @@ def test_gemm_dequant_extreme_scales(out, M, N, K):
 
 def _tile_of_shape(M, N):
     """The tiled kernel's tile choice for an M x N output (restated from the
-    launcher: 128 x 32 tiles for 129-256 tokens on up to 4096 channels;
+    launcher: 128 x 32 tiles for 129-512 tokens on up to 4096 channels;
     otherwise the fullest last wave of blocks over 256 CUs, times the useful
     fraction of padded token rows, times a per-tile preference)."""
-    if 128 < M <= 256 and N <= 4096:
+    if 128 < M <= 512 and N <= 4096:
         return (128, 32)
     best, best_score = None, -1.0
     for bm, bn, eff in ((256, 256, 1.0), (256, 128, 0.92), (128, 128, 0.8), (256, 192, 0.96)):
@@ -295,9 +295,10 @@ def _tile_of_shape(M, N):
 
 
 @pytest.mark.parametrize("M,N,K,tile", [(2000, 24560, 272, (256, 256)), (2000, 12280, 272, (256, 192)),
-                                        (2000, 4088, 1040, (256, 128)), (300, 1000, 1040, (128, 128)),
+                                        (2000, 4088, 1040, (256, 128)), (600, 1000, 1040, (128, 128)),
                                         (2000, 22000, 272, "two"), (4000, 7160, 1040, "two"),
-                                        (200, 4000, 1040, (128, 32)), (130, 1000, 272, (128, 32))])
+                                        (200, 4000, 1040, (128, 32)), (130, 1000, 272, (128, 32)),
+                                        (500, 4096, 528, (128, 32))])
 def test_gemm_tiles_ragged(M, N, K, tile):
     """Each tile of the tiled kernel, and the grid of two tile shapes (whole
     waves of 256 x 256 tiles, then 256 x 192 tiles over the last channels),

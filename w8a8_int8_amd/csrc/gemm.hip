@@ -241,13 +241,24 @@ __device__ __forceinline__ void interleave_cols() {
 
 
 // The tiled kernels' LDS, sized for the largest tile's stages (every tiled
-// kernel runs one block per CU).  It is one file-scope array rather than a
+// kernel but the 128 x 32 one runs one block per CU).  It is one file-scope array rather than a
 // pointer handed to the tile code: with a pointer the compiler can no longer
 // tell the LDS-mode loads of later stages from the fragment reads of the
 // current one and waits for every outstanding load before the first reads
 // (measured 12% slower on the 256 x 192 tile).
 constexpr int kTileLds = 2 * 256 * 128 + 3 * 256 * 128;  // 160 KiB, the whole LDS
 __shared__ __attribute__((aligned(1024))) int8_t lds[kTileLds];
+// The narrow 128 x 32 tile's own, smaller LDS, so that two of its blocks fit
+// a CU (with its registers held to two waves per SIMD).  Selected at compile
+// time from one of two file-scope arrays, so the compiler still sees which
+// array every access uses.
+constexpr int kSmallLds = 80 * 1024;
+__shared__ __attribute__((aligned(1024))) int8_t lds_small[kSmallLds];
+template <bool SMALL>
+__device__ __forceinline__ int8_t* tile_lds() {
+  if constexpr (SMALL) return lds_small;
+  else return lds;
+}
 
 // One output tile (token tile tm, channel tile tn) of the tiled GEMM.  OUT as
 // in MmaKind.  The block has WGM x WGN waves; K (in bytes per row) advances
@@ -288,7 +299,7 @@ __device__ __forceinline__ void gemm_tile(const int8_t* __restrict__ qa,
                 FM >= 1 && FN >= 1 && FM * MB == WM && FN * MB == WN && KK % 2 == 0 &&
                 (MB / RPW) % CPR == 0, "unsupported tile");
   static_assert(NST >= 2 && (NST - 1) * 2 * L < 64, "unsupported pipeline depth");  // vmcnt range
-  static_assert(NSA * BM * BK + NSB * BN * BK <= kTileLds, "LDS size");
+  static_assert(NSA * BM * BK + NSB * BN * BK <= (BN == 32 ? kSmallLds : kTileLds), "LDS size");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -330,10 +341,12 @@ __device__ __forceinline__ void gemm_tile(const int8_t* __restrict__ qa,
   // fixed vmcnt values serve every iteration) and only touches the slot that
   // the stage would have used, which no live stage occupies.
   auto slot_a = [&](int st) -> int8_t* {
-    return kSym ? lds + (st % NST) * SLOT : lds + (st % NSA) * BM * BK;
+    int8_t* const base = tile_lds<BN == 32>();
+    return kSym ? base + (st % NST) * SLOT : base + (st % NSA) * BM * BK;
   };
   auto slot_b = [&](int st) -> int8_t* {
-    return kSym ? lds + (st % NST) * SLOT + BM * BK : lds + NSA * BM * BK + (st % NSB) * BN * BK;
+    int8_t* const base = tile_lds<BN == 32>();
+    return kSym ? base + (st % NST) * SLOT + BM * BK : base + NSA * BM * BK + (st % NSB) * BN * BK;
   };
   auto dma = [&](int st, int j0, int j1) {
     const int k0 = st * BK;
@@ -627,7 +640,7 @@ __device__ __forceinline__ void gemm_tile(const int8_t* __restrict__ qa,
   // every wave is past its last fragment read and its last LDS-mode load
   wait_lgkmcnt0();
   block_barrier();
-  int8_t* stage = lds + wave * MB * PITCH;
+  int8_t* stage = tile_lds<BN == 32>() + wave * MB * PITCH;
 #pragma unroll
   for (int b = 0; b < FM; ++b) {
 #pragma unroll
@@ -680,7 +693,8 @@ __device__ __forceinline__ void gemm_tile(const int8_t* __restrict__ qa,
 
 template <int BM, int BN, int BK, int NST, int WGM, int WGN, int OUT>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WGM * WGN, 64 * WGM * WGN),
-                          amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4))) void
+                          amdgpu_waves_per_eu(BN == 32 ? 2 : WGM * WGN / 4,
+                                              BN == 32 ? 2 : WGM * WGN / 4))) void
 k_gemm_i8(const int8_t* __restrict__ qa, const int8_t* __restrict__ qb, int M, int N, int K,
           const float* __restrict__ sa, const float* __restrict__ sb, void* __restrict__ out,
           int m_tiles, int n_tiles) {
@@ -1187,13 +1201,14 @@ hipError_t launch_gemm(const int8_t* qa, const int8_t* qb, int64_t M, int64_t N,
     return launch_fewtok<4>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
   if (!tiled_only && M <= 128 && N <= 8192)
     return launch_fewtok<8>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
-  // 129 to 256 tokens on up to 4096 channels (INT8): 128 x 32 tiles, four
-  // waves, six stages in flight, so that one wave of up to 256 blocks covers
-  // the output, where the other tiles give 32 to 64 blocks.  Measured 1.7
-  // times faster on 4096 x 4096 (24 -> 14.2 us) and 11008 -> 4096 (57 ->
-  // 32.5 us); from 384 tokens (two waves of blocks) slower.
-  if (out_mode <= 2 && M <= 256 && N <= 4096)
-    return launch_tile<128, 32, 128, 6, 4, 1>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
+  // 129 to 512 tokens on up to 4096 channels (INT8): 128 x 32 tiles, four
+  // waves, four stages in flight in an LDS array of their own (80 KiB), two
+  // blocks per CU, so that up to 512 blocks run at once where the other
+  // tiles give 32 to 128.  Measured on 4096 x 4096 24 -> 11.3-12.5 us at
+  // 129-256 tokens and 24-25 -> 18-21 us at 320-512; on 11008 -> 4096
+  // 57 -> 27.5-31.3 us and 57-59 -> 50-56 us.
+  if (out_mode <= 2 && M <= 512 && N <= 4096)
+    return launch_tile<128, 32, 128, 4, 4, 1>(qa, qb, M, N, K, sa, sb, out, out_mode, st);
   // Pick the tile whose last wave of blocks over 256 CUs is fullest, weighted
   // by the tile's output rate per CU relative to 256 x 256 (eff).  INT8
   // (16 x 16 x 64 MFMAs), measured per wave of blocks at K = 4096 on
