@@ -84,6 +84,27 @@ def test_rmsnorm_quant_rows_eps(eps):
     check(h, gamma, inv_s, eps)
 
 
+@pytest.mark.parametrize("dtype,exp", [(torch.float16, -20), (torch.bfloat16, -66)])
+@pytest.mark.parametrize("cols", [512, 4096, 11008])
+def test_rmsnorm_quant_rows_tiny_rows(dtype, exp, cols):
+    """Rows of tiny values with eps = 0, where a sum of squares lost to
+    flushing would show as an infinite row scale: fp16 subnormal inputs (their
+    squares are normal fp32 values), and bf16 values near 2^-66, whose squares
+    are fp32 subnormals (exact: 16 significant bits above 2^-149)."""
+    g = torch.Generator(device="cpu").manual_seed(cols + exp)
+    h = torch.randn((9, cols), generator=g) * 2.0 ** exp
+    gamma = torch.rand(cols, generator=g) * 1.5 + 0.25
+    inv_s = torch.exp(torch.rand(cols, generator=g) * 6 - 4)
+    h = h.to(dtype)
+    assert h.abs().max() > 0
+    if dtype == torch.float16:
+        assert (h.float().abs() < 2.0 ** -14).all()  # every input subnormal
+    else:
+        assert (h.float() ** 2 < 2.0 ** -126).all()  # every square subnormal in fp32
+    _, d = check(h.to(DEV), gamma.to(DEV), inv_s.to(DEV), 0.0)
+    assert torch.isfinite(d).all()
+
+
 def test_rmsnorm_quant_rows_codes_equal_folded_smoothing_quantizer():
     """The same codes as the smoothing quantizer with the folded weight g."""
     h, gamma, inv_s = case(300, 4096, torch.bfloat16, 3)

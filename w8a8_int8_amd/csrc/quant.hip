@@ -14,12 +14,14 @@
 // G threads (a multiple of the 64-wide wavefront, at most 1024) owns a row:
 // thread g holds the 16-byte chunks g, g + G, ... (CPT of them, normally 2),
 // so every wave load is 1 KiB of consecutive bytes and every wave store
-// 512 B.  The scaled row slice stays in registers between the max pass and
-// the quantize pass, so x is read from HBM exactly once.  A block handles R
+// 512 B.  The row slice stays in registers between the max pass and the
+// quantize pass (scaled, or as its 16-bit inputs), so x is read from HBM
+// exactly once.  A block handles R
 // consecutive rows with the same column ownership (the column scales are
 // loaded once per block and stay L2 resident) and issues all of its row loads
-// before the first reduction.  The row max is a wave-level butterfly followed
-// by one LDS round across the waves of the block.  Per element the VALU work
+// before the first reduction.  The row max is a wave reduction by DPP moves
+// within 16-lane rows and four lane reads, followed by one LDS round across
+// the waves of the block.  Per element the VALU work
 // is about six operations (widen, scale, max, rescale, round, pack/4).
 //
 // The FP8 variant (same smoothing, FP8 E4M3 grid as the page's remark on
@@ -39,10 +41,33 @@ namespace {
 // in the low mantissa bits, two's complement in the low byte.
 constexpr float kRoundMagic = 12582912.0f;
 
+// v as seen from the lane that the DPP control CTRL names (within rows of 16
+// lanes); every lane of the wave must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Reduction over the 64 lanes of a wave (all active), the same value in
+// every lane: pairs of lanes (quad_perm 1,0,3,2), quads (2,3,0,1), the other
+// quad of each 8 (row_half_mirror), the other 8 of each 16 (row_mirror),
+// then the four 16-lane rows read out and combined in a fixed order.  Each
+// step combines a value with its partner symmetrically, so the lanes agree.
+template <class Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+  v = op(v, dpp<0xb1>(v));
+  v = op(v, dpp<0x4e>(v));
+  v = op(v, dpp<0x141>(v));
+  v = op(v, dpp<0x140>(v));
+  return op(op(lane_value(v, 0), lane_value(v, 16)), op(lane_value(v, 32), lane_value(v, 48)));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-  return v;
+  return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); });
 }
 
 // Low bytes of four magic-rounded floats, packed little-endian.
@@ -83,9 +108,21 @@ __device__ __forceinline__ unsigned pack_e4m3(float a, float b, float c, float d
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  return wave_reduce(v, [](float a, float b) { return a + b; });
+}
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// acc + a^2 + b^2 for the 16-bit pair (a, b) packed in w (v_dot2_f32_*):
+// the squares of 16-bit values are exact in fp32.
+template <bool BF16>
+__device__ __forceinline__ float add_squares(unsigned w, float acc) {
+  if (BF16)
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                           __builtin_bit_cast(bf16x2, w), acc, false);
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), __builtin_bit_cast(f16x2, w), acc,
+                                false);
 }
 
 // FMT 0: symmetric INT8 codes (grid max 127); FMT 1: FP8 E4M3 codes (max 448).
@@ -153,8 +190,7 @@ __global__ __launch_bounds__(1024) void k_scale_quant_rows(RowSet a, RowSet b, u
     }
   }
 
-  // pass 1: v = x * c (kept in registers) and the row max of |v|
-  float v[R][CPT][8];
+  // pass 1: the row max of |v|, v = x * c
   float m[R], ss[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -162,17 +198,27 @@ __global__ __launch_bounds__(1024) void k_scale_quant_rows(RowSet a, RowSet b, u
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float xe = elem<BF16>(xv[r][i], e);
-        v[r][i][e] = xe * sc[i][e];
-        mr = fmaxf(mr, fabsf(v[r][i][e]));
-        // the square of a 16-bit value is exact in fp32, so the fused form
-        // rounds once, like the separate multiply and add would
-        if (NORM) sr = __builtin_fmaf(xe, xe, sr);
-      }
+      for (int e = 0; e < 8; ++e) mr = fmaxf(mr, fabsf(elem<BF16>(xv[r][i], e) * sc[i][e]));
+      // the sum of squares straight from the packed pairs
+      if (NORM)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) sr = add_squares<BF16>(xv[r][i][d], sr);
     }
     m[r] = wave_max(mr);
     ss[r] = NORM ? wave_sum(sr) : 0.0f;
+  }
+  // Pass 2 forms v again from the 16-bit inputs (the same one rounding).  In
+  // the RMS-norm form with several rows per block, the empty asm hides their
+  // values, so the fp32 products of pass 1 cannot be kept instead: the packed
+  // inputs take half their registers (66-68 in place of 83-104 at four rows
+  // of 11008 values, which admits a second block per CU).  The plain
+  // quantizer measured no faster that way on its own (2048 x 11008: 16.4
+  // against 15.1 us), so it is left to the compiler.
+  if constexpr (NORM && R > 1) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) asm volatile("" : "+v"(xv[r][i]));
   }
   __shared__ float red[R][16];
   __shared__ float red2[R][16];
@@ -221,7 +267,7 @@ __global__ __launch_bounds__(1024) void k_scale_quant_rows(RowSet a, RowSet b, u
       float t[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        t[e] = v[r][i][e] * rcp;
+        t[e] = (elem<BF16>(xv[r][i], e) * sc[i][e]) * rcp;
         if (FMT == 0) t[e] = t[e] + kRoundMagic;
       }
       uint2 o;
