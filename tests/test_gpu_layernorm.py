@@ -72,8 +72,13 @@ def stress_rows(x):
     return x
 
 
+# Row lengths reach every launch form: one chunk per thread (16-512), two
+# (1024), three on blocks of up to 512 threads (1040, 8208, 11008, ragged)
+# and above (16384 on 704 threads, 20480 on 1024), four on up to 512 threads
+# (4096, 5120, 7168) and on 1024 (28672), eight (65536).
 @pytest.mark.parametrize("rows,cols", [(4, 16), (5, 48), (9, 4096), (7, 11008), (64, 512), (1025, 4096), (2050, 7168),
-                                       (33, 28672), (5, 65536)])
+                                       (33, 28672), (5, 65536), (4, 1024), (4, 1040), (6, 5120),
+                                       (5, 8208), (5, 16384), (4, 20480)])
 def test_layernorm_quant_rows(rows, cols):
     x, gamma, beta, inv_s = case(rows, cols, rows * 7 + cols, offset=0.3)
     x = stress_rows(x)

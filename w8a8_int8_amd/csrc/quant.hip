@@ -207,14 +207,16 @@ __global__ __launch_bounds__(1024) void k_scale_quant_rows(RowSet a, RowSet b, u
     m[r] = wave_max(mr);
     ss[r] = NORM ? wave_sum(sr) : 0.0f;
   }
-  // Pass 2 forms v again from the 16-bit inputs (the same one rounding).  In
-  // the RMS-norm form with several rows per block, the empty asm hides their
-  // values, so the fp32 products of pass 1 cannot be kept instead: the packed
-  // inputs take half their registers (66-68 in place of 83-104 at four rows
-  // of 11008 values, which admits a second block per CU).  The plain
-  // quantizer measured no faster that way on its own (2048 x 11008: 16.4
-  // against 15.1 us), so it is left to the compiler.
-  if constexpr (NORM && R > 1) {
+  // In the RMS-norm form at four rows of two chunks (rows of 8200 to 12288
+  // values), pass 2 forms v again from the 16-bit inputs (the same one
+  // rounding): the empty asm hides their values, so the fp32 products of
+  // pass 1 cannot be kept instead, and the packed inputs take half their
+  // registers (66-68 in place of 83-104, which admits a second 11-wave block
+  // per CU).  Elsewhere the instance fits its occupancy either way and the
+  // extra pass-2 work only costs time (RMS-norm fold at 2048 x 4096: 9.07
+  // against 8.75 us; plain quantizer at 2048 x 11008: 16.4 against 15.1 us),
+  // so the compiler keeps the products.
+  if constexpr (NORM && R > 1 && R * CPT >= 8) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -425,11 +427,13 @@ __device__ __forceinline__ LnSums ln_add(LnSums a, const LnSums& b) {
   return a;
 }
 
-// Up to four chunks per thread the registers are held to 64, so that two
-// blocks of 1024 threads fit on a CU (one block per CU measured 15% slower).
-template <int CPT>
+// WPE bounds the registers: 8 waves per SIMD (64 registers) so that two
+// blocks of 1024 threads fit on a CU (one block per CU measured 15% slower),
+// 6 (80 registers) for blocks of up to 512 threads at three or four chunks,
+// 4 beyond four chunks.
+template <int CPT, int WPE>
 __global__ __attribute__((amdgpu_flat_work_group_size(64, 1024),
-                          amdgpu_waves_per_eu(CPT <= 4 ? 8 : 4))) void
+                          amdgpu_waves_per_eu(WPE))) void
 k_layernorm_quant_rows(const v4u* __restrict__ x,
                                                                int cols8,
                                                                const float4* __restrict__ gv,
@@ -543,10 +547,10 @@ k_layernorm_quant_rows(const v4u* __restrict__ x,
   }
 }
 
-template <int CPT>
+template <int CPT, int WPE = (CPT <= 4 ? 8 : 4)>
 void launch_ln(const void* x, int64_t rows, int cols8, int G, const float* g, const float* b,
                float eps, void* q, float* row_scale, hipStream_t st) {
-  hipLaunchKernelGGL(k_layernorm_quant_rows<CPT>, dim3((unsigned)rows), dim3(G), 0, st,
+  hipLaunchKernelGGL((k_layernorm_quant_rows<CPT, WPE>), dim3((unsigned)rows), dim3(G), 0, st,
                      (const v4u*)x, cols8, (const float4*)g, (const float4*)b, eps, (uint2*)q,
                      row_scale);
 }
@@ -558,15 +562,29 @@ hipError_t launch_layernorm_quant_rows(const void* x, int64_t rows, int64_t cols
                                        hipStream_t st) {
   if (rows == 0) return hipSuccess;
   const int cols8 = (int)(cols / 8);
-  int G = (cols8 + 1) / 2;  // two 16-byte chunks per thread, whole waves, at most 1024
+  // Chunks per thread: four for rows of up to 8192 values, three up to 16384,
+  // then blocks of 1024 threads.  The per-row work (the fp64 wave sums and
+  // their fixed-point conversion, two LDS rounds) is paid once per wave, so
+  // fewer, fuller waves per row issue fewer VALU instructions per element.
+  // Measured at 2048 rows against two chunks per thread: 13.3 against 15.0 us
+  // at 5120 columns, 16.9 against 18.5 at 7168, 24.3 against 30.1 at 11008;
+  // at 20480 columns three chunks measured slower (29.8 against 26.2).
+  const int target = cols8 <= 1024 ? 4 : cols8 <= 2048 ? 3 : 2;
+  int G = (cols8 + target - 1) / target;  // whole waves, at most 1024
   G = ((G + kWave - 1) / kWave) * kWave;
   if (G < kWave) G = kWave;
   if (G > 1024) G = 1024;
   switch ((cols8 + G - 1) / G) {
     case 1: launch_ln<1>(x, rows, cols8, G, g, b, eps, q, row_scale, st); break;
     case 2: launch_ln<2>(x, rows, cols8, G, g, b, eps, q, row_scale, st); break;
-    case 3: launch_ln<3>(x, rows, cols8, G, g, b, eps, q, row_scale, st); break;
-    case 4: launch_ln<4>(x, rows, cols8, G, g, b, eps, q, row_scale, st); break;
+    case 3:
+      if (G <= 512) launch_ln<3, 6>(x, rows, cols8, G, g, b, eps, q, row_scale, st);
+      else launch_ln<3>(x, rows, cols8, G, g, b, eps, q, row_scale, st);
+      break;
+    case 4:
+      if (G <= 512) launch_ln<4, 6>(x, rows, cols8, G, g, b, eps, q, row_scale, st);
+      else launch_ln<4>(x, rows, cols8, G, g, b, eps, q, row_scale, st);
+      break;
     case 5: launch_ln<5>(x, rows, cols8, G, g, b, eps, q, row_scale, st); break;
     case 6: launch_ln<6>(x, rows, cols8, G, g, b, eps, q, row_scale, st); break;
     case 7: launch_ln<7>(x, rows, cols8, G, g, b, eps, q, row_scale, st); break;
