@@ -63,6 +63,10 @@ def parse():
     ap.add_argument("--other-workloads", default="opt30b_prefill,llama2_70b_prefill,opt6.7b_decode",
                     help="comma-separated workloads whose kernels are also timed (per-kernel pass "
                          "only, into the `other_workloads` key); empty for none")
+    ap.add_argument("--steady-steps", type=int, default=200,
+                    help="after the timed steps, this many more steps with no pause, reported apart "
+                         "(`steady_state`) and not in `value`: the GPU's clock settles over the first "
+                         "15-20 ms of load, longer than the warm-up and timed steps together")
     ap.add_argument("--ceilings", action="store_true",
                     help="only run the hardware probes (read-only streaming, copy, INT8 MFMA from "
                          "registers with the shader clock) and print their figures")
@@ -217,6 +221,41 @@ class Layer:
         w8.gemm_dequant(self.qx, self.sx, self.qw, self.sw, self.x.dtype, self.y)
         if ev is not None:
             ev[1].record()
+
+
+def steady_state(run_step, step_i, n, every, te, layers, gemm_avg, ops_per_step, ops_per_launch):
+    """The same step, n more times right after the timed ones, with no pause
+    in between, timed in blocks of n // 4 steps.  After an idle spell the GPU
+    runs at a lower clock for the first 15-20 ms of load; the warm-up and
+    timed steps of the default run fall within that ramp.  The last block
+    shows the step at the settled clock.  Informational: `value` and
+    `roofline` come from the timed steps alone."""
+    import torch
+
+    blk = max(1, n // 4)
+    evs = {k: [(te.create(), te.create()) for _ in layers]
+           for k in range(3 * blk, 4 * blk) if k % every == 0}
+    ms = []
+    for b in range(4):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(b * blk, (b + 1) * blk):
+            run_step(step_i + k, evs.get(k))
+        torch.cuda.synchronize()
+        ms.append((time.perf_counter() - t0) / blk * 1e3)
+    avg = gemm_avg(evs)
+    return {
+        "steps": 4 * blk,
+        "ms_per_step_by_block": [round(t, 4) for t in ms],
+        "last_block": {
+            "ms_per_step": round(ms[-1], 4),
+            "TOPS": round(ops_per_step / (ms[-1] * 1e-3) / 1e12, 3),
+            "gemm_avg_launch_us": round(avg * 1e6, 3),
+            "gemm_frac_mfma": round(ops_per_launch / avg / 1e12 / PEAK_INT8_TOPS, 4),
+        },
+        "note": "informational, not `value`: the same step continued without pause after the "
+                "timed steps, in four blocks; the last block at the settled clock",
+    }
 
 
 def graph_time(fn, n):
@@ -592,16 +631,18 @@ def main():
     print(f"[bench] {wl.name}: {len(layers)} layers, M={wl.M[0]}, buffers ready", file=sys.stderr,
           flush=True)
 
-    step_i = 0
-    for _ in range(args.warmup):
-        run_step(step_i)
-        step_i += 1
-    torch.cuda.synchronize()
-
+    # The timing events are created before the warm-up steps, so that no host
+    # work leaves the GPU idle between the warm-up and the timed steps (an idle
+    # gap of 10 ms or more lets the GPU drop back to a lower clock state).
     te = TimingEvents()
     every = max(1, args.event_every)
     ev_steps = [k for k in range(args.steps) if k % every == 0]
     evs = {k: [(te.create(), te.create()) for _ in layers] for k in ev_steps}
+
+    step_i = 0
+    for _ in range(args.warmup):
+        run_step(step_i)
+        step_i += 1
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -614,12 +655,15 @@ def main():
     ops_per_step = sum(L.gemm_ops() for L in layers)
     value = ops_per_step / (elapsed / args.steps) / 1e12
 
-    gemm_s = [sum(a.elapsed_time(b) for a, b in row) * 1e-3 for row in evs.values()]
-    for row in evs.values():
-        for a, b in row:
-            a.destroy()
-            b.destroy()
-    gemm_launch_avg = sum(gemm_s) / (len(gemm_s) * len(layers))
+    def gemm_avg(evs):
+        gemm_s = [sum(a.elapsed_time(b) for a, b in row) * 1e-3 for row in evs.values()]
+        for row in evs.values():
+            for a, b in row:
+                a.destroy()
+                b.destroy()
+        return sum(gemm_s) / (len(gemm_s) * len(layers))
+
+    gemm_launch_avg = gemm_avg(evs)
     ops_per_launch = ops_per_step / len(layers)
     achieved = ops_per_launch / gemm_launch_avg / 1e12
     # few tokens (decode): the GEMM streams the weight and is HBM-bound
@@ -627,6 +671,11 @@ def main():
     # the kernel the launcher picks for that token count (one or two tokens:
     # whole weight rows streamed; up to 32: weight pieces transposed in LDS)
     decode_kernel = "k_gemv_rows" if wl.M[0] <= 2 else "k_gemm_fewtok"
+    steady = None
+    if args.steady_steps > 0 and not decode:
+        steady = steady_state(run_step, step_i, args.steady_steps, every, te, layers, gemm_avg,
+                              ops_per_step, ops_per_launch)
+        step_i += args.steady_steps
     bytes_per_launch = sum(L.gemm_bytes() for L in layers) / len(layers)
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
 
@@ -688,6 +737,8 @@ def main():
         },
         "kernels": kernels,
     }
+    if steady is not None:
+        rec["steady_state"] = steady
     if others:
         rec["other_workloads"] = others
     if not args.no_cpu_baseline:
