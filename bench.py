@@ -12,6 +12,13 @@ of the Llama-2-7B-shaped decoder block (prefill, M = 2048 tokens):
   4.+5. INT8 GEMM with the fused dequant epilogue -> fp16 Y
 All inputs are resident in HBM before the timed region.
 
+Order of a run: inputs built on the GPU; the per-kernel pass (each kernel
+timed alone, seconds of GPU work, which also brings the GPU from its idle
+clock to its working clock: the ramp takes 15-20 ms of load, longer than the
+warm-up steps); W warm-up steps; K timed steps; then `steady_state` (more
+steps with no pause, reported apart), the calibration-volume or decode pass,
+the other workloads and the CPU oracle.
+
 value = the step's INT8 GEMM work (2 M N K summed over the layers) divided by
 the whole step's wall time, in TOPS.  The per-kernel breakdown also times the
 dense fp16 product of each layer (same tiling on the 16-bit matrix cores) to
@@ -65,8 +72,8 @@ def parse():
                          "only, into the `other_workloads` key); empty for none")
     ap.add_argument("--steady-steps", type=int, default=200,
                     help="after the timed steps, this many more steps with no pause, reported apart "
-                         "(`steady_state`) and not in `value`: the GPU's clock settles over the first "
-                         "15-20 ms of load, longer than the warm-up and timed steps together")
+                         "(`steady_state`) and not in `value`: a check that the timed steps ran at "
+                         "the settled clock")
     ap.add_argument("--ceilings", action="store_true",
                     help="only run the hardware probes (read-only streaming, copy, INT8 MFMA from "
                          "registers with the shader clock) and print their figures")
@@ -226,10 +233,9 @@ class Layer:
 def steady_state(run_step, step_i, n, every, te, layers, gemm_avg, ops_per_step, ops_per_launch):
     """The same step, n more times right after the timed ones, with no pause
     in between, timed in blocks of n // 4 steps.  After an idle spell the GPU
-    runs at a lower clock for the first 15-20 ms of load; the warm-up and
-    timed steps of the default run fall within that ramp.  The last block
-    shows the step at the settled clock.  Informational: `value` and
-    `roofline` come from the timed steps alone."""
+    runs at a lower clock for the first 15-20 ms of load; the last block shows
+    the step at the settled clock, a check on the timed steps.
+    Informational: `value` and `roofline` come from the timed steps alone."""
     import torch
 
     blk = max(1, n // 4)
@@ -631,9 +637,16 @@ def main():
     print(f"[bench] {wl.name}: {len(layers)} layers, M={wl.M[0]}, buffers ready", file=sys.stderr,
           flush=True)
 
-    # The timing events are created before the warm-up steps, so that no host
-    # work leaves the GPU idle between the warm-up and the timed steps (an idle
-    # gap of 10 ms or more lets the GPU drop back to a lower clock state).
+    # The per-kernel pass (each kernel of the workload timed alone, a few
+    # seconds of GPU work) runs before the warm-up steps.  After an idle spell
+    # the GPU needs 15-20 ms of continuous load to reach its working clock,
+    # more than the warm-up steps take, so the timed steps would otherwise sit
+    # in that ramp.  The timing events are created before the warm-up steps
+    # too, so that no host work leaves the GPU idle between warm-up and timed
+    # steps (an idle gap of 10 ms or more lets the clock drop back).
+    kernels = kernel_breakdown(layers, args.kernel_reps)
+    torch.cuda.synchronize()
+    print("[bench] per-kernel pass done", file=sys.stderr, flush=True)
     te = TimingEvents()
     every = max(1, args.event_every)
     ev_steps = [k for k in range(args.steps) if k % every == 0]
@@ -679,12 +692,11 @@ def main():
     bytes_per_launch = sum(L.gemm_bytes() for L in layers) / len(layers)
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
 
-    kernels = kernel_breakdown(layers, args.kernel_reps)
     if decode:
         kernels["decode_sweep"] = decode_sweep(wl, layers, max(args.kernel_reps, 20))
     else:
         kernels["calibration_volume"] = calibration_volume(wl, layers, args.kernel_reps)
-    print("[bench] per-kernel pass done", file=sys.stderr, flush=True)
+    print("[bench] decode sweep / calibration volume done", file=sys.stderr, flush=True)
     others = {}
     for name in [n for n in args.other_workloads.split(",") if n and n != wl.name]:
         others[name] = other_workload(name, args.alpha, args.kernel_reps, dev)
