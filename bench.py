@@ -562,6 +562,19 @@ def ceilings(dev):
             best = max(best, nb / t / 1e9)
         sizes[f"{mb}MiB"] = round(best, 1)
     out["read_only_stream_GBs"]["by_size_best"] = sizes
+    # the same read of one buffer over and over (its second and later reads
+    # can come from the 256 MB last-level cache) beside the rotated read, at
+    # the sizes of the path's weights: what a second pass over W could gain
+    llc = {}
+    for mb in (64, 100, 150, 200, 300):
+        nb = mb << 20
+        nbuf = n // nb
+        t_same = graph_time(lambda i: lib.w8a8probe_read(src.data_ptr(), nb, sink.data_ptr(), 4096, 1,
+                                                         st()), 20)
+        t_rot = graph_time(lambda i: lib.w8a8probe_read(src[(i % nbuf) * nb:].data_ptr(), nb,
+                                                        sink.data_ptr(), 4096, 1, st()), 20)
+        llc[f"{mb}MiB"] = {"same_buffer": round(nb / t_same / 1e9, 1), "rotated": round(nb / t_rot / 1e9, 1)}
+    out["read_only_stream_GBs"]["reread_vs_rotated_4096_blocks"] = llc
     half = n // 2
     dst = torch.empty(half, dtype=torch.uint8, device=dev)
     copies = {}
