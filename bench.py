@@ -520,7 +520,7 @@ def cpu_baseline(wl, layers, alpha, min_seconds=10.0):
 
 
 def ceilings(dev):
-    """The box's practical ceilings, from the probes in libw8a8_probe.so (not
+    """The GPU's practical ceilings, from the probes in libw8a8_probe.so (not
     part of the path): read-only streaming and a plain copy over buffers past
     the 256 MB last-level cache, and back-to-back INT8 MFMAs from registers
     with each block's shader clock, for three operand patterns."""

@@ -1,4 +1,4 @@
-// Hardware probes of the box, for the roofline figures of the benchmark.
+// Hardware probes of the GPU, for the roofline figures of the benchmark.
 // They are not part of the W8A8 path: libw8a8_probe.so is a separate
 // library that only bench.py --ceilings loads.
 //
