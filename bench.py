@@ -4,9 +4,9 @@ One step = one pass of the whole path over one batch, for every linear layer
 of the Llama-2-7B-shaped decoder block (prefill, M = 2048 tokens):
   1. channel amax: fold one fresh 2048-token calibration batch into the
      layer's running max|X_j| (streaming calibration; step i uses batch i)
-  2. max|W_j| over the weight, smoothing factors s and 1/s (1 and these in one
-     launch, w8a8_calibrate_smooth), fold s into W and quantize it per output
-     channel
+  2. max|W_j| over the weight, smoothing factors s and 1/s (1 and these, for
+     every layer at once, in one launch: w8a8_calibrate_smooth_layers), fold s
+     into W and quantize it per output channel
   3. smooth X (X / s) and quantize it per token (2's fold + quantize and this
      in one launch, w8a8_scale_quant_pair)
   4.+5. INT8 GEMM with the fused dequant epilogue -> fp16 Y
@@ -214,14 +214,23 @@ class Layer:
         M = self.M if M is None else M
         return float(M * self.K + self.N * self.K + 2 * M * self.N + 4 * (M + self.N))
 
+    def calib_args(self, i):
+        """This layer's entry of the grouped calibration call for step i."""
+        return (self.cal[i % len(self.cal)], self.w, self.amax_x, self.amax_w, self.s, self.inv_s,
+                self.scratch)
+
     def step(self, i, ev=None):
-        """One pass of the path for this layer: calibration batch i folded into
-        the running max|X_j|, max|W_j| and the smoothing factors (one launch),
-        the weight folded and quantized and the activations smoothed and
+        """One pass of the path for this layer alone: calibration batch i
+        folded into the running max|X_j|, max|W_j| and the smoothing factors
+        (one launch), then quantize_forward."""
+        self.w8.calibrate_smooth(self.cal[i % len(self.cal)], self.w, self.alpha, self.amax_x,
+                                 self.amax_w, self.s, self.inv_s, self.scratch)
+        self.quantize_forward(ev)
+
+    def quantize_forward(self, ev=None):
+        """The weight folded and quantized and the activations smoothed and
         quantized (one launch), and the INT8 GEMM with its dequant epilogue."""
         w8 = self.w8
-        w8.calibrate_smooth(self.cal[i % len(self.cal)], self.w, self.alpha, self.amax_x,
-                            self.amax_w, self.s, self.inv_s, self.scratch)
         w8.scale_quant_pair(self.w, self.s, self.x, self.inv_s, self.qw, self.sw, self.qx, self.sx)
         if ev is not None:
             ev[0].record()
@@ -623,6 +632,7 @@ def main():
         sys.exit(2)
     import torch
 
+    import w8a8_int8_amd as w8
     from w8a8_int8_amd import _lib, synth
 
     _lib.load()
@@ -643,8 +653,11 @@ def main():
     layers = [Layer(wl, li, n_batches, args.alpha, dev) for li in range(len(wl.layers))]
 
     def run_step(i, evs_row=None):
+        # every layer's calibration batch, weight maxima and smoothing factors
+        # in one launch, then per layer the two quantizations and the GEMM
+        w8.calibrate_smooth_layers([L.calib_args(i) for L in layers], args.alpha)
         for li, L in enumerate(layers):
-            L.step(i, None if evs_row is None else evs_row[li])
+            L.quantize_forward(None if evs_row is None else evs_row[li])
 
     torch.cuda.synchronize()
     print(f"[bench] {wl.name}: {len(layers)} layers, M={wl.M[0]}, buffers ready", file=sys.stderr,
@@ -705,6 +718,17 @@ def main():
     bytes_per_launch = sum(L.gemm_bytes() for L in layers) / len(layers)
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
 
+    # the step's form of the calibration: every layer in one launch (timed
+    # here, after the timed steps: memory-bound work just before the warm-up
+    # steps would leave them at a lower clock)
+    t = graph_time(lambda i: w8.calibrate_smooth_layers([L.calib_args(i) for L in layers], args.alpha),
+                   args.kernel_reps)
+    by = sum(L.cal[0].numel() * 2 + L.w.numel() * 2 for L in layers)
+    kernels["calibrate_smooth_layers"] = {
+        "us": round(t * 1e6, 3), "GBs": round(by / t / 1e9, 1),
+        "frac_hbm": round(by / t / 1e9 / PEAK_HBM_GBS, 4),
+        "one_launch_per_layer_us": round(sum(v["calibrate_smooth"]["us"] for v in kernels.values()
+                                             if isinstance(v, dict) and "calibrate_smooth" in v), 3)}
     if decode:
         kernels["decode_sweep"] = decode_sweep(wl, layers, max(args.kernel_reps, 20))
     else:

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define W8A8_ABI_VERSION 6
+#define W8A8_ABI_VERSION 7
 
 /* Largest K for which 127 * 127 * K fits int32, so that every accumulator
  * (and every partial sum) of the INT8 product is exact in int32. */
@@ -151,6 +151,44 @@ w8a8_status_t w8a8_calibrate_smooth(const void* x_cal, int64_t cal_rows, const v
                                     int dtype, int64_t K, double alpha, float* amax_x,
                                     float* amax_w, float* s, float* inv_s, void* scratch,
                                     size_t scratch_bytes, hipStream_t stream);
+
+/*
+ * w8a8_calibrate_smooth for several layers in one launch: the usage example's
+ * `smooth_lm(model, act_scales, alpha)` smooths every linear layer of the
+ * model (page section "インストール・使用例"), and the layers are independent,
+ * so their calibration folds, weight maxima and smoothing factors can share a
+ * grid.  Each entry's results are the same bits as w8a8_calibrate_smooth with
+ * its arguments.  One launch covers up to 8 entries (more are split into
+ * several launches, in order).
+ *
+ *   layers   HOST array of n entries, read during the call only (the library
+ *            keeps no pointer to it).  Each entry: x_cal, cal_rows, w, N, K,
+ *            alpha, amax_x, amax_w, s, inv_s, scratch, scratch_bytes, with the
+ *            meaning, layout and rules of the w8a8_calibrate_smooth arguments
+ *            of the same names (device pointers).  The entries must not share
+ *            an output array or a scratch.
+ *   n        number of entries, n >= 0 (0: nothing is enqueued).
+ *   dtype    one dtype for every entry's x_cal and w.
+ * Errors: NULL (layers NULL with n > 0, or an entry's pointer), SHAPE (n < 0
+ * or an entry's sizes), ALIGN, DTYPE, ARG (an entry's alpha or scratch size),
+ * HIP.  Every entry is checked before anything is enqueued.
+ */
+typedef struct {
+  const void* x_cal;
+  int64_t cal_rows;
+  const void* w;
+  int64_t N;
+  int64_t K;
+  double alpha;
+  float* amax_x;
+  float* amax_w;
+  float* s;
+  float* inv_s;
+  void* scratch;
+  size_t scratch_bytes;
+} w8a8_calib_layer_t;
+w8a8_status_t w8a8_calibrate_smooth_layers(const w8a8_calib_layer_t* layers, int n, int dtype,
+                                           hipStream_t stream);
 
 /*
  * Steps 2 (weights) and 3 (activations): scale every column, then quantize

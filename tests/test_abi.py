@@ -36,11 +36,11 @@ def declared_symbols():
 def test_library_loads_and_exports_header_symbols():
     lib = _lib.load()
     syms = declared_symbols()
-    assert len(syms) == 19
+    assert len(syms) == 20
     for s in syms:
         assert hasattr(lib, s), s
         assert s in _lib.PROTOTYPES, s
-    assert lib.w8a8_abi_version() == 6
+    assert lib.w8a8_abi_version() == 7
 
 
 def declared_prototypes():
@@ -238,6 +238,53 @@ def test_calibrate_smooth_rejects():
     assert call(alpha=1.5) == EARG and call(alpha=float("nan")) == EARG
     assert call(nbytes=need - 1) == EARG
     assert call(x=PODD) == EALIGN and call(scratch=P + 4) == EALIGN and call(s=P + 2) == EALIGN
+
+
+def test_calib_layer_struct_matches_the_header():
+    """The binding's w8a8_calib_layer_t has the header's fields, in order, with
+    the pointer / integer / floating kind of each, and no padding."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct \{(.*?)\}\s*w8a8_calib_layer_t;", text, flags=re.S).group(1)
+    decls = [d.strip() for d in body.split(";") if d.strip()]
+    names = [d.split()[-1].lstrip("*") for d in decls]
+    assert names == [f[0] for f in _lib.CalibLayer._fields_]
+    for d, (_, t) in zip(decls, _lib.CalibLayer._fields_):
+        kind = "ptr" if "*" in d else "fp" if d.startswith("double") else "int"
+        assert kind == ("ptr" if t is ctypes.c_void_p else "fp" if t is ctypes.c_double else "int"), d
+    assert ctypes.sizeof(_lib.CalibLayer) == 8 * len(names)
+
+
+@cpu_only
+def test_calibrate_smooth_layers_rejects():
+    """Every entry is checked before anything is enqueued; a bad entry
+    anywhere in the array fails the whole call."""
+    lib = _lib.load()
+    f = lib.w8a8_calibrate_smooth_layers
+    need = lib.w8a8_calibrate_smooth_scratch_bytes(64)
+
+    def entry(**kw):
+        e = dict(x_cal=P, cal_rows=4, w=P, N=8, K=64, alpha=0.5, amax_x=P, amax_w=P, s=P, inv_s=P,
+                 scratch=P, scratch_bytes=need)
+        e.update(kw)
+        return _lib.CalibLayer(**e)
+
+    def call(entries, dtype=0, n=None):
+        arr = (_lib.CalibLayer * max(1, len(entries)))(*entries)
+        return f(ctypes.addressof(arr), len(entries) if n is None else n, dtype, 0)
+
+    assert f(None, 0, 0, 0) == 0  # nothing to do
+    assert f(None, 1, 0, 0) == ENULL
+    assert call([entry()], n=-1) == ESHAPE
+    assert call([entry()], dtype=2) == EDTYPE
+    for bad, code in ((dict(K=12), ESHAPE), (dict(N=-1), ESHAPE), (dict(cal_rows=-1), ESHAPE),
+                      (dict(x_cal=0), ENULL), (dict(scratch=0), ENULL), (dict(inv_s=0), ENULL),
+                      (dict(alpha=1.5), EARG), (dict(alpha=float("nan")), EARG),
+                      (dict(scratch_bytes=need - 1), EARG), (dict(w=PODD), EALIGN),
+                      (dict(s=P + 2), EALIGN)):
+        # the bad entry last, after good ones: still rejected before any launch
+        assert call([entry(), entry(), entry(**bad)]) == code, bad
+    # entries past 8 are checked too (they would go to a second launch)
+    assert call([entry()] * 9 + [entry(K=0)]) == ESHAPE
 
 
 @cpu_only

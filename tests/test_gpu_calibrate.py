@@ -112,3 +112,72 @@ def test_calibrate_smooth_running_over_batches():
     assert np.array_equal(host(ax).view(np.uint32), want.view(np.uint32))
     aw_or = oracle.channel_amax(np_bits(w), "f16")
     assert assert_s_parity(host(s), host(inv_s), want, aw_or, 0.5) == 0
+
+
+LAYER_SETS = [
+    # the Llama-2-7B block's four layers, one 2048-token batch each
+    [(2048, 12288, 4096), (2048, 4096, 4096), (2048, 22016, 4096), (2048, 4096, 11008)],
+    # one layer; mixed and ragged shapes, empty calibration batch and empty weight
+    [(129, 520, 1032)],
+    [(37, 136, 136), (0, 520, 1032), (300, 0, 4104), (5, 7, 8), (0, 0, 264)],
+    # ten layers: two launches (eight, then two)
+    [(64 + 9 * i, 256 + 40 * i, 8 * (32 + 17 * i)) for i in range(10)],
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("si", range(len(LAYER_SETS)))
+def test_calibrate_smooth_layers(si, dtype):
+    """Several layers in one launch: every layer's maxima against the oracle
+    bit for bit, s and inv_s to the smoothing-factor bar, and the same bits
+    as one calibrate_smooth call per layer; every scratch ends zero."""
+    alpha = 0.5 if si != 2 else 0.8
+    shapes = LAYER_SETS[si]
+    ins = [inputs(c, n, k, dtype, seed=1000 * si + 10 * i + (dtype == torch.bfloat16))
+           for i, (c, n, k) in enumerate(shapes)]
+    f32 = dict(dtype=torch.float32, device=DEV)
+    groups, outs = [], []
+    for (c, n, k), (xc, w, start) in zip(shapes, ins):
+        ax = start.clone()
+        o = (ax, torch.empty(k, **f32), torch.empty(k, **f32), torch.empty(k, **f32),
+             w8.calibrate_smooth_scratch(k, DEV))
+        outs.append(o)
+        groups.append((xc if c else None, w) + o)
+    w8.calibrate_smooth_layers(groups, alpha)
+    torch.cuda.synchronize()
+    for (c, n, k), (xc, w, start), (ax, aw, s, inv_s, scratch) in zip(shapes, ins, outs):
+        assert not scratch.any()
+        ax_or = oracle.channel_amax(np_bits(xc), dt_name(xc), amax=host(start)) if c \
+            else host(start)
+        aw_or = oracle.channel_amax(np_bits(w), dt_name(w)) if n else np.zeros(k, np.float32)
+        assert np.array_equal(host(ax).view(np.uint32), ax_or.view(np.uint32)), (c, n, k)
+        assert np.array_equal(host(aw).view(np.uint32), aw_or.view(np.uint32)), (c, n, k)
+        assert assert_s_parity(host(s), host(inv_s), ax_or, aw_or, alpha) == 0
+        ax1 = start.clone()
+        aw1, s1, inv1 = w8.calibrate_smooth(xc if c else None, w, alpha, ax1)
+        for a, b in ((ax, ax1), (aw, aw1), (s, s1), (inv_s, inv1)):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), (c, n, k)
+
+
+def test_calibrate_smooth_layers_repeated():
+    """The grouped call over the same layers and scratches 20 times in a row,
+    with fresh calibration batches: the running maxima follow the per-layer
+    calls, and the scratches stay zero between calls."""
+    shapes = [(512, 1024, 4096), (256, 4096, 1024), (1000, 2048, 2048)]
+    f32 = dict(dtype=torch.float32, device=DEV)
+    st = [(torch.zeros(k, **f32), torch.empty(k, **f32), torch.empty(k, **f32),
+           torch.empty(k, **f32), w8.calibrate_smooth_scratch(k, DEV)) for _, _, k in shapes]
+    ref = [torch.zeros(k, **f32) for _, _, k in shapes]
+    ws = [inputs(0, n, k, torch.float16, seed=50 + i)[1] for i, (_, n, k) in enumerate(shapes)]
+    for it in range(20):
+        xcs = [inputs(c, 0, k, torch.float16, seed=7000 + 10 * it + i)[0]
+               for i, (c, _, k) in enumerate(shapes)]
+        w8.calibrate_smooth_layers([(xc, w) + o for xc, w, o in zip(xcs, ws, st)], 0.5)
+        for i, (xc, w) in enumerate(zip(xcs, ws)):
+            aw1, s1, inv1 = w8.calibrate_smooth(xc, w, 0.5, ref[i])
+            ax, aw, s, inv_s, _ = st[i]
+            for a, b in ((ax, ref[i]), (aw, aw1), (s, s1), (inv_s, inv1)):
+                assert torch.equal(a.view(torch.int32), b.view(torch.int32)), (it, i)
+    torch.cuda.synchronize()
+    for o in st:
+        assert not o[4].any()

@@ -21,6 +21,7 @@ PROTOTYPES = {
     "w8a8_calibrate_smooth_scratch_bytes": (c_size, [c_i64]),
     "w8a8_calibrate_smooth": (c_int, [c_vp, c_i64, c_vp, c_i64, c_int, c_i64, ctypes.c_double,
                                       c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
+    "w8a8_calibrate_smooth_layers": (c_int, [c_vp, c_int, c_int, c_vp]),
     "w8a8_scale_quant_rows": (c_int, [c_vp, c_int, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp]),
     "w8a8_scale_quant_pair": (c_int, [c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp,
                                       c_int, c_i64, c_vp]),
@@ -41,8 +42,17 @@ PROTOTYPES = {
     "w8a8_linear_noalloc": (c_int, [c_vp, c_int, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_vp]),
 }
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 W8A8_F16, W8A8_BF16 = 0, 1
+
+
+
+class CalibLayer(ctypes.Structure):
+    """w8a8_calib_layer_t (include/w8a8.h): one entry of w8a8_calibrate_smooth_layers."""
+    _fields_ = [("x_cal", c_vp), ("cal_rows", c_i64), ("w", c_vp), ("N", c_i64), ("K", c_i64),
+                ("alpha", ctypes.c_double), ("amax_x", c_vp), ("amax_w", c_vp), ("s", c_vp),
+                ("inv_s", c_vp), ("scratch", c_vp), ("scratch_bytes", c_size)]
+
 
 _lib = None
 

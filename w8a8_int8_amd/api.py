@@ -14,6 +14,7 @@ smooth and quantize a layer (``smooth_lm``, ``quantize_model``), and
 """
 from __future__ import annotations
 
+import ctypes
 from typing import Optional
 
 import torch
@@ -121,6 +122,34 @@ def calibrate_smooth(x_cal: Optional[torch.Tensor], w: torch.Tensor, alpha: floa
         _ptr(x_cal), cal_rows, _ptr(w), N, _dtype_code(w), K, float(alpha), _ptr(amax_x),
         _ptr(amax_w), _ptr(s), _ptr(inv_s), _ptr(scratch), scratch.numel(), _stream()))
     return amax_w, s, inv_s
+
+
+def calibrate_smooth_layers(layers, alpha: float) -> None:
+    """calibrate_smooth for several layers in one launch (up to 8 per launch):
+    ``layers`` is a sequence of (x_cal or None, w, amax_x, amax_w, s, inv_s,
+    scratch) with every tensor given, all of one dtype; the outputs are
+    written in place, the same bits as one calibrate_smooth per layer."""
+    arr = (_lib.CalibLayer * max(1, len(layers)))()
+    dtype = None
+    for i, (x_cal, w, amax_x, amax_w, s, inv_s, scratch) in enumerate(layers):
+        _dev(w, amax_x, amax_w, s, inv_s, scratch)
+        N, K = w.shape
+        dtype = w.dtype if dtype is None else dtype
+        if w.dtype != dtype:
+            raise TypeError("calibrate_smooth_layers: every layer must have the same dtype")
+        cal_rows = 0 if x_cal is None else x_cal.shape[0]
+        if x_cal is not None:
+            _dev(x_cal)
+            _need(x_cal, w.dtype, (cal_rows, K))
+        for t in (amax_x, amax_w, s, inv_s):
+            _need(t, torch.float32, (K,))
+        _need(scratch, torch.uint8, (scratch.numel(),))
+        arr[i] = _lib.CalibLayer(_ptr(x_cal), cal_rows, _ptr(w), N, K, float(alpha), _ptr(amax_x),
+                                 _ptr(amax_w), _ptr(s), _ptr(inv_s), _ptr(scratch), scratch.numel())
+    lib = _lib.load()
+    code = _dtype_code(layers[0][1]) if layers else 0
+    _lib.check("w8a8_calibrate_smooth_layers", lib.w8a8_calibrate_smooth_layers(
+        ctypes.addressof(arr), len(layers), code, _stream()))
 
 
 def scale_quant_rows(x: torch.Tensor, col_scale: torch.Tensor,

@@ -132,11 +132,13 @@ size_t w8a8_calibrate_smooth_scratch_bytes(int64_t K) {
   return w8a8::calibrate_smooth_scratch_bytes(K);
 }
 
-w8a8_status_t w8a8_calibrate_smooth(const void* x_cal, int64_t cal_rows, const void* w, int64_t N,
-                                    int dtype, int64_t K, double alpha, float* amax_x,
-                                    float* amax_w, float* s, float* inv_s, void* scratch,
-                                    size_t scratch_bytes, hipStream_t stream) {
-  if (!valid_dtype(dtype)) return W8A8_ERR_DTYPE;
+namespace {
+
+// The checks of one w8a8_calibrate_smooth call (dtype checked by the caller).
+w8a8_status_t check_calibrate(const void* x_cal, int64_t cal_rows, const void* w, int64_t N,
+                              int64_t K, double alpha, const float* amax_x, const float* amax_w,
+                              const float* s, const float* inv_s, const void* scratch,
+                              size_t scratch_bytes) {
   if (cal_rows < 0 || N < 0 || cal_rows >= ((int64_t)1 << 40) || N >= ((int64_t)1 << 40) ||
       K < 1 || K % 8 != 0 || K >= kMaxRows)
     return W8A8_ERR_SHAPE;
@@ -147,6 +149,47 @@ w8a8_status_t w8a8_calibrate_smooth(const void* x_cal, int64_t cal_rows, const v
   if (!aligned(x_cal, 16) || !aligned(w, 16) || !aligned(amax_x, 4) || !aligned(amax_w, 4) ||
       !aligned(s, 4) || !aligned(inv_s, 4) || !aligned(scratch, 16))
     return W8A8_ERR_ALIGN;
+  return W8A8_OK;
+}
+
+}  // namespace
+
+w8a8_status_t w8a8_calibrate_smooth_layers(const w8a8_calib_layer_t* layers, int n, int dtype,
+                                           hipStream_t stream) {
+  if (!valid_dtype(dtype)) return W8A8_ERR_DTYPE;
+  if (n < 0) return W8A8_ERR_SHAPE;
+  if (n == 0) return W8A8_OK;
+  if (!layers) return W8A8_ERR_NULL;
+  for (int i = 0; i < n; ++i) {
+    const w8a8_calib_layer_t& l = layers[i];
+    const w8a8_status_t st = check_calibrate(l.x_cal, l.cal_rows, l.w, l.N, l.K, l.alpha, l.amax_x,
+                                             l.amax_w, l.s, l.inv_s, l.scratch, l.scratch_bytes);
+    if (st != W8A8_OK) return st;
+  }
+  // the kernel arguments of one launch, in chunks of up to 8 entries
+  w8a8::CalibLayerArgs a[8];
+  for (int i0 = 0; i0 < n; i0 += 8) {
+    const int m = n - i0 < 8 ? n - i0 : 8;
+    for (int i = 0; i < m; ++i) {
+      const w8a8_calib_layer_t& l = layers[i0 + i];
+      a[i] = w8a8::CalibLayerArgs{l.x_cal, l.cal_rows, l.w, l.N, l.K, l.alpha,
+                                  l.amax_x, l.amax_w, l.s, l.inv_s, l.scratch};
+    }
+    const w8a8_status_t st =
+        hip_status(w8a8::launch_calibrate_smooth_layers(m, a, dtype == W8A8_BF16, stream));
+    if (st != W8A8_OK) return st;
+  }
+  return W8A8_OK;
+}
+
+w8a8_status_t w8a8_calibrate_smooth(const void* x_cal, int64_t cal_rows, const void* w, int64_t N,
+                                    int dtype, int64_t K, double alpha, float* amax_x,
+                                    float* amax_w, float* s, float* inv_s, void* scratch,
+                                    size_t scratch_bytes, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return W8A8_ERR_DTYPE;
+  const w8a8_status_t st = check_calibrate(x_cal, cal_rows, w, N, K, alpha, amax_x, amax_w, s,
+                                           inv_s, scratch, scratch_bytes);
+  if (st != W8A8_OK) return st;
   return hip_status(w8a8::launch_calibrate_smooth(x_cal, cal_rows, w, N, dtype == W8A8_BF16, K,
                                                   alpha, amax_x, amax_w, s, inv_s, scratch,
                                                   stream));

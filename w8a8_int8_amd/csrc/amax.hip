@@ -26,7 +26,8 @@
 //
 // k_calibrate_smooth runs the same strip code over a calibration batch and a
 // weight in one grid and forms the smoothing factors at the end of each strip
-// (its comment gives the cross-block protocol).
+// (its comment gives the cross-block protocol); k_calibrate_smooth_layers
+// does that for several layers in one flat grid.
 #include "common.h"
 #include "smooth_factor.h"
 
@@ -62,12 +63,12 @@ __device__ __forceinline__ v4u vmax(v4u m, v4u v) {
 // U loads in flight per lane, U * kRowsPerGroup rows per batch.
 template <bool BF16, int U>
 __device__ __forceinline__ unsigned short strip_max(const v4u* __restrict__ x, int64_t cols8,
-                                                    int64_t r_begin, int64_t r_end) {
+                                                    int64_t strip, int64_t r_begin, int64_t r_end) {
   constexpr int kRowsPerBatch = kRowsPerGroup * U;
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
   const int sub = lane / kLanesPerRow;  // row within a wave load
-  const int64_t chunk = (int64_t)blockIdx.x * kLanesPerRow + (lane % kLanesPerRow);  // 16-byte chunk
+  const int64_t chunk = strip * kLanesPerRow + (lane % kLanesPerRow);  // 16-byte chunk
   const bool active = chunk < cols8;
 
   v4u m = {0u, 0u, 0u, 0u};
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(kAmaxThreads) void k_channel_amax(const v4u* __rest
                                                                unsigned* __restrict__ amax_bits) {
   const int64_t r_begin = (int64_t)blockIdx.y * rows_per_block;
   const unsigned short b =
-      strip_max<BF16, kAmaxUnroll>(x, cols8, r_begin, min(rows, r_begin + rows_per_block));
+      strip_max<BF16, kAmaxUnroll>(x, cols8, blockIdx.x, r_begin, min(rows, r_begin + rows_per_block));
   const int64_t col = (int64_t)blockIdx.x * kStripCols + threadIdx.x;
   if (col < cols8 * 8 && b != 0)  // +0 never raises a non-negative running max
     atomicMax(amax_bits + col, __float_as_uint(widen16(b, BF16)));
@@ -153,45 +154,83 @@ __global__ __launch_bounds__(kAmaxThreads) void k_channel_amax(const v4u* __rest
 // accumulator zero for the next call.
 // It resets its counter the same way.  Its plain stores (amax_w, s, inv_s)
 // are for later kernels.
+// One layer's part of a calibrate-smooth launch: the two matrices, their row
+// split and the outputs.  Row blocks yb < rb_x take rows of the calibration
+// batch, the others rows of the weight; the layer has strips x rb blocks.
+struct CalLayer {
+  const v4u* xc;
+  const v4u* w;
+  unsigned* amax_x_bits;
+  unsigned* acc_w_bits;
+  unsigned* arrivals;
+  float* amax_w;
+  float* s;
+  float* inv_s;
+  int64_t cal_rows, w_rows, cols8, rows_per_block, rb_x, rb, strips, block0;
+  double alpha;
+};
+
 template <bool BF16>
-__global__ __launch_bounds__(kAmaxThreads) void k_calibrate_smooth(
-    const v4u* __restrict__ xc, int64_t cal_rows, const v4u* __restrict__ w, int64_t w_rows,
-    int64_t cols8, int64_t rows_per_block, int64_t rb_x, double alpha,
-    unsigned* __restrict__ amax_x_bits, unsigned* __restrict__ acc_w_bits,
-    unsigned* __restrict__ arrivals, float* __restrict__ amax_w, float* __restrict__ s,
-    float* __restrict__ inv_s) {
-  const bool cal = (int64_t)blockIdx.y < rb_x;
-  const v4u* x = cal ? xc : w;
-  const int64_t rows = cal ? cal_rows : w_rows;
-  const int64_t r_begin = (cal ? (int64_t)blockIdx.y : (int64_t)blockIdx.y - rb_x) * rows_per_block;
-  const unsigned short b =
-      strip_max<BF16, kFusedUnroll>(x, cols8, r_begin, min(rows, r_begin + rows_per_block));
+__device__ __forceinline__ void calibrate_block(const CalLayer& g, int64_t strip, int64_t yb) {
+  const bool cal = yb < g.rb_x;
+  const v4u* x = cal ? g.xc : g.w;
+  const int64_t rows = cal ? g.cal_rows : g.w_rows;
+  const int64_t r_begin = (cal ? yb : yb - g.rb_x) * g.rows_per_block;
+  const unsigned short b = strip_max<BF16, kFusedUnroll>(x, g.cols8, strip, r_begin,
+                                                         min(rows, r_begin + g.rows_per_block));
   const int c = threadIdx.x;
-  const int64_t col = (int64_t)blockIdx.x * kStripCols + c;
-  const bool live = col < cols8 * 8;
+  const int64_t col = strip * kStripCols + c;
+  const bool live = col < g.cols8 * 8;
   unsigned seen = 0u;
   if (live && b != 0)
-    seen = atomicMax((cal ? amax_x_bits : acc_w_bits) + col, __float_as_uint(widen16(b, BF16)));
+    seen = atomicMax((cal ? g.amax_x_bits : g.acc_w_bits) + col, __float_as_uint(widen16(b, BF16)));
   // the returned value has arrived, so this thread's maximum has been
   // performed, before the block is counted
   asm volatile("s_waitcnt vmcnt(0)" : : "v"(seen) : "memory");
   __shared__ unsigned last;
   __syncthreads();
-  if (c == 0) last = atomicAdd(arrivals + blockIdx.x, 1u) == gridDim.y - 1 ? 1u : 0u;
+  if (c == 0) last = atomicAdd(g.arrivals + strip, 1u) == (unsigned)g.rb - 1 ? 1u : 0u;
   __syncthreads();
   if (!last) return;
   if (live) {
     // a compare-and-swap that never matches (the pattern is a NaN, never
     // stored) reads the value as a read-modify-write, like the maxima
-    const float ax = __uint_as_float(atomicCAS(amax_x_bits + col, 0xffffffffu, 0xffffffffu));
-    const float aw = __uint_as_float(atomicExch(acc_w_bits + col, 0u));
-    amax_w[col] = aw;
+    const float ax = __uint_as_float(atomicCAS(g.amax_x_bits + col, 0xffffffffu, 0xffffffffu));
+    const float aw = __uint_as_float(atomicExch(g.acc_w_bits + col, 0u));
+    g.amax_w[col] = aw;
     float sj, ij;
-    smooth_factor(ax, aw, alpha, sj, ij);
-    s[col] = sj;
-    inv_s[col] = ij;
+    smooth_factor(ax, aw, g.alpha, sj, ij);
+    g.s[col] = sj;
+    g.inv_s[col] = ij;
   }
-  if (c == 0) atomicExch(arrivals + blockIdx.x, 0u);
+  if (c == 0) atomicExch(g.arrivals + strip, 0u);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kAmaxThreads) void k_calibrate_smooth(const CalLayer g) {
+  calibrate_block<BF16>(g, blockIdx.x, blockIdx.y);
+}
+
+// Several layers in one launch: a flat grid, the layers' blocks one after
+// another in the order of the one-layer grid (strip fastest), so every layer
+// gets the same blocks, rows and protocol as its own launch would.  The
+// layers are independent (their own inputs, outputs and scratch), so their
+// blocks run side by side and one layer's tail (the last block of each strip
+// forming s) overlaps the others' streaming.
+constexpr int kMaxCalLayers = 8;
+struct CalLayers {
+  CalLayer l[kMaxCalLayers];
+  int n;
+};
+
+template <bool BF16>
+__global__ __launch_bounds__(kAmaxThreads) void k_calibrate_smooth_layers(const CalLayers gs) {
+  const int64_t b = blockIdx.x;
+  int i = 0;
+  while (i + 1 < gs.n && b >= gs.l[i + 1].block0) ++i;
+  const CalLayer& g = gs.l[i];
+  const int64_t local = b - g.block0;
+  calibrate_block<BF16>(g, local % g.strips, local / g.strips);
 }
 
 }  // namespace
@@ -227,37 +266,83 @@ size_t calibrate_smooth_scratch_bytes(int64_t K) {
   return (size_t)((4 * K + 255) / 256 * 256 + 4 * strips);
 }
 
+namespace {
+
+// The grid of one layer: about 448 blocks over both matrices, the same rows
+// per block for both, with 16 loads in flight per lane.  Measured on the
+// Llama-2-7B layers: more blocks lose time to the arrival protocol (each
+// strip's counter and each column's maximum take one atomic per row block,
+// one after another), fewer lose streaming rate on the larger weights.
+CalLayer plan_calibrate(const void* xc, int64_t cal_rows, const void* w, int64_t w_rows, int64_t K,
+                        double alpha, float* amax_x, float* amax_w, float* s, float* inv_s,
+                        void* scratch) {
+  CalLayer g;
+  g.cols8 = K / 8;
+  g.strips = (g.cols8 + kLanesPerRow - 1) / kLanesPerRow;
+  const int64_t target = (448 + g.strips - 1) / g.strips;
+  int64_t rpb = (cal_rows + w_rows + target - 1) / target;
+  rpb = (rpb + kRowsPerGroup - 1) / kRowsPerGroup * kRowsPerGroup;
+  if (rpb < kRowsPerGroup) rpb = kRowsPerGroup;
+  g.rows_per_block = rpb;
+  g.rb_x = (cal_rows + rpb - 1) / rpb;
+  int64_t rb_w = (w_rows + rpb - 1) / rpb;
+  if (g.rb_x + rb_w == 0) rb_w = 1;  // no rows at all: one empty block per strip still forms s
+  g.rb = g.rb_x + rb_w;
+  g.xc = (const v4u*)xc;
+  g.w = (const v4u*)w;
+  g.cal_rows = cal_rows;
+  g.w_rows = w_rows;
+  g.alpha = alpha;
+  g.amax_x_bits = (unsigned*)amax_x;
+  g.acc_w_bits = (unsigned*)scratch;
+  g.arrivals = g.acc_w_bits + (K + 63) / 64 * 64;
+  g.amax_w = amax_w;
+  g.s = s;
+  g.inv_s = inv_s;
+  g.block0 = 0;
+  return g;
+}
+
+}  // namespace
+
 hipError_t launch_calibrate_smooth(const void* xc, int64_t cal_rows, const void* w,
                                    int64_t w_rows, bool bf16, int64_t K, double alpha,
                                    float* amax_x, float* amax_w, float* s, float* inv_s,
                                    void* scratch, hipStream_t st) {
   if (K == 0) return hipSuccess;
-  const int64_t cols8 = K / 8;
-  const int64_t strips = (cols8 + kLanesPerRow - 1) / kLanesPerRow;
-  // about 448 blocks over both matrices, the same rows per block for both,
-  // with 16 loads in flight per lane.  Measured on the Llama-2-7B layers:
-  // more blocks lose time to the arrival protocol (each strip's counter and
-  // each column's maximum take one atomic per row block, one after another),
-  // fewer lose streaming rate on the larger weights.
-  const int64_t target = (448 + strips - 1) / strips;
-  int64_t rpb = (cal_rows + w_rows + target - 1) / target;
-  rpb = (rpb + kRowsPerGroup - 1) / kRowsPerGroup * kRowsPerGroup;
-  if (rpb < kRowsPerGroup) rpb = kRowsPerGroup;
-  const int64_t rb_x = (cal_rows + rpb - 1) / rpb;
-  int64_t rb_w = (w_rows + rpb - 1) / rpb;
-  if (rb_x + rb_w == 0) rb_w = 1;  // no rows at all: one empty block per strip still forms s
-  unsigned* acc_w = (unsigned*)scratch;
-  unsigned* arrivals = acc_w + (K + 63) / 64 * 64;
-  const dim3 grid((unsigned)strips, (unsigned)(rb_x + rb_w));
+  const CalLayer g = plan_calibrate(xc, cal_rows, w, w_rows, K, alpha, amax_x, amax_w, s, inv_s,
+                                    scratch);
+  const dim3 grid((unsigned)g.strips, (unsigned)g.rb);
   if (bf16)
-    hipLaunchKernelGGL(k_calibrate_smooth<true>, grid, dim3(kAmaxThreads), 0, st,
-                       (const v4u*)xc, cal_rows, (const v4u*)w, w_rows, cols8, rpb, rb_x, alpha,
-                       (unsigned*)amax_x, acc_w, arrivals, amax_w, s, inv_s);
+    hipLaunchKernelGGL(k_calibrate_smooth<true>, grid, dim3(kAmaxThreads), 0, st, g);
   else
-    hipLaunchKernelGGL(k_calibrate_smooth<false>, grid, dim3(kAmaxThreads), 0, st,
-                       (const v4u*)xc, cal_rows, (const v4u*)w, w_rows, cols8, rpb, rb_x, alpha,
-                       (unsigned*)amax_x, acc_w, arrivals, amax_w, s, inv_s);
+    hipLaunchKernelGGL(k_calibrate_smooth<false>, grid, dim3(kAmaxThreads), 0, st, g);
   return hipGetLastError();
+}
+
+hipError_t launch_calibrate_smooth_layers(int n, const CalibLayerArgs* a, bool bf16,
+                                          hipStream_t st) {
+  for (int i0 = 0; i0 < n; i0 += kMaxCalLayers) {
+    CalLayers gs;
+    gs.n = 0;
+    int64_t blocks = 0;
+    for (int i = i0; i < n && i < i0 + kMaxCalLayers; ++i) {
+      CalLayer g = plan_calibrate(a[i].x_cal, a[i].cal_rows, a[i].w, a[i].n, a[i].k, a[i].alpha,
+                                  a[i].amax_x, a[i].amax_w, a[i].s, a[i].inv_s, a[i].scratch);
+      g.block0 = blocks;
+      blocks += g.strips * g.rb;
+      gs.l[gs.n++] = g;
+    }
+    if (bf16)
+      hipLaunchKernelGGL(k_calibrate_smooth_layers<true>, dim3((unsigned)blocks), dim3(kAmaxThreads),
+                         0, st, gs);
+    else
+      hipLaunchKernelGGL(k_calibrate_smooth_layers<false>, dim3((unsigned)blocks),
+                         dim3(kAmaxThreads), 0, st, gs);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace w8a8

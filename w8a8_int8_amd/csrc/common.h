@@ -25,6 +25,19 @@ hipError_t launch_calibrate_smooth(const void* xc, int64_t cal_rows, const void*
                                    int64_t w_rows, bool bf16, int64_t K, double alpha,
                                    float* amax_x, float* amax_w, float* s, float* inv_s,
                                    void* scratch, hipStream_t st);
+// Several layers' launch_calibrate_smooth in one launch (same dtype); each
+// entry as that call's arguments, with n = the weight's rows and k = K.
+struct CalibLayerArgs {
+  const void* x_cal;
+  int64_t cal_rows;
+  const void* w;
+  int64_t n, k;
+  double alpha;
+  float *amax_x, *amax_w, *s, *inv_s;
+  void* scratch;
+};
+hipError_t launch_calibrate_smooth_layers(int n, const CalibLayerArgs* a, bool bf16,
+                                          hipStream_t st);
 // fmt: 0 = symmetric INT8 codes, 1 = FP8 E4M3 codes.  norm (INT8 only): the
 // rows are RMS-norm inputs and col_scale the folded norm weight; the row scale
 // is divided by the row's rms (with eps).  The same launch sets the nzero
